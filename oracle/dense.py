@@ -1,0 +1,255 @@
+"""Dense fp64 reference: the plain definition of windowed attention and its VJP.
+
+TEST INFRASTRUCTURE ONLY (see the package header): never imported by the
+product path.
+
+What is computed, per packed sequence b, query head h (KV head g = h // G with
+G = Hq / Hkv), query row i and key j:
+
+  visibility   "Off NVIDIA, you fix the platform yourself" (labs.layer2c.com),
+               section "What was broken?": under the sliding-window rule a
+               token sees only the most recent tokens before it; under the
+               plain causal rule it sees every earlier token. Reading used:
+               query i sits at key position p = i + (L_k - L_q) (queries are
+               the last L_q positions; the lab's "Method and disclosure"
+               section has key tiles left unvisited when there are fewer
+               queries than keys, which needs that alignment). Cell (i, j) is
+               visible iff j <= p and p - j < w: w keys counting the token
+               itself, so w = 1 sees only itself (the record entry "Gradient
+               parity, small shapes": at window 1 the true gradient is zero).
+               Non-causal without a window: every key is visible.
+  forward      s_ij = scale * q_i . k_j on visible cells, -inf elsewhere;
+               LSE_i = log sum_j exp(s_ij) (natural log); P_ij = exp(s_ij - LSE_i);
+               O_i = sum_j P_ij v_j. The saved state is O and LSE (mlx-train-perf
+               README, flash-attention passage: the flash path keeps the
+               attention output and the log-sum-exp, O(N) state).
+  backward     the vector-Jacobian product of the loss L = sum(O * dO):
+               dP_ij = dO_i . v_j, D_i = dO_i . O_i, dS_ij = P_ij (dP_ij - D_i),
+               dQ_i = scale sum_j dS_ij k_j,
+               dK_j = scale sum_{h in group} sum_i dS_ij q_i,
+               dV_j = sum_{h in group} sum_i P_ij dO_i.
+               (The lab's "What did fixing it take?" section: the backward
+               must give every query and key its gradient, including key
+               blocks no query visits, whose gradient is zero.)
+  empty rows   a query with no visible key (unreachable when L_q <= L_k) gets
+               O = 0, LSE = -inf, dQ = 0.
+
+The full L_q x L_k masked matrix is built for each (sequence, head), a panel of
+at most ``panel_rows`` query rows at a time, so memory stays bounded while
+nothing is tiled along keys. The mask comes from arange comparisons.
+"""
+from __future__ import annotations
+
+import os
+from typing import Iterable, Optional
+
+import numpy as np
+
+F64 = np.float64
+
+
+class HostRamExceeded(MemoryError):
+    """Raised before an allocation that would exceed the host-RAM ceiling."""
+
+
+CUSHION_BYTES = 2 << 30
+
+
+def available_host_bytes() -> int:
+    """MemAvailable from /proc/meminfo (bytes); a large number if unreadable."""
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemAvailable:"):
+                    return int(line.split()[1]) * 1024
+    except OSError:
+        pass
+    return 1 << 62
+
+
+def check_host_ram(nbytes: int, ceiling: Optional[int] = None) -> None:
+    """Refuse up front, rather than thrash, if ``nbytes`` exceeds the ceiling.
+
+    The ceiling defaults to what the machine has available minus a 2 GiB
+    cushion (the mlx-train-perf README's memory-guard passage sets its ceiling
+    from the machine's own free memory minus such a cushion).
+    """
+    if ceiling is None:
+        ceiling = available_host_bytes() - CUSHION_BYTES
+    if nbytes > ceiling:
+        raise HostRamExceeded(
+            f"oracle step needs {nbytes} bytes of host RAM, ceiling is {ceiling}")
+
+
+def visible_cells(lq: int, lk: int, window: int, causal: bool,
+                  rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Boolean [len(rows), lk] mask of visible (query, key) cells."""
+    if not causal and window < lk:
+        raise ValueError("a window is defined only for causal attention")
+    i = np.arange(lq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    j = np.arange(lk, dtype=np.int64)
+    if not causal:
+        return np.ones((i.size, lk), dtype=bool)
+    pos = (i + (lk - lq))[:, None]
+    return (j[None, :] <= pos) & (pos - j[None, :] < window)
+
+
+def _panel(qh, kg, vg, doh, mask, scale, with_backward):
+    """One panel of query rows against every key of the sequence (fp64)."""
+    s = scale * (qh @ kg.T)
+    s = np.where(mask, s, -np.inf)
+    has_key = mask.any(axis=1)
+    m = np.where(has_key, s.max(axis=1, initial=-np.inf), 0.0)
+    e = np.exp(s - m[:, None])                      # exp(-inf) = 0 on masked cells
+    z = e.sum(axis=1)
+    zs = np.where(has_key, z, 1.0)
+    lse = np.where(has_key, m + np.log(zs), -np.inf)
+    p = e / zs[:, None]
+    o = p @ vg
+    if not with_backward:
+        return dict(p=p, o=o, lse=lse)
+    dp = doh @ vg.T
+    dlt = np.sum(doh * o, axis=1)
+    ds = p * (dp - dlt[:, None])
+    return dict(p=p, o=o, lse=lse, delta=dlt, ds=ds)
+
+
+def _as64(a):
+    return np.asarray(a, dtype=F64)
+
+
+def _check_shapes(q, k, v, do, cu_q, cu_k):
+    tq, hq, d = q.shape
+    tk, hkv, dk = k.shape
+    if v.shape != k.shape or dk != d or (do is not None and do.shape != q.shape):
+        raise ValueError("shape mismatch")
+    if hq % hkv:
+        raise ValueError("heads_q must be a multiple of heads_kv")
+    if len(cu_q) != len(cu_k) or cu_q[-1] != tq or cu_k[-1] != tk:
+        raise ValueError("cu_seqlens do not match the packed tensors")
+    return tq, tk, hq, hkv, d
+
+
+def sdpa_reference(q, k, v, do, cu_q, cu_k, scale: float, window: int, causal: bool, *,
+                   with_backward: bool = True, panel_rows: int = 512,
+                   ram_ceiling: Optional[int] = None) -> dict:
+    """Full forward (and backward) over a packed batch.
+
+    q, do: [T_q, Hq, d]; k, v: [T_k, Hkv, d]; cu_q, cu_k: [B+1] offsets.
+    Returns fp64 arrays: o [T_q, Hq, d], lse [Hq, T_q], and with the backward
+    delta (= D) [Hq, T_q], dq [T_q, Hq, d], dk, dv [T_k, Hkv, d].
+    """
+    tq, tk, hq, hkv, d = _check_shapes(q, k, v, do if with_backward else None, cu_q, cu_k)
+    grp = hq // hkv
+    o = np.zeros((tq, hq, d), F64)
+    lse = np.full((hq, tq), -np.inf, F64)
+    out = dict(o=o, lse=lse)
+    if with_backward:
+        delta = np.zeros((hq, tq), F64)
+        dq = np.zeros((tq, hq, d), F64)
+        dk = np.zeros((tk, hkv, d), F64)
+        dv = np.zeros((tk, hkv, d), F64)
+        out.update(delta=delta, dq=dq, dk=dk, dv=dv)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        lq, lk = q1 - q0, k1 - k0
+        if lq == 0:
+            continue
+        rows_per = max(1, min(panel_rows, lq))
+        # ~8 panel-sized fp64 arrays live at once
+        check_host_ram(8 * rows_per * max(lk, 1) * 8, ram_ceiling)
+        for h in range(hq):
+            g = h // grp
+            kg = _as64(k[k0:k1, g, :])
+            vg = _as64(v[k0:k1, g, :])
+            for r0 in range(0, lq, rows_per):
+                r1 = min(lq, r0 + rows_per)
+                mask = visible_cells(lq, lk, window, causal, np.arange(r0, r1))
+                qh = _as64(q[q0 + r0:q0 + r1, h, :])
+                doh = _as64(do[q0 + r0:q0 + r1, h, :]) if with_backward else None
+                res = _panel(qh, kg, vg, doh, mask, scale, with_backward)
+                o[q0 + r0:q0 + r1, h, :] = res["o"]
+                lse[h, q0 + r0:q0 + r1] = res["lse"]
+                if with_backward:
+                    ds = res["ds"]
+                    delta[h, q0 + r0:q0 + r1] = res["delta"]
+                    dq[q0 + r0:q0 + r1, h, :] = scale * (ds @ kg)
+                    dk[k0:k1, g, :] += scale * (ds.T @ qh)
+                    dv[k0:k1, g, :] += res["p"].T @ doh
+    return out
+
+
+def _locate(cu, t):
+    b = int(np.searchsorted(cu, t, side="right") - 1)
+    return b, int(t - cu[b])
+
+
+def sdpa_query_rows(q, k, v, do, cu_q, cu_k, scale, window, causal,
+                    tokens: Iterable[int], heads: Iterable[int]) -> dict:
+    """O, LSE, D and dQ for selected (packed query token, query head) rows.
+
+    Each row is the same plain definition as :func:`sdpa_reference`, built as a
+    one-row panel against all keys of its sequence.
+    """
+    _check_shapes(q, k, v, do, cu_q, cu_k)
+    grp = q.shape[1] // k.shape[1]
+    res = dict(o=[], lse=[], delta=[], dq=[])
+    for t, h in zip(tokens, heads):
+        b, i = _locate(cu_q, t)
+        k0, k1 = int(cu_k[b]), int(cu_k[b + 1])
+        lq = int(cu_q[b + 1] - cu_q[b])
+        g = h // grp
+        kg, vg = _as64(k[k0:k1, g, :]), _as64(v[k0:k1, g, :])
+        mask = visible_cells(lq, k1 - k0, window, causal, np.array([i]))
+        r = _panel(_as64(q[t:t + 1, h, :]), kg, vg, _as64(do[t:t + 1, h, :]), mask, scale, True)
+        res["o"].append(r["o"][0])
+        res["lse"].append(r["lse"][0])
+        res["delta"].append(r["delta"][0])
+        res["dq"].append(scale * (r["ds"] @ kg)[0])
+    return {key: np.array(val) for key, val in res.items()}
+
+
+def sdpa_key_rows(q, k, v, do, cu_q, cu_k, scale, window, causal,
+                  tokens: Iterable[int], kv_heads: Iterable[int], *,
+                  panel_rows: int = 512) -> dict:
+    """dK and dV for selected (packed key token, KV head) rows.
+
+    Every query row that sees the key is rebuilt in full (its whole masked
+    score row), so its P and dS come from the same definition as above.
+    """
+    _check_shapes(q, k, v, do, cu_q, cu_k)
+    grp = q.shape[1] // k.shape[1]
+    res = dict(dk=[], dv=[])
+    for t, g in zip(tokens, kv_heads):
+        b, j = _locate(cu_k, t)
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        k0, k1 = int(cu_k[b]), int(cu_k[b + 1])
+        lq, lk = q1 - q0, k1 - k0
+        kg, vg = _as64(k[k0:k1, g, :]), _as64(v[k0:k1, g, :])
+        # the column of the mask for key j, built 1024 rows at a time
+        col = np.concatenate([
+            visible_cells(lq, lk, window, causal, np.arange(r, min(lq, r + 1024)))[:, j]
+            for r in range(0, lq, 1024)]) if lq else np.zeros(0, bool)
+        rows = np.nonzero(col)[0]
+        dk_j = np.zeros(k.shape[2], F64)
+        dv_j = np.zeros(k.shape[2], F64)
+        for h in range(g * grp, (g + 1) * grp):
+            for r0 in range(0, rows.size, panel_rows):
+                rr = rows[r0:r0 + panel_rows]
+                mask = visible_cells(lq, lk, window, causal, rr)
+                qh = _as64(q[q0 + rr, h, :])
+                doh = _as64(do[q0 + rr, h, :])
+                r = _panel(qh, kg, vg, doh, mask, scale, True)
+                dk_j += scale * (r["ds"][:, j] @ qh)
+                dv_j += r["p"][:, j] @ doh
+        res["dk"].append(dk_j)
+        res["dv"].append(dv_j)
+    return {key: np.array(val) for key, val in res.items()}
+
+
+def oracle_threads() -> int:
+    """Host cores this process may use (what BLAS is asked to use)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1

@@ -1,0 +1,76 @@
+"""Brute-force attention, one query at a time, in plain Python floats.
+
+TEST INFRASTRUCTURE ONLY (see the package header). Independent of
+``oracle.dense``: it shares no helper with it. It walks each query, lists the
+keys it may see with explicit comparisons, and applies the softmax and its
+vector-Jacobian product with ``math.fsum`` sums. Tiny shapes only.
+
+Visibility, softmax, saved state and gradients are the same definitions as in
+``oracle.dense`` (pages: "Off NVIDIA, you fix the platform yourself", sections
+"What was broken?" and "What did fixing it take?"; the mlx-train-perf README's
+flash-attention passage for the O + log-sum-exp saved state).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _dot(a, b):
+    return math.fsum(x * y for x, y in zip(a, b))
+
+
+def sdpa_loop(q, k, v, do, cu_q, cu_k, scale, window, causal) -> dict:
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    grp = hq // hkv
+    o = np.zeros((tq, hq, d))
+    lse = np.full((hq, tq), -math.inf)
+    delta = np.zeros((hq, tq))
+    dq = np.zeros((tq, hq, d))
+    dk = [[[[] for _ in range(d)] for _ in range(hkv)] for _ in range(tk)]
+    dv = [[[[] for _ in range(d)] for _ in range(hkv)] for _ in range(tk)]
+    for b in range(len(cu_q) - 1):
+        qa, qb, ka, kb = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        shift = (kb - ka) - (qb - qa)
+        for h in range(hq):
+            g = h // grp
+            for i in range(qb - qa):
+                me = i + shift
+                keys = []
+                for j in range(kb - ka):
+                    if causal:
+                        if j <= me and me - j < window:
+                            keys.append(j)
+                    else:
+                        keys.append(j)
+                if not keys:
+                    continue
+                qi = q[qa + i, h]
+                doi = do[qa + i, h]
+                sc = [scale * _dot(qi, k[ka + j, g]) for j in keys]
+                top = max(sc)
+                lsum = top + math.log(math.fsum(math.exp(x - top) for x in sc))
+                pr = [math.exp(x - lsum) for x in sc]
+                oi = [math.fsum(pr[n] * v[ka + j, g, c] for n, j in enumerate(keys))
+                      for c in range(d)]
+                dd = _dot(doi, oi)
+                dsc = [pr[n] * (_dot(doi, v[ka + j, g]) - dd) for n, j in enumerate(keys)]
+                o[qa + i, h] = oi
+                lse[h, qa + i] = lsum
+                delta[h, qa + i] = dd
+                for c in range(d):
+                    dq[qa + i, h, c] = scale * math.fsum(
+                        dsc[n] * k[ka + j, g, c] for n, j in enumerate(keys))
+                for n, j in enumerate(keys):
+                    for c in range(d):
+                        dk[ka + j][g][c].append(scale * dsc[n] * qi[c])
+                        dv[ka + j][g][c].append(pr[n] * doi[c])
+    dk_arr = np.array([[[math.fsum(x) for x in row] for row in head] for head in dk]).reshape(tk, hkv, d)
+    dv_arr = np.array([[[math.fsum(x) for x in row] for row in head] for head in dv]).reshape(tk, hkv, d)
+    return dict(o=o, lse=lse, delta=delta, dq=dq, dk=dk_arr, dv=dv_arr)

@@ -1,0 +1,167 @@
+"""Seeded synthetic workloads for windowed, grouped-query attention.
+
+This module holds shapes and random draws only. It contains none of the
+attention arithmetic, so both the HIP path (through the binding) and the fp64
+CPU oracle can take their inputs from it without sharing any of the method.
+
+Workloads follow the shapes the pages measure:
+  * "Off NVIDIA, you fix the platform yourself" (labs.layer2c.com), record
+    entry "Attention backward memory, one sliding-window layer": bf16, 32 query
+    heads, a 1,024-token window, 8K to 32K tokens.
+  * the mlx-train-perf README, attention-op timing passage: batch 1, 32 query /
+    8 KV heads, 8,192 tokens, head_dim 128, causal.
+  * the lab's "load" entry: a corpus of transcripts with mean 8,663 tokens and
+    longest 30,553, trained 4 per step. That corpus is not available; ragged
+    batches are drawn from a lognormal with that mean, clipped to that longest.
+
+Draw order for one workload with seed s (numpy ``default_rng(s)``):
+  1. ragged workloads only: 4 sequence lengths,
+     ``clip(rint(lognormal(8.9085, 0.5627, 4)), 512, 30553)``;
+  2. Q, K, V, dO in that order, each ``standard_normal(shape, float32)`` over
+     the packed shape ``[T, H, d]``;
+  3. dO is multiplied by the workload's dO scale in fp32;
+  4. bf16 workloads round all four tensors to bf16 (round to nearest even,
+     done by torch on the CPU). The oracle sees exactly these rounded values.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+INT32_MAX = 2**31 - 1
+
+# Lognormal fitted so that 171 draws have mean ~8,663 and a typical maximum
+# near the 30,553-token longest transcript of the lab's corpus.
+LOGNORMAL_MU = 8.9085
+LOGNORMAL_SIGMA = 0.5627
+LEN_MIN, LEN_MAX = 512, 30553
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    lengths_q: tuple          # per-sequence query lengths (packed in order)
+    lengths_k: tuple          # per-sequence key lengths, each >= the query length
+    heads_q: int
+    heads_kv: int
+    head_dim: int
+    window: int               # >= 1; INT32_MAX or >= every key length means none
+    causal: bool
+    dtype: str                # "f32" or "bf16"
+    scale: float
+    do_scale: float
+    seed: int
+    lengths_drawn: bool = False  # lengths were the first draw from ``seed``
+
+    @property
+    def batch(self) -> int:
+        return len(self.lengths_q)
+
+    @property
+    def total_q(self) -> int:
+        return int(sum(self.lengths_q))
+
+    @property
+    def total_k(self) -> int:
+        return int(sum(self.lengths_k))
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return int(max(self.lengths_q)) if self.lengths_q else 0
+
+    @property
+    def max_seqlen_k(self) -> int:
+        return int(max(self.lengths_k)) if self.lengths_k else 0
+
+    def cu_seqlens_q(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.lengths_q)]).astype(np.int32)
+
+    def cu_seqlens_k(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.lengths_k)]).astype(np.int32)
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+def ragged_lengths(seed: int, n: int = 4) -> tuple:
+    """Step 1 of the draw order: n lognormal sequence lengths."""
+    rng = np.random.default_rng(seed)
+    lens = np.clip(np.rint(rng.lognormal(LOGNORMAL_MU, LOGNORMAL_SIGMA, n)), LEN_MIN, LEN_MAX)
+    return tuple(int(x) for x in lens)
+
+
+def _fixed(name, n, hq, hkv, d, window, dtype, scale, do_scale, seed, batch=1):
+    return Workload(name, (n,) * batch, (n,) * batch, hq, hkv, d, window, True, dtype,
+                    scale, do_scale, seed)
+
+
+# The five measured workloads, by what they are.
+TINY_F32 = _fixed("tiny_f32_n256_w32_gqa2_d64", 256, 2, 1, 64, 32, "f32", 1 / 8, 1.0, 1)
+GQA_2K = _fixed("bf16_n2048_w1024_32q8kv_d128", 2048, 32, 8, 128, 1024, "bf16",
+                1 / math.sqrt(128), 0.1, 2)
+CAUSAL_8K = _fixed("bf16_n8192_causal_32q8kv_d128", 8192, 32, 8, 128, 8192, "bf16",
+                   1 / math.sqrt(128), 0.1, 3)
+SWA_32K = _fixed("bf16_n32768_w1024_32q8kv_d128", 32768, 32, 8, 128, 1024, "bf16",
+                 1 / math.sqrt(128), 0.1, 4)
+
+
+def varlen_workload(seed: int = 5, window: int = 1024) -> Workload:
+    lens = ragged_lengths(seed)
+    return Workload(f"bf16_varlen4_w{window}_32q8kv_d128", lens, lens, 32, 8, 128, window,
+                    True, "bf16", 1 / math.sqrt(128), 0.1, seed, lengths_drawn=True)
+
+
+VARLEN_4 = varlen_workload()
+
+WORKLOADS = {w.name: w for w in (TINY_F32, GQA_2K, CAUSAL_8K, SWA_32K, VARLEN_4)}
+
+# Edge sweep windows for the ragged batch: 1, around one 128-key tile, and the
+# longest sequence (equivalent to plain causal).
+VARLEN_SWEEP_WINDOWS = (1, 127, 128, 129, max(VARLEN_4.lengths_k))
+
+
+def _round_bf16(x: np.ndarray) -> np.ndarray:
+    import torch  # plumbing only: torch's fp32 -> bf16 cast rounds to nearest even
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
+    """Draw Q, K, V, dO for workload ``w`` (fp32 arrays; bf16-representable
+    values when ``w.dtype == 'bf16'``) plus the int32 cumulative offsets.
+
+    The ragged length draw (step 1) is made by :func:`varlen_workload`, with the
+    same generator state the tensors then continue from, so that a ragged
+    workload built from seed s and its tensors come from one stream.
+    """
+    s = w.seed if seed is None else seed
+    rng = np.random.default_rng(s)
+    if w.lengths_drawn and s == w.seed:
+        # one stream: the lengths were the first draw from this seed
+        rng.lognormal(LOGNORMAL_MU, LOGNORMAL_SIGMA, w.batch)
+    tq, tk, hq, hkv, d = w.total_q, w.total_k, w.heads_q, w.heads_kv, w.head_dim
+    q = rng.standard_normal((tq, hq, d), dtype=np.float32)
+    k = rng.standard_normal((tk, hkv, d), dtype=np.float32)
+    v = rng.standard_normal((tk, hkv, d), dtype=np.float32)
+    do = rng.standard_normal((tq, hq, d), dtype=np.float32)
+    if w.do_scale != 1.0:
+        do *= np.float32(w.do_scale)
+    if w.dtype == "bf16":
+        q, k, v, do = (_round_bf16(a) for a in (q, k, v, do))
+    return dict(q=q, k=k, v=v, do=do, cu_q=w.cu_seqlens_q(), cu_k=w.cu_seqlens_k())
+
+
+def small_case(lengths_q: Sequence[int], lengths_k: Optional[Sequence[int]] = None, *,
+               heads_q=2, heads_kv=1, head_dim=64, window=INT32_MAX, causal=True,
+               dtype="f32", scale=None, do_scale=1.0, seed=0) -> Workload:
+    """A custom (test-sized) workload with explicit lengths."""
+    lengths_k = tuple(lengths_q) if lengths_k is None else tuple(lengths_k)
+    if scale is None:
+        scale = 1 / math.sqrt(head_dim)
+    return Workload(f"case_s{seed}", tuple(int(x) for x in lengths_q),
+                    tuple(int(x) for x in lengths_k), heads_q, heads_kv, head_dim, window,
+                    causal, dtype, float(scale), do_scale, seed)

@@ -1,0 +1,259 @@
+"""Pins for the fp64 oracle: facts fixed by the pages and by the mathematics.
+
+Each ``pin_*`` function takes an oracle module exposing ``sdpa_reference`` (the
+real ``oracle.dense`` or a copy with a planted mistake) and raises
+AssertionError if the module disagrees with:
+
+  * central finite differences of its own forward (backward formula),
+  * the independent per-query brute-force loop (``oracle.loop``),
+  * closed forms: window 1 (each query sees only itself: O = V, dQ = dK = 0;
+    the lab record's "Gradient parity, small shapes" entry says the true
+    gradient there is zero), scale 0 (uniform attention = a causal moving
+    average, written with prefix sums), and a hand-derived two-token example,
+  * invariants: softmax rows sum to one; shifting all keys changes nothing
+    (sum_j dK_j = 0); shifting all values shifts O (sum_j dV_j = sum_i dO_i);
+    grouped-query = multi-head with repeated K/V; a packed batch = independent
+    runs; a window w query = plain causal attention over its last w keys;
+    window >= N is plain causal.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from oracle import fd, loop
+from sliding_window_flash_amd.workloads import INT32_MAX, make_inputs, small_case
+
+
+def _call(ref, w, x, **kw):
+    args = dict(q=x["q"], k=x["k"], v=x["v"], do=x["do"], cu_q=x["cu_q"], cu_k=x["cu_k"],
+                scale=w.scale, window=w.window, causal=w.causal)
+    args.update(kw)
+    return ref.sdpa_reference(args["q"], args["k"], args["v"], args["do"], args["cu_q"],
+                              args["cu_k"], args["scale"], args["window"], args["causal"])
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    fin = np.isfinite(b)
+    assert np.array_equal(np.isfinite(a), fin), what
+    err = np.max(np.abs(a[fin] - b[fin]), initial=0.0)
+    assert err <= tol, f"{what}: max abs error {err} > {tol}"
+
+
+FD_CASES = [
+    # (lengths_q, lengths_k, heads_q, heads_kv, head_dim, window, causal)
+    ([5, 7], None, 2, 1, 3, 1, True),
+    ([5, 7], None, 2, 1, 3, 2, True),
+    ([5, 7], None, 2, 1, 3, 3, True),
+    ([5, 7], None, 2, 1, 3, INT32_MAX, True),
+    ([3, 4], [5, 7], 2, 1, 2, 2, True),
+    ([4], None, 2, 2, 2, INT32_MAX, False),
+]
+
+
+def pin_finite_differences(ref):
+    for n, (lq, lk, hq, hkv, d, win, causal) in enumerate(FD_CASES):
+        w = small_case(lq, lk, heads_q=hq, heads_kv=hkv, head_dim=d, window=win,
+                       causal=causal, seed=100 + n)
+        x = make_inputs(w)
+        out = _call(ref, w, x)
+        num = fd.grads(x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale,
+                       w.window, w.causal, forward=ref.sdpa_reference)
+        for g in ("dq", "dk", "dv"):
+            _close(out[g], num[g], 1e-8, f"finite differences {g} case {n}")
+
+
+LOOP_CASES = FD_CASES + [
+    ([6, 9], [6, 12], 4, 2, 3, 4, True),
+    ([8], None, 4, 1, 4, 5, True),
+]
+
+
+def pin_loop(ref):
+    for n, (lq, lk, hq, hkv, d, win, causal) in enumerate(LOOP_CASES):
+        w = small_case(lq, lk, heads_q=hq, heads_kv=hkv, head_dim=d, window=win,
+                       causal=causal, seed=200 + n)
+        x = make_inputs(w)
+        out = _call(ref, w, x)
+        bf = loop.sdpa_loop(x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale,
+                            w.window, w.causal)
+        for key in ("o", "lse", "delta", "dq", "dk", "dv"):
+            scale = max(1.0, float(np.max(np.abs(bf[key][np.isfinite(bf[key])]), initial=0)))
+            _close(out[key], bf[key], 1e-12 * scale, f"loop {key} case {n}")
+
+
+def pin_window_one(ref):
+    w = small_case([6, 9], [6, 11], heads_q=4, heads_kv=2, head_dim=5, window=1, seed=3)
+    x = make_inputs(w)
+    out = _call(ref, w, x)
+    grp = w.heads_q // w.heads_kv
+    dv_expect = np.zeros_like(x["v"], dtype=np.float64)
+    for b in range(w.batch):
+        lq, lk = w.lengths_q[b], w.lengths_k[b]
+        shift = lk - lq
+        for i in range(lq):
+            t, kt = x["cu_q"][b] + i, x["cu_k"][b] + i + shift
+            for h in range(w.heads_q):
+                g = h // grp
+                _close(out["o"][t, h], x["v"][kt, g], 1e-13, "window 1: O = V")
+                lse = w.scale * float(np.dot(x["q"][t, h].astype(np.float64),
+                                             x["k"][kt, g].astype(np.float64)))
+                _close(out["lse"][h, t], lse, 1e-13, "window 1: LSE = scale q.k")
+                dv_expect[kt, g] += x["do"][t, h]
+    _close(out["dq"], np.zeros_like(out["dq"]), 1e-12, "window 1: dQ = 0")
+    _close(out["dk"], np.zeros_like(out["dk"]), 1e-12, "window 1: dK = 0")
+    _close(out["dv"], dv_expect, 1e-13, "window 1: dV = sum of the group's dO")
+
+
+def pin_scale_zero(ref):
+    w = small_case([9, 13], [11, 13], heads_q=4, heads_kv=2, head_dim=3, window=4,
+                   scale=0.0, seed=4)
+    x = make_inputs(w)
+    out = _call(ref, w, x)
+    grp = w.heads_q // w.heads_kv
+    for b in range(w.batch):
+        lq, lk = w.lengths_q[b], w.lengths_k[b]
+        shift = lk - lq
+        q0, k0 = x["cu_q"][b], x["cu_k"][b]
+        for h in range(w.heads_q):
+            g = h // grp
+            vs = np.concatenate([np.zeros((1, w.head_dim)),
+                                 np.cumsum(x["v"][k0:k0 + lk, g].astype(np.float64), axis=0)])
+            cnt = np.array([min(i + shift + 1, w.window) for i in range(lq)], np.float64)
+            hi = np.arange(lq) + shift + 1
+            o_expect = (vs[hi] - vs[hi - cnt.astype(int)]) / cnt[:, None]
+            _close(out["o"][q0:q0 + lq, h], o_expect, 1e-13, "scale 0: moving average")
+            _close(out["lse"][h, q0:q0 + lq], np.log(cnt), 1e-13, "scale 0: LSE = ln c")
+        for g in range(w.heads_kv):
+            wdo = sum(x["do"][q0:q0 + lq, h].astype(np.float64) for h in range(g * grp, (g + 1) * grp))
+            cnt = np.array([min(i + shift + 1, w.window) for i in range(lq)], np.float64)
+            ps = np.concatenate([np.zeros((1, w.head_dim)), np.cumsum(wdo / cnt[:, None], axis=0)])
+            for j in range(lk):
+                lo_i = max(0, j - shift)
+                hi_i = min(lq, j - shift + w.window)
+                dv = ps[hi_i] - ps[lo_i] if hi_i > lo_i else np.zeros(w.head_dim)
+                _close(out["dv"][k0 + j, g], dv, 1e-13, "scale 0: dV closed form")
+    assert np.all(out["dq"] == 0) and np.all(out["dk"] == 0), "scale 0: dQ = dK = 0 exactly"
+
+
+def pin_hand_example(ref):
+    """One head, d = 1, causal, scale 1: q = (1, 2), k = (0, 1), v = (3, 5),
+    dO = (1, 1).
+
+    Row 0 sees key 0 only: O = 3, LSE = 0, P = 1, dP = 3 = D, so dS = 0.
+    Row 1 sees scores (0, 2): P = (a, b), a = 1/(1+e^2), b = e^2/(1+e^2),
+    LSE = ln(1+e^2), O = 3a + 5b, dP = (3, 5), D = O. With a + b = 1,
+    3 - O = -2b and 5 - O = 2a, so dS = (-2ab, 2ab).
+    dQ = (0, -2ab*0 + 2ab*1) = (0, 2ab); dK_j = sum_i dS_ij q_i = (-4ab, 4ab);
+    dV_j = sum_i P_ij dO_i = (1 + a, b). With window 1, row 1 sees key 1 only:
+    O = 5, LSE = 2.
+    """
+    q = np.array([[[1.0]], [[2.0]]])
+    k = np.array([[[0.0]], [[1.0]]])
+    v = np.array([[[3.0]], [[5.0]]])
+    do = np.ones((2, 1, 1))
+    cu = np.array([0, 2], np.int32)
+    e2 = math.exp(2.0)
+    a, b = 1 / (1 + e2), e2 / (1 + e2)
+    out = ref.sdpa_reference(q, k, v, do, cu, cu, 1.0, INT32_MAX, True)
+    _close(out["o"][:, 0, 0], [3.0, 3 * a + 5 * b], 1e-14, "hand example O")
+    _close(out["lse"][0], [0.0, math.log(1 + e2)], 1e-14, "hand example LSE")
+    _close(out["dq"][:, 0, 0], [0.0, 2 * a * b], 1e-14, "hand example dQ")
+    _close(out["dk"][:, 0, 0], [-4 * a * b, 4 * a * b], 1e-14, "hand example dK")
+    _close(out["dv"][:, 0, 0], [1 + a, b], 1e-14, "hand example dV")
+    out1 = ref.sdpa_reference(q, k, v, do, cu, cu, 1.0, 1, True)
+    _close(out1["o"][:, 0, 0], [3.0, 5.0], 1e-14, "hand example window 1 O")
+    _close(out1["lse"][0], [0.0, 2.0], 1e-14, "hand example window 1 LSE")
+
+
+def pin_softmax_rows(ref):
+    w = small_case([10, 14], heads_q=2, heads_kv=1, head_dim=4, window=5, seed=6)
+    x = make_inputs(w)
+    out = _call(ref, w, x)
+    for b in range(w.batch):
+        lq = w.lengths_q[b]
+        q0 = x["cu_q"][b]
+        for h in range(w.heads_q):
+            for i in range(lq):
+                total = 0.0
+                for j in range(lq):
+                    if j <= i and i - j < w.window:
+                        s = w.scale * float(np.dot(x["q"][q0 + i, h].astype(np.float64),
+                                                   x["k"][q0 + j, 0].astype(np.float64)))
+                        total += math.exp(s - out["lse"][h, q0 + i])
+                assert abs(total - 1.0) < 1e-12, f"softmax row sum {total}"
+
+
+def pin_shift_identities(ref):
+    w = small_case([7, 12], [9, 12], heads_q=4, heads_kv=2, head_dim=3, window=3, seed=7)
+    x = make_inputs(w)
+    out = _call(ref, w, x)
+    grp = w.heads_q // w.heads_kv
+    for b in range(w.batch):
+        k0, k1 = x["cu_k"][b], x["cu_k"][b + 1]
+        q0, q1 = x["cu_q"][b], x["cu_q"][b + 1]
+        for g in range(w.heads_kv):
+            _close(out["dk"][k0:k1, g].sum(0), np.zeros(w.head_dim), 1e-12, "sum_j dK_j = 0")
+            want = x["do"][q0:q1, g * grp:(g + 1) * grp].astype(np.float64).sum((0, 1))
+            _close(out["dv"][k0:k1, g].sum(0), want, 1e-12, "sum_j dV_j = sum_i dO_i")
+
+
+def pin_gqa_is_repeated_mha(ref):
+    w = small_case([6, 8], heads_q=4, heads_kv=2, head_dim=3, window=3, seed=8)
+    x = make_inputs(w)
+    gqa = _call(ref, w, x)
+    mha = _call(ref, w, x, k=np.repeat(x["k"], 2, axis=1), v=np.repeat(x["v"], 2, axis=1))
+    for key in ("o", "lse", "dq"):
+        _close(gqa[key], mha[key], 1e-13, f"GQA vs MHA {key}")
+    for key in ("dk", "dv"):
+        summed = mha[key].reshape(mha[key].shape[0], 2, 2, -1).sum(2)
+        _close(gqa[key], summed, 1e-13, f"GQA vs MHA {key}")
+
+
+def pin_packed_is_concatenation(ref):
+    w = small_case([5, 8], [7, 8], heads_q=2, heads_kv=1, head_dim=3, window=4, seed=9)
+    x = make_inputs(w)
+    out = _call(ref, w, x)
+    for b in range(w.batch):
+        q0, q1 = x["cu_q"][b], x["cu_q"][b + 1]
+        k0, k1 = x["cu_k"][b], x["cu_k"][b + 1]
+        one = _call(ref, w, x, q=x["q"][q0:q1], k=x["k"][k0:k1], v=x["v"][k0:k1],
+                    do=x["do"][q0:q1], cu_q=np.array([0, q1 - q0], np.int32),
+                    cu_k=np.array([0, k1 - k0], np.int32))
+        _close(out["o"][q0:q1], one["o"], 1e-13, "packed O")
+        _close(out["lse"][:, q0:q1], one["lse"], 1e-13, "packed LSE")
+        _close(out["dq"][q0:q1], one["dq"], 1e-13, "packed dQ")
+        _close(out["dk"][k0:k1], one["dk"], 1e-13, "packed dK")
+        _close(out["dv"][k0:k1], one["dv"], 1e-13, "packed dV")
+
+
+def pin_window_is_local(ref):
+    wnd = 4
+    w = small_case([12], heads_q=1, heads_kv=1, head_dim=3, window=wnd, seed=10)
+    x = make_inputs(w)
+    out = _call(ref, w, x)
+    for i in range(wnd - 1, 12):
+        sl = slice(i - wnd + 1, i + 1)
+        cu = np.array([0, wnd], np.int32)
+        part = ref.sdpa_reference(x["q"][sl], x["k"][sl], x["v"][sl], x["do"][sl], cu, cu,
+                                  w.scale, INT32_MAX, True)
+        _close(out["o"][i], part["o"][-1], 1e-13, "windowed row = causal over its last w keys")
+        _close(out["lse"][:, i], part["lse"][:, -1], 1e-13, "windowed LSE = causal over slice")
+
+
+def pin_wide_window_is_causal(ref):
+    w = small_case([9, 6], heads_q=2, heads_kv=1, head_dim=3, window=9, seed=12)
+    x = make_inputs(w)
+    a = _call(ref, w, x)
+    c = _call(ref, w, x, window=INT32_MAX)
+    for key in a:
+        assert np.array_equal(a[key], c[key]), f"window >= N vs causal {key}"
+
+
+ALL_PINS = [pin_finite_differences, pin_loop, pin_window_one, pin_scale_zero,
+            pin_hand_example, pin_softmax_rows, pin_shift_identities, pin_gqa_is_repeated_mha,
+            pin_packed_is_concatenation, pin_window_is_local, pin_wide_window_is_causal]

@@ -1,0 +1,65 @@
+"""The oracle against what the pages and the mathematics fix (no GPU)."""
+import numpy as np
+import pytest
+
+import oracle_pins as pins
+from oracle import dense
+from sliding_window_flash_amd.workloads import INT32_MAX, make_inputs, small_case
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(dense)
+
+
+def test_sampled_rows_match_full_reference():
+    w = small_case([150, 90, 0, 70], [180, 90, 5, 70], heads_q=4, heads_kv=2, head_dim=16,
+                   window=40, seed=21)
+    x = make_inputs(w)
+    args = (x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale, w.window, w.causal)
+    full = dense.sdpa_reference(*args, panel_rows=37)
+    rng = np.random.default_rng(0)
+    toks = rng.integers(0, w.total_q, 25)
+    heads = rng.integers(0, w.heads_q, 25)
+    rows = dense.sdpa_query_rows(*args, toks, heads)
+    np.testing.assert_allclose(rows["o"], full["o"][toks, heads], atol=1e-13)
+    np.testing.assert_allclose(rows["lse"], full["lse"][heads, toks], atol=1e-13)
+    np.testing.assert_allclose(rows["delta"], full["delta"][heads, toks], atol=1e-13)
+    np.testing.assert_allclose(rows["dq"], full["dq"][toks, heads], atol=1e-13)
+    ktoks = np.concatenate([rng.integers(0, w.total_k, 20), [0, 179, 180, 275]])
+    kh = rng.integers(0, w.heads_kv, ktoks.size)
+    keys = dense.sdpa_key_rows(*args, ktoks, kh, panel_rows=11)
+    np.testing.assert_allclose(keys["dk"], full["dk"][ktoks, kh], atol=1e-13)
+    np.testing.assert_allclose(keys["dv"], full["dv"][ktoks, kh], atol=1e-13)
+
+
+def test_unvisited_keys_get_exact_zero():
+    # fewer queries than keys with a short window: the first keys are seen by nobody
+    w = small_case([4], [20], heads_q=2, heads_kv=1, head_dim=3, window=3, seed=22)
+    x = make_inputs(w)
+    out = dense.sdpa_reference(x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"],
+                               w.scale, w.window, w.causal)
+    assert np.all(out["dk"][:14] == 0) and np.all(out["dv"][:14] == 0)
+    assert np.all(np.abs(out["dv"][14:]).sum(-1) > 0)
+
+
+def test_empty_rows_convention():
+    # a sequence with queries but no keys: O = 0, LSE = -inf, dQ = 0
+    w = small_case([3], [0], heads_q=1, heads_kv=1, head_dim=2, seed=23)
+    x = make_inputs(w)
+    out = dense.sdpa_reference(x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"],
+                               w.scale, INT32_MAX, True)
+    assert np.all(out["o"] == 0) and np.all(np.isneginf(out["lse"])) and np.all(out["dq"] == 0)
+
+
+def test_window_without_causal_is_refused():
+    with pytest.raises(ValueError):
+        dense.visible_cells(4, 4, 2, False)
+
+
+def test_host_ram_guard_refuses_up_front():
+    w = small_case([64], heads_q=1, heads_kv=1, head_dim=4, seed=24)
+    x = make_inputs(w)
+    with pytest.raises(dense.HostRamExceeded):
+        dense.sdpa_reference(x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale,
+                             8, True, ram_ceiling=1024)

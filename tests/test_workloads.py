@@ -1,0 +1,42 @@
+"""The synthetic workloads use the shapes the pages print (tests/golden)."""
+import json
+import os
+
+import numpy as np
+
+from sliding_window_flash_amd import workloads as W
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_shapes.json")))
+
+
+def test_window_and_token_counts_come_from_the_pages():
+    assert W.SWA_32K.window == GOLDEN["sliding_window_tokens"]["value"]
+    assert W.SWA_32K.max_seqlen_q in GOLDEN["memory_probe_tokens"]["value"]
+    op = GOLDEN["op_timing_shape"]["value"]
+    c = W.CAUSAL_8K
+    assert (c.batch, c.heads_q, c.heads_kv, c.max_seqlen_q, c.head_dim) == (
+        op["batch"], op["heads_q"], op["heads_kv"], op["tokens"], op["head_dim"])
+    assert c.window >= c.max_seqlen_k  # plain causal
+
+
+def test_ragged_lengths_follow_the_corpus_statistics():
+    corpus = GOLDEN["corpus_lengths"]["value"]
+    v = W.VARLEN_4
+    assert v.batch == corpus["per_step"]
+    assert v.lengths_q == (4709, 3510, 6430, 9368)  # seed 5, numpy default_rng
+    assert all(W.LEN_MIN <= n <= corpus["longest"] for n in v.lengths_q)
+    # the lognormal's mean matches the corpus mean to within 1%
+    mean = np.exp(W.LOGNORMAL_MU + W.LOGNORMAL_SIGMA ** 2 / 2)
+    assert abs(mean - corpus["mean"]) / corpus["mean"] < 0.01
+
+
+def test_inputs_are_seeded_and_bf16_representable():
+    a = W.make_inputs(W.TINY_F32)
+    b = W.make_inputs(W.TINY_F32)
+    for k in a:
+        assert np.array_equal(a[k], b[k])
+    w = W.small_case([33], heads_q=2, heads_kv=1, head_dim=8, dtype="bf16", do_scale=0.1, seed=3)
+    x = W.make_inputs(w)
+    for k in ("q", "k", "v", "do"):
+        bits = x[k].view(np.uint32)
+        assert np.all(bits & 0xFFFF == 0), k
