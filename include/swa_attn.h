@@ -1,0 +1,155 @@
+/*
+ * swa_attn.h - C ABI of the sliding-window flash-attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (the pages it follows are cited by title and
+ * section):
+ *
+ *   Tiled, memory-linear scaled-dot-product attention, forward and backward,
+ *   with causal and sliding-window masks, grouped-query heads and ragged packed
+ *   batches. The forward saves only O and the per-row log-sum-exp; the backward
+ *   recomputes score tiles from them and from D = rowsum(dO * O), and never
+ *   holds the full score matrix ("Off NVIDIA, you fix the platform yourself",
+ *   sections "What was broken?" and "What did fixing it take?"; the
+ *   mlx-train-perf README, flash-attention passage: O(N) saved state, the
+ *   output and the log-sum-exp, tiles recomputed in the backward).
+ *
+ *   Visibility. Sequence b has L_q query and L_k key tokens, L_q <= L_k;
+ *   query i sits at key position p = i + L_k - L_q. Key j is visible to query
+ *   i iff j <= p and p - j < window (causal), or always (non-causal, which
+ *   requires window >= max_seqlen_k). window = 1 sees only the token itself.
+ *   Key tiles lying wholly outside a query tile's window are skipped; cells on
+ *   the window edge are masked ("What did fixing it take?": skip blocks
+ *   entirely outside the window, mask the cells at its edge). A query tile's
+ *   first visited key tile need not be tile zero, and key tiles that no query
+ *   sees get exact-zero dK and dV (same section: the two assumptions that
+ *   broke silently).
+ *
+ * Layouts (all row-major, contiguous, device memory, 16-byte aligned):
+ *   Q, O, dO, dQ : [total_q, heads_q, head_dim]
+ *   K, V, dK, dV : [total_k, heads_kv, head_dim]
+ *   LSE          : [heads_q, total_q] fp32, natural log of the scaled scores
+ *   cu_seqlens_q : [batch + 1] int32, cu_seqlens_q[0] = 0, last = total_q
+ *   cu_seqlens_k : [batch + 1] int32, likewise with total_k
+ *   Head h of Q uses KV head h / (heads_q / heads_kv) (contiguous groups).
+ *
+ * Ownership: the caller owns every buffer, including the backward workspace.
+ * The library allocates no device memory and keeps no state between calls, so
+ * all device memory is visible to the caller's allocator. Every element of
+ * every output is written (zeros where the definition gives zero): outputs
+ * need no clearing.
+ *
+ * Execution: calls enqueue kernels on `stream` (a hipStream_t; NULL = the
+ * default stream) and return. They never synchronise, copy between host and
+ * device or read device memory on the host. They are reentrant.
+ *
+ * Errors: every argument check happens before any launch and returns a status
+ * code; nothing is launched on error. Unsupported inputs are refused up front,
+ * never silently routed elsewhere (the mlx-train-perf README's refusal table:
+ * unsupported configurations raise at enable time rather than fail mid-run;
+ * "auto" never silently downgrades). There is no fallback path and no
+ * exception crosses this boundary.
+ *
+ * Preconditions the host cannot check without reading device memory:
+ * cu_seqlens are non-decreasing, every sequence has L_q <= L_k, and
+ * L_q <= max_seqlen_q, L_k <= max_seqlen_k. If L_q <= L_k is violated,
+ * queries with no visible key get O = 0, LSE = -inf and dQ = 0.
+ */
+#ifndef SWA_ATTN_H
+#define SWA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_F32 = 0,  /* Q, K, V, O, dO, dQ, dK, dV are float32 */
+  ATTN_BF16 = 1  /* ... are bfloat16; accumulation and score tiles stay fp32 */
+} attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* sizes inconsistent (batch < 1, heads_q % heads_kv, totals ...) */
+  ATTN_ERR_WINDOW = 3,      /* window < 1 */
+  ATTN_ERR_UNSUPPORTED = 4, /* head_dim not 64/128, unknown dtype, window without causal */
+  ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than attn_bwd_workspace_bytes */
+  ATTN_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
+  ATTN_ERR_ALIGN = 7        /* a tensor pointer is not 16-byte aligned */
+} attn_status_t;
+
+typedef struct {
+  int32_t batch;        /* B >= 1 packed sequences */
+  int32_t heads_q;      /* query heads, a multiple of heads_kv */
+  int32_t heads_kv;     /* key/value heads; G = heads_q / heads_kv queries share one */
+  int32_t head_dim;     /* 64 or 128 */
+  int32_t total_q;      /* cu_seqlens_q[B] */
+  int32_t total_k;      /* cu_seqlens_k[B] */
+  int32_t max_seqlen_q; /* >= every L_q; sizes the launch grid (no device reads) */
+  int32_t max_seqlen_k; /* >= every L_k */
+  int32_t window;       /* >= 1; any value >= max_seqlen_k (e.g. INT32_MAX) is no window */
+  int32_t causal;       /* 1 causal; 0 full attention (then window >= max_seqlen_k) */
+  float scale;          /* softmax scale, e.g. 1/sqrt(head_dim) */
+  int32_t dtype;        /* attn_dtype_t */
+} attn_params_t;
+
+/* Forward. Writes O [total_q, heads_q, head_dim] (dtype) and LSE [heads_q,
+ * total_q] (fp32). */
+attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, const void* v,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o,
+                       float* lse, void* stream);
+
+/* Bytes of device workspace attn_bwd needs for these parameters (D = rowsum(dO * O),
+ * fp32 [heads_q, total_q], 256-byte aligned). 0 if the parameters are invalid. */
+size_t attn_bwd_workspace_bytes(const attn_params_t* p);
+
+/* Backward: the vector-Jacobian product of sum(O * dO). Reads Q, K, V, O, LSE
+ * (as written by attn_fwd with the same parameters) and dO; writes dQ, dK, dV
+ * (dtype) in full. `workspace` must hold attn_bwd_workspace_bytes(p) bytes;
+ * its contents on entry do not matter. */
+attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v,
+                       const void* o, const float* lse, const void* dout,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dq,
+                       void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* attn_status_str(attn_status_t s);
+
+/* Validate parameters without launching anything (the same checks attn_fwd and
+ * attn_bwd make first). Pointers are not inspected. */
+attn_status_t attn_check_params(const attn_params_t* p);
+
+/* Tile sizes the compiled kernels use for (head_dim, dtype): query rows per
+ * forward/dQ tile, key rows per forward/dQ step, key rows per dK/dV tile and
+ * query rows per dK/dV step. Returns ATTN_ERR_UNSUPPORTED for an unsupported
+ * pair. Host only. */
+attn_status_t attn_tile_sizes(int32_t head_dim, int32_t dtype, int32_t* fwd_bm,
+                              int32_t* fwd_bn, int32_t* bwd_bn, int32_t* bwd_bm);
+
+/* Block-range scheduler, host build (the kernels run the same code). For query
+ * tile qb of sequence b (tile = rows [qb*bm, qb*bm+bm)), the range of key tiles
+ * of size bn the kernels visit: [*kb_lo, *kb_hi] (empty when *kb_lo > *kb_hi),
+ * and the sub-range [*full_lo, *full_hi] of tiles in which every cell is visible
+ * (no per-cell mask needed; empty when *full_lo > *full_hi). cu_seqlens_q/k are
+ * HOST arrays here. */
+attn_status_t attn_query_tile_range(const attn_params_t* p, const int32_t* cu_seqlens_q_host,
+                                    const int32_t* cu_seqlens_k_host, int32_t b, int32_t qb,
+                                    int32_t bm, int32_t bn, int32_t* kb_lo, int32_t* kb_hi,
+                                    int32_t* full_lo, int32_t* full_hi);
+
+/* Key-major counterpart used by the dK/dV kernel: for key tile kb of sequence
+ * b (size bn), the query tiles of size bm that see it: [*qb_lo, *qb_hi], empty
+ * when *qb_lo > *qb_hi (then dK and dV of that tile are written as zeros). */
+attn_status_t attn_key_tile_range(const attn_params_t* p, const int32_t* cu_seqlens_q_host,
+                                  const int32_t* cu_seqlens_k_host, int32_t b, int32_t kb,
+                                  int32_t bn, int32_t bm, int32_t* qb_lo, int32_t* qb_hi);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_ATTN_H */

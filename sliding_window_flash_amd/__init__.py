@@ -1,0 +1,211 @@
+"""Sliding-window flash attention for MI355X (gfx950): Python binding.
+
+A thin ctypes layer over the C ABI in include/swa_attn.h (libswa_attn.so,
+built in-tree by ``sliding_window_flash_amd.build``). It marshals arguments
+only: every step of the forward and backward runs in the HIP kernels. PyTorch
+supplies device memory and the stream. There is no CPU path: if the library
+is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libswa_attn.so")
+
+ATTN_F32, ATTN_BF16 = 0, 1
+INT32_MAX = 2**31 - 1
+
+STATUS = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_WINDOW",
+    4: "ATTN_ERR_UNSUPPORTED", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP", 7: "ATTN_ERR_ALIGN",
+}
+
+EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
+            "attn_check_params", "attn_tile_sizes", "attn_query_tile_range",
+            "attn_key_tile_range")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_status_str(status)})")
+
+
+class AttnParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("total_q", ctypes.c_int32), ("total_k", ctypes.c_int32),
+        ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_k", ctypes.c_int32),
+        ("window", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library. Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m sliding_window_flash_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(AttnParams)
+        vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+        L.attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.attn_fwd.restype = ctypes.c_int
+        L.attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.attn_bwd.restype = ctypes.c_int
+        L.attn_bwd_workspace_bytes.argtypes = [P]
+        L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_status_str.argtypes = [ctypes.c_int]
+        L.attn_status_str.restype = ctypes.c_char_p
+        L.attn_check_params.argtypes = [P]
+        L.attn_check_params.restype = ctypes.c_int
+        L.attn_tile_sizes.argtypes = [ctypes.c_int32, ctypes.c_int32, i32p, i32p, i32p, i32p]
+        L.attn_tile_sizes.restype = ctypes.c_int
+        L.attn_query_tile_range.argtypes = [P, i32p, i32p, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, i32p, i32p, i32p, i32p]
+        L.attn_query_tile_range.restype = ctypes.c_int
+        L.attn_key_tile_range.argtypes = [P, i32p, i32p, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, i32p, i32p]
+        L.attn_key_tile_range.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def _status_str(status: int) -> str:
+    try:
+        return lib().attn_status_str(status).decode()
+    except Exception:  # pragma: no cover - only while reporting another error
+        return "?"
+
+
+def make_params(*, batch, heads_q, heads_kv, head_dim, total_q, total_k, max_seqlen_q,
+                max_seqlen_k, window=INT32_MAX, causal=True, scale=None, dtype=ATTN_BF16) -> AttnParams:
+    if scale is None:
+        scale = head_dim ** -0.5
+    return AttnParams(int(batch), int(heads_q), int(heads_kv), int(head_dim), int(total_q),
+                      int(total_k), int(max_seqlen_q), int(max_seqlen_k),
+                      int(min(window, INT32_MAX)), int(bool(causal)), float(scale), int(dtype))
+
+
+def check_params(p: AttnParams) -> int:
+    return lib().attn_check_params(ctypes.byref(p))
+
+
+def workspace_bytes(p: AttnParams) -> int:
+    return int(lib().attn_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def tile_sizes(head_dim: int, dtype: int) -> Tuple[int, int, int, int]:
+    out = [ctypes.c_int32() for _ in range(4)]
+    st = lib().attn_tile_sizes(head_dim, dtype, *[ctypes.byref(x) for x in out])
+    if st:
+        raise AttnError(st, "attn_tile_sizes")
+    return tuple(x.value for x in out)
+
+
+def _i32_array(xs):
+    arr = (ctypes.c_int32 * len(xs))(*[int(x) for x in xs])
+    return arr
+
+
+def query_tile_range(p: AttnParams, cu_q, cu_k, b: int, qb: int, bm: int, bn: int):
+    out = [ctypes.c_int32() for _ in range(4)]
+    st = lib().attn_query_tile_range(ctypes.byref(p), _i32_array(cu_q), _i32_array(cu_k), b, qb,
+                                     bm, bn, *[ctypes.byref(x) for x in out])
+    if st:
+        raise AttnError(st, "attn_query_tile_range")
+    return tuple(x.value for x in out)
+
+
+def key_tile_range(p: AttnParams, cu_q, cu_k, b: int, kb: int, bn: int, bm: int):
+    out = [ctypes.c_int32() for _ in range(2)]
+    st = lib().attn_key_tile_range(ctypes.byref(p), _i32_array(cu_q), _i32_array(cu_k), b, kb,
+                                   bn, bm, *[ctypes.byref(x) for x in out])
+    if st:
+        raise AttnError(st, "attn_key_tile_range")
+    return tuple(x.value for x in out)
+
+
+# ---------------------------------------------------------------- torch glue
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_ptr(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def params_for(q, k, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=INT32_MAX, causal=True,
+               scale=None) -> AttnParams:
+    torch = _torch()
+    dt = {torch.bfloat16: ATTN_BF16, torch.float32: ATTN_F32}.get(q.dtype)
+    if dt is None:
+        raise AttnError(4, f"dtype {q.dtype}")
+    return make_params(batch=cu_q.numel() - 1, heads_q=q.shape[1], heads_kv=k.shape[1],
+                       head_dim=q.shape[2], total_q=q.shape[0], total_k=k.shape[0],
+                       max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, window=window,
+                       causal=causal, scale=scale, dtype=dt)
+
+
+def _require(t, name):
+    torch = _torch()
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    return t
+
+
+def fwd(q, k, v, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=INT32_MAX, causal=True,
+        scale=None, out=None, lse=None, stream=None):
+    """O [T_q, Hq, d] (q.dtype) and LSE [Hq, T_q] (fp32) through attn_fwd."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (cu_q, "cu_q"), (cu_k, "cu_k")):
+        _require(t, n)
+    p = params_for(q, k, cu_q, cu_k, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
+                   window=window, causal=causal, scale=scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    st = lib().attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_q), _ptr(cu_k),
+                        _ptr(out), _ptr(lse), _stream_ptr(stream))
+    if st:
+        raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def bwd(q, k, v, o, lse, do, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=INT32_MAX,
+        causal=True, scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV through attn_bwd (the VJP of sum(O * dO))."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (do, "do"),
+                 (cu_q, "cu_q"), (cu_k, "cu_k")):
+        _require(t, n)
+    p = params_for(q, k, cu_q, cu_k, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
+                   window=window, causal=causal, scale=scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    nbytes = workspace_bytes(p)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib().attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                        _ptr(cu_q), _ptr(cu_k), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                        workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    if st:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv

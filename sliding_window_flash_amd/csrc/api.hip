@@ -1,0 +1,205 @@
+// C ABI of the attention library: argument checks, then launches on the
+// caller's stream. Declarations and the contract are in include/swa_attn.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/swa_attn.h"
+#include "launch.hpp"
+#include "sched.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// A tensor pointer may be NULL only when the tensor has no elements.
+attn_status_t check_tensor(const void* ptr, int64_t elems, bool vec16) {
+  if (elems == 0) return ATTN_OK;
+  if (ptr == nullptr) return ATTN_ERR_NULL;
+  if (vec16 ? !aligned16(ptr) : !aligned4(ptr)) return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
+swa::AttnArgs base_args(const attn_params_t* p) {
+  swa::AttnArgs a{};
+  a.batch = p->batch;
+  a.heads_q = p->heads_q;
+  a.heads_kv = p->heads_kv;
+  a.total_q = p->total_q;
+  a.total_k = p->total_k;
+  a.max_seqlen_q = p->max_seqlen_q;
+  a.max_seqlen_k = p->max_seqlen_k;
+  a.window = p->window;
+  a.causal = p->causal;
+  a.scale = p->scale;
+  return a;
+}
+
+int64_t q_elems(const attn_params_t* p) { return (int64_t)p->total_q * p->heads_q * p->head_dim; }
+int64_t k_elems(const attn_params_t* p) { return (int64_t)p->total_k * p->heads_kv * p->head_dim; }
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_check_params(const attn_params_t* p) {
+  if (p == nullptr) return ATTN_ERR_NULL;
+  if (p->batch < 1 || p->heads_q < 1 || p->heads_kv < 1 || p->heads_q % p->heads_kv != 0 ||
+      p->total_q < 0 || p->total_k < 0 || p->max_seqlen_q < 0 || p->max_seqlen_k < 0 ||
+      p->max_seqlen_q > p->total_q || p->max_seqlen_k > p->total_k)
+    return ATTN_ERR_SHAPE;
+  if (p->window < 1) return ATTN_ERR_WINDOW;
+  if (p->head_dim != 64 && p->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (p->dtype != ATTN_F32 && p->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (p->causal != 0 && p->causal != 1) return ATTN_ERR_UNSUPPORTED;
+  if (p->causal == 0 && p->window < p->max_seqlen_k) return ATTN_ERR_UNSUPPORTED;
+  if (!isfinite(p->scale)) return ATTN_ERR_SHAPE;
+  // packed element counts must stay addressable
+  if ((int64_t)p->total_q * p->heads_q > INT32_MAX || (int64_t)p->total_k * p->heads_kv > INT32_MAX)
+    return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, const void* v,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o,
+                       float* lse, void* stream) {
+  attn_status_t s = attn_check_params(p);
+  if (s != ATTN_OK) return s;
+  if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return ATTN_ERR_NULL;
+  if (!aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k)) return ATTN_ERR_ALIGN;
+  const int64_t nq = q_elems(p), nk = k_elems(p);
+  if ((s = check_tensor(q, nq, true)) != ATTN_OK) return s;
+  if ((s = check_tensor(k, nk, true)) != ATTN_OK) return s;
+  if ((s = check_tensor(v, nk, true)) != ATTN_OK) return s;
+  if ((s = check_tensor(o, nq, true)) != ATTN_OK) return s;
+  if ((s = check_tensor(lse, (int64_t)p->total_q * p->heads_q, false)) != ATTN_OK) return s;
+  swa::AttnArgs a = base_args(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.out_o = o;
+  a.out_lse = lse;
+  if (swa::launch_fwd(p->dtype, p->head_dim, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+size_t attn_bwd_workspace_bytes(const attn_params_t* p) {
+  if (attn_check_params(p) != ATTN_OK) return 0;
+  const size_t d_bytes = (size_t)p->heads_q * (size_t)p->total_q * sizeof(float);
+  return round_up(d_bytes > 0 ? d_bytes : 1, 256);
+}
+
+attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v,
+                       const void* o, const float* lse, const void* dout,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dq,
+                       void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  attn_status_t s = attn_check_params(p);
+  if (s != ATTN_OK) return s;
+  if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return ATTN_ERR_NULL;
+  if (!aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k)) return ATTN_ERR_ALIGN;
+  const int64_t nq = q_elems(p), nk = k_elems(p);
+  if ((s = check_tensor(q, nq, true)) != ATTN_OK) return s;
+  if ((s = check_tensor(k, nk, true)) != ATTN_OK) return s;
+  if ((s = check_tensor(v, nk, true)) != ATTN_OK) return s;
+  if ((s = check_tensor(o, nq, true)) != ATTN_OK) return s;
+  if ((s = check_tensor(dout, nq, true)) != ATTN_OK) return s;
+  if ((s = check_tensor(lse, (int64_t)p->total_q * p->heads_q, false)) != ATTN_OK) return s;
+  if ((s = check_tensor(dq, nq, true)) != ATTN_OK) return s;
+  if ((s = check_tensor(dk, nk, true)) != ATTN_OK) return s;
+  if ((s = check_tensor(dv, nk, true)) != ATTN_OK) return s;
+  if (workspace == nullptr || workspace_bytes < attn_bwd_workspace_bytes(p)) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  swa::AttnArgs a = base_args(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = static_cast<float*>(workspace);
+  if (swa::launch_bwd(p->dtype, p->head_dim, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+const char* attn_status_str(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "inconsistent sizes";
+    case ATTN_ERR_WINDOW: return "window must be >= 1";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration (head_dim, dtype, or a window without the causal mask)";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP launch error";
+    case ATTN_ERR_ALIGN: return "pointer not aligned (tensors need 16 bytes)";
+  }
+  return "unknown status";
+}
+
+attn_status_t attn_tile_sizes(int32_t head_dim, int32_t dtype, int32_t* fwd_bm, int32_t* fwd_bn,
+                              int32_t* bwd_bn, int32_t* bwd_bm) {
+  if (!fwd_bm || !fwd_bn || !bwd_bn || !bwd_bm) return ATTN_ERR_NULL;
+  int a, b, c, d;
+  if (!swa::tile_sizes(dtype, head_dim, &a, &b, &c, &d)) return ATTN_ERR_UNSUPPORTED;
+  *fwd_bm = a;
+  *fwd_bn = b;
+  *bwd_bn = c;
+  *bwd_bm = d;
+  return ATTN_OK;
+}
+
+static attn_status_t seq_geom(const attn_params_t* p, const int32_t* cq, const int32_t* ck, int32_t b,
+                              swa::SeqGeom* g) {
+  attn_status_t s = attn_check_params(p);
+  if (s != ATTN_OK) return s;
+  if (!cq || !ck) return ATTN_ERR_NULL;
+  if (b < 0 || b >= p->batch) return ATTN_ERR_SHAPE;
+  const int64_t lq = (int64_t)cq[b + 1] - cq[b], lk = (int64_t)ck[b + 1] - ck[b];
+  if (lq < 0 || lk < 0) return ATTN_ERR_SHAPE;
+  *g = swa::SeqGeom{lq, lk, p->window, p->causal != 0};
+  return ATTN_OK;
+}
+
+attn_status_t attn_query_tile_range(const attn_params_t* p, const int32_t* cu_seqlens_q_host,
+                                    const int32_t* cu_seqlens_k_host, int32_t b, int32_t qb,
+                                    int32_t bm, int32_t bn, int32_t* kb_lo, int32_t* kb_hi,
+                                    int32_t* full_lo, int32_t* full_hi) {
+  if (!kb_lo || !kb_hi || !full_lo || !full_hi) return ATTN_ERR_NULL;
+  if (bm < 1 || bn < 1 || qb < 0) return ATTN_ERR_SHAPE;
+  swa::SeqGeom g;
+  attn_status_t s = seq_geom(p, cu_seqlens_q_host, cu_seqlens_k_host, b, &g);
+  if (s != ATTN_OK) return s;
+  const swa::TileRange r = swa::query_tile_keys(g, qb, bm, bn);
+  *kb_lo = r.lo;
+  *kb_hi = r.hi;
+  *full_lo = r.full_lo;
+  *full_hi = r.full_hi;
+  return ATTN_OK;
+}
+
+attn_status_t attn_key_tile_range(const attn_params_t* p, const int32_t* cu_seqlens_q_host,
+                                  const int32_t* cu_seqlens_k_host, int32_t b, int32_t kb,
+                                  int32_t bn, int32_t bm, int32_t* qb_lo, int32_t* qb_hi) {
+  if (!qb_lo || !qb_hi) return ATTN_ERR_NULL;
+  if (bm < 1 || bn < 1 || kb < 0) return ATTN_ERR_SHAPE;
+  swa::SeqGeom g;
+  attn_status_t s = seq_geom(p, cu_seqlens_q_host, cu_seqlens_k_host, b, &g);
+  if (s != ATTN_OK) return s;
+  const swa::TileRange r = swa::key_tile_queries(g, kb, bn, bm);
+  *qb_lo = r.lo;
+  *qb_hi = r.hi;
+  return ATTN_OK;
+}
+
+}  // extern "C"

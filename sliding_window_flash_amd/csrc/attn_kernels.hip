@@ -1,0 +1,471 @@
+// Forward and backward attention kernels for gfx950, and their launchers.
+//
+// Forward (per query tile of BM rows, one query head): S^T = K Q^T on MFMA,
+// scale, mask edge cells, online softmax per query (exp2 domain), O^T += V^T P^T
+// on MFMA; epilogue writes O and the natural-log LSE. The mlx-train-perf
+// README's flash-attention passage describes this saved state (O and the
+// log-sum-exp) and the tile recompute in the backward.
+//
+// Backward, split into three launches on the caller's stream:
+//   delta: D = rowsum(dO * O) per (token, head), fp32 workspace.
+//   dq:    per query tile: recompute S^T, dP^T = V dO^T, P = exp(S - LSE),
+//          dS = P (dP - D), dQ^T += K^T dS^T. The accumulator is cleared
+//          before the first visited key tile, which under a window is not
+//          tile zero ("Off NVIDIA, you fix the platform yourself", section
+//          "What did fixing it take?").
+//   dkdv:  per key tile of BN keys and KV head: K and V stay in registers; for
+//          each query head of the group and each query tile that sees the key
+//          tile: S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS. A key
+//          tile no query sees writes exact zeros (same section: some key
+//          blocks are never visited).
+// Score tiles S, P, dP, dS stay fp32 in registers; P and dS are rounded to
+// bf16 only as MFMA operands (the lab record's "Attention gradient error, real
+// Gemma 4 activations" entry: bf16 scratch scores cost about fourfold in dQ
+// error against fp32 score tiles).
+#include <math.h>
+
+#include "kernel_common.hpp"
+#include "launch.hpp"
+#include "sched.hpp"
+
+namespace swa {
+
+// Store 4 consecutive fp32 values as T (8 bytes for bf16, 16 for fp32).
+template <typename T> __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void store4<bf16>(bf16* p, float a, float b, float c, float d) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+template <> __device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  f32x4 v = {a, b, c, d};
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+
+// Write a D/32-block accumulator set (one query or key per lane, rows = head
+// dim) to row pointer `row`, multiplied by `mul`.
+template <typename T, int D>
+__device__ __forceinline__ void store_acc_rows(T* row, const f32x16 (&acc)[D / 32], float mul, int half) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * dt + 8 * r4 + 4 * half;
+      store4<T>(row + d, acc[dt][4 * r4] * mul, acc[dt][4 * r4 + 1] * mul, acc[dt][4 * r4 + 2] * mul,
+                acc[dt][4 * r4 + 3] * mul);
+    }
+}
+
+struct QueryItem {
+  int qb, h, b, q0, lq, k0, lk;
+};
+
+// Query-major work decode. Tiles with more rows of work come first (for the
+// causal mask, late query tiles see the most keys).
+__device__ __forceinline__ QueryItem decode_query_item(const AttnArgs& a, int bm) {
+  QueryItem it;
+  const int nqb = (a.max_seqlen_q + bm - 1) / bm;
+  const int per = a.heads_q * a.batch;
+  const int id = blockIdx.x;
+  it.qb = nqb - 1 - id / per;
+  const int rest = id % per;
+  it.h = rest % a.heads_q;
+  it.b = rest / a.heads_q;
+  it.q0 = a.cu_q[it.b];
+  it.lq = a.cu_q[it.b + 1] - it.q0;
+  it.k0 = a.cu_k[it.b];
+  it.lk = a.cu_k[it.b + 1] - it.k0;
+  return it;
+}
+
+// ---------------------------------------------------------------- forward
+template <typename T, int D, int BM, int BN>
+__global__ void __launch_bounds__(BM * 2) fwd_kernel(AttnArgs a) {
+  constexpr int NT = BM * 2;
+  using KTile = LdsTile<T, BN, D>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * KTile::kBytes];
+  char* ks = smem;
+  char* vs = smem + KTile::kBytes;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
+  const QueryItem it = decode_query_item(a, BM);
+  if (it.qb * BM >= it.lq) return;
+  const int g = it.h / (a.heads_q / a.heads_kv);
+  const SeqGeom sg{it.lq, it.lk, a.window, a.causal != 0};
+  const TileRange kr = query_tile_keys(sg, it.qb, BM, BN);
+
+  const int64_t qstride = (int64_t)a.heads_q * D;
+  const int64_t kstride = (int64_t)a.heads_kv * D;
+  const T* __restrict__ Q = static_cast<const T*>(a.q);
+  const T* __restrict__ K = static_cast<const T*>(a.k);
+  const T* __restrict__ V = static_cast<const T*>(a.v);
+
+  const int i = it.qb * BM + w * 32 + l32;  // this lane's query row
+  const bool row_ok = i < it.lq;
+  Frag<T> qf[D / 16];
+  {
+    const T* qrow = Q + (int64_t)(it.q0 + (row_ok ? i : 0)) * qstride + it.h * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qf[s] = row_ok ? global_frag<T>(qrow + 16 * s) : zero_frag<T>();
+  }
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+  float m = -INFINITY, lsum = 0.f;
+  const float c = a.scale * kLog2e;
+
+  for (int kb = kr.lo; kb <= kr.hi; ++kb) {
+    __syncthreads();
+    const int kvalid = min(BN, it.lk - kb * BN);
+    const int64_t koff = (int64_t)(it.k0 + kb * BN) * kstride + g * D;
+    load_tile<T, BN, D, NT>(ks, K + koff, kstride, kvalid, tid);
+    load_tile<T, BN, D, NT>(vs, V + koff, kstride, kvalid, tid);
+    __syncthreads();
+
+    f32x16 s[BN / 32];
+#pragma unroll
+    for (int kt = 0; kt < BN / 32; ++kt) {
+      s[kt] = f32x16{};
+#pragma unroll
+      for (int ss = 0; ss < D / 16; ++ss)
+        mma(s[kt], row_frag<T, BN, D>(ks, 32 * kt + l32, 2 * ss + half), qf[ss]);
+    }
+    const bool edge = !(kr.full_lo <= kb && kb <= kr.full_hi);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < BN / 32; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[kt][r] * c;
+        if (edge && !cell_visible(sg, i, (int64_t)kb * BN + 32 * kt + acc_row(r, half))) x = -INFINITY;
+        s[kt][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, xor32(mx));
+    const float mnew = fmaxf(m, mx);
+    const float mref = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = fast_exp2(m - mref);
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < BN / 32; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = fast_exp2(s[kt][r] - mref);
+        s[kt][r] = pv;
+        rs += pv;
+      }
+    lsum = lsum * alpha + rs;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+    m = mnew;
+#pragma unroll
+    for (int u = 0; u < BN / 16; ++u) {
+      const Frag<T> pf = acc_frag<T>(s[u >> 1], u & 1);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) mma(acc[dt], col_frag<T, BN, D>(vs, 16 * u, 32 * dt, lane), pf);
+    }
+  }
+
+  const float ltot = lsum + xor32(lsum);
+  if (row_ok) {
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    T* orow = static_cast<T*>(a.out_o) + (int64_t)(it.q0 + i) * qstride + it.h * D;
+    store_acc_rows<T, D>(orow, acc, inv, half);
+    if (half == 0)
+      a.out_lse[(int64_t)it.h * a.total_q + it.q0 + i] =
+          ltot > 0.f ? (m + fast_log2(ltot)) * kLn2 : -INFINITY;
+  }
+}
+
+// ------------------------------------------------------ backward: D = rowsum(dO*O)
+template <typename T, int D>
+__global__ void __launch_bounds__(256) bwd_delta_kernel(AttnArgs a) {
+  constexpr int LPR = D / 8;  // lanes per (token, head) row, 8 elements each
+  const int64_t rows = (int64_t)a.total_q * a.heads_q;
+  const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int sub = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const Frag<T> o = global_frag<T>(static_cast<const T*>(a.o) + row * D + sub * 8);
+    const Frag<T> d = global_frag<T>(static_cast<const T*>(a.dout) + row * D + sub * 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += to_f32(o.v[j]) * to_f32(d.v[j]);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (sub == 0 && row < rows) {
+    const int64_t t = row / a.heads_q, h = row % a.heads_q;
+    a.delta[h * a.total_q + t] = acc;
+  }
+}
+
+// ------------------------------------------------------------- backward: dQ
+template <typename T, int D, int BM, int BN>
+__global__ void __launch_bounds__(BM * 2) bwd_dq_kernel(AttnArgs a) {
+  constexpr int NT = BM * 2;
+  using KTile = LdsTile<T, BN, D>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * KTile::kBytes];
+  char* ks = smem;
+  char* vs = smem + KTile::kBytes;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
+  const QueryItem it = decode_query_item(a, BM);
+  if (it.qb * BM >= it.lq) return;
+  const int g = it.h / (a.heads_q / a.heads_kv);
+  const SeqGeom sg{it.lq, it.lk, a.window, a.causal != 0};
+  const TileRange kr = query_tile_keys(sg, it.qb, BM, BN);
+
+  const int64_t qstride = (int64_t)a.heads_q * D;
+  const int64_t kstride = (int64_t)a.heads_kv * D;
+  const T* __restrict__ K = static_cast<const T*>(a.k);
+  const T* __restrict__ V = static_cast<const T*>(a.v);
+
+  const int i = it.qb * BM + w * 32 + l32;
+  const bool row_ok = i < it.lq;
+  Frag<T> qf[D / 16], df[D / 16];
+  float lse2 = INFINITY, dlt = 0.f;
+  {
+    const int64_t roff = (int64_t)(it.q0 + (row_ok ? i : 0)) * qstride + it.h * D + 8 * half;
+    const T* qrow = static_cast<const T*>(a.q) + roff;
+    const T* drow = static_cast<const T*>(a.dout) + roff;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      qf[s] = row_ok ? global_frag<T>(qrow + 16 * s) : zero_frag<T>();
+      df[s] = row_ok ? global_frag<T>(drow + 16 * s) : zero_frag<T>();
+    }
+    if (row_ok) {
+      const float l = a.lse[(int64_t)it.h * a.total_q + it.q0 + i];
+      lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+      dlt = a.delta[(int64_t)it.h * a.total_q + it.q0 + i];
+    }
+  }
+  // cleared before the first visited key tile (kr.lo), not on key tile zero
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+  const float c = a.scale * kLog2e;
+
+  for (int kb = kr.lo; kb <= kr.hi; ++kb) {
+    __syncthreads();
+    const int kvalid = min(BN, it.lk - kb * BN);
+    const int64_t koff = (int64_t)(it.k0 + kb * BN) * kstride + g * D;
+    load_tile<T, BN, D, NT>(ks, K + koff, kstride, kvalid, tid);
+    load_tile<T, BN, D, NT>(vs, V + koff, kstride, kvalid, tid);
+    __syncthreads();
+
+    const bool edge = !(kr.full_lo <= kb && kb <= kr.full_hi);
+    f32x16 s[BN / 32];
+#pragma unroll
+    for (int kt = 0; kt < BN / 32; ++kt) {
+      f32x16 dp = f32x16{};
+      s[kt] = f32x16{};
+#pragma unroll
+      for (int ss = 0; ss < D / 16; ++ss) {
+        mma(s[kt], row_frag<T, BN, D>(ks, 32 * kt + l32, 2 * ss + half), qf[ss]);
+        mma(dp, row_frag<T, BN, D>(vs, 32 * kt + l32, 2 * ss + half), df[ss]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = fast_exp2(s[kt][r] * c - lse2);
+        if (edge && !cell_visible(sg, i, (int64_t)kb * BN + 32 * kt + acc_row(r, half))) pv = 0.f;
+        s[kt][r] = pv * (dp[r] - dlt);  // dS
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < BN / 16; ++u) {
+      const Frag<T> dsf = acc_frag<T>(s[u >> 1], u & 1);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) mma(acc[dt], col_frag<T, BN, D>(ks, 16 * u, 32 * dt, lane), dsf);
+    }
+  }
+  if (row_ok) {
+    T* row = static_cast<T*>(a.dq) + (int64_t)(it.q0 + i) * qstride + it.h * D;
+    store_acc_rows<T, D>(row, acc, a.scale, half);
+  }
+}
+
+// ---------------------------------------------------------- backward: dK, dV
+template <typename T, int D, int BN, int BM>
+__global__ void __launch_bounds__(BN * 2) bwd_dkdv_kernel(AttnArgs a) {
+  constexpr int NT = BN * 2;
+  using QTile = LdsTile<T, BM, D>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * QTile::kBytes + 2 * BM * 4];
+  char* qs = smem;
+  char* dos = smem + QTile::kBytes;
+  float* lse2s = reinterpret_cast<float*>(smem + 2 * QTile::kBytes);
+  float* dlts = lse2s + BM;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
+  const int nkb = (a.max_seqlen_k + BN - 1) / BN;
+  (void)nkb;
+  const int per = a.heads_kv * a.batch;
+  const int kb = blockIdx.x / per;
+  const int rest = blockIdx.x % per;
+  const int g = rest % a.heads_kv;
+  const int b = rest / a.heads_kv;
+  const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
+  const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
+  if (kb * BN >= lk) return;
+  const int grp = a.heads_q / a.heads_kv;
+  const SeqGeom sg{lq, lk, a.window, a.causal != 0};
+  const TileRange qr = key_tile_queries(sg, kb, BN, BM);
+
+  const int64_t qstride = (int64_t)a.heads_q * D;
+  const int64_t kstride = (int64_t)a.heads_kv * D;
+  const int j = kb * BN + w * 32 + l32;  // this lane's key
+  const bool key_ok = j < lk;
+  Frag<T> kf[D / 16], vf[D / 16];
+  {
+    const int64_t roff = (int64_t)(k0 + (key_ok ? j : 0)) * kstride + g * D + 8 * half;
+    const T* krow = static_cast<const T*>(a.k) + roff;
+    const T* vrow = static_cast<const T*>(a.v) + roff;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      kf[s] = key_ok ? global_frag<T>(krow + 16 * s) : zero_frag<T>();
+      vf[s] = key_ok ? global_frag<T>(vrow + 16 * s) : zero_frag<T>();
+    }
+  }
+  f32x16 dka[D / 32], dva[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    dka[dt] = f32x16{};
+    dva[dt] = f32x16{};
+  }
+  const float c = a.scale * kLog2e;
+  const T* __restrict__ Qg = static_cast<const T*>(a.q);
+  const T* __restrict__ Dg = static_cast<const T*>(a.dout);
+
+  // An empty range (no query sees this key tile) skips both loops and writes zeros.
+  for (int h = g * grp; h < (g + 1) * grp; ++h) {
+    for (int qb = qr.lo; qb <= qr.hi; ++qb) {
+      __syncthreads();
+      const int qvalid = min(BM, lq - qb * BM);
+      const int64_t qoff = (int64_t)(q0 + qb * BM) * qstride + h * D;
+      load_tile<T, BM, D, NT>(qs, Qg + qoff, qstride, qvalid, tid);
+      load_tile<T, BM, D, NT>(dos, Dg + qoff, qstride, qvalid, tid);
+      for (int t = tid; t < BM; t += NT) {
+        float l2 = INFINITY, dl = 0.f;
+        if (t < qvalid) {
+          const int64_t idx = (int64_t)h * a.total_q + q0 + qb * BM + t;
+          const float l = a.lse[idx];
+          l2 = l == -INFINITY ? INFINITY : l * kLog2e;
+          dl = a.delta[idx];
+        }
+        lse2s[t] = l2;
+        dlts[t] = dl;
+      }
+      __syncthreads();
+
+      const bool edge = !tile_is_full(sg, qb, BM, kb, BN);
+#pragma unroll
+      for (int mt = 0; mt < BM / 32; ++mt) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ss = 0; ss < D / 16; ++ss) {
+          mma(s, row_frag<T, BM, D>(qs, 32 * mt + l32, 2 * ss + half), kf[ss]);
+          mma(dp, row_frag<T, BM, D>(dos, 32 * mt + l32, 2 * ss + half), vf[ss]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rr = 32 * mt + acc_row(r, half);
+          float pv = fast_exp2(s[r] * c - lse2s[rr]);
+          if (edge && !cell_visible(sg, (int64_t)qb * BM + rr, j)) pv = 0.f;
+          s[r] = pv;
+          dp[r] = pv * (dp[r] - dlts[rr]);  // dS
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const Frag<T> pf = acc_frag<T>(s, u);
+          const Frag<T> dsf = acc_frag<T>(dp, u);
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            mma(dva[dt], col_frag<T, BM, D>(dos, 32 * mt + 16 * u, 32 * dt, lane), pf);
+            mma(dka[dt], col_frag<T, BM, D>(qs, 32 * mt + 16 * u, 32 * dt, lane), dsf);
+          }
+        }
+      }
+    }
+  }
+  if (key_ok) {
+    const int64_t roff = (int64_t)(k0 + j) * kstride + g * D;
+    store_acc_rows<T, D>(static_cast<T*>(a.dk) + roff, dka, a.scale, half);
+    store_acc_rows<T, D>(static_cast<T*>(a.dv) + roff, dva, 1.f, half);
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+template <typename T, int D> struct Tiles;
+// bf16 and fp32 share tile shapes: forward / dQ 128 query rows x 64 keys per
+// step (4 waves, 32 queries each); dK/dV 128 keys (4 waves, 32 keys each) x
+// 64 query rows per step.
+template <typename T, int D> struct Tiles {
+  static constexpr int kFwdBM = 128, kFwdBN = 64, kBwdBN = 128, kBwdBM = 64;
+};
+
+template <typename T, int D>
+static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
+  using TL = Tiles<T, D>;
+  const int64_t nqb = (a.max_seqlen_q + TL::kFwdBM - 1) / TL::kFwdBM;
+  const int64_t grid = nqb * a.heads_q * a.batch;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_kernel<T, D, TL::kFwdBM, TL::kFwdBN>), dim3((unsigned)grid),
+                     dim3(TL::kFwdBM * 2), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t st) {
+  using TL = Tiles<T, D>;
+  const int64_t rows = (int64_t)a.total_q * a.heads_q;
+  if (rows > 0) {
+    const int64_t g0 = (rows + (256 / (D / 8)) - 1) / (256 / (D / 8));
+    hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)g0), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nqb = (a.max_seqlen_q + TL::kFwdBM - 1) / TL::kFwdBM;
+    const int64_t g1 = nqb * a.heads_q * a.batch;
+    if (g1 > 0) {
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, TL::kFwdBM, TL::kFwdBN>), dim3((unsigned)g1),
+                         dim3(TL::kFwdBM * 2), 0, st, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  const int64_t nkb = (a.max_seqlen_k + TL::kBwdBN - 1) / TL::kBwdBN;
+  const int64_t g2 = nkb * a.heads_kv * a.batch;
+  if (g2 > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, TL::kBwdBN, TL::kBwdBM>), dim3((unsigned)g2),
+                       dim3(TL::kBwdBN * 2), 0, st, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_fwd(int dtype, int head_dim, const AttnArgs& a, hipStream_t st) {
+  if (dtype == 1 && head_dim == 128) return launch_fwd_t<bf16, 128>(a, st);
+  if (dtype == 1 && head_dim == 64) return launch_fwd_t<bf16, 64>(a, st);
+  if (dtype == 0 && head_dim == 128) return launch_fwd_t<float, 128>(a, st);
+  if (dtype == 0 && head_dim == 64) return launch_fwd_t<float, 64>(a, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd(int dtype, int head_dim, const AttnArgs& a, hipStream_t st) {
+  if (dtype == 1 && head_dim == 128) return launch_bwd_t<bf16, 128>(a, st);
+  if (dtype == 1 && head_dim == 64) return launch_bwd_t<bf16, 64>(a, st);
+  if (dtype == 0 && head_dim == 128) return launch_bwd_t<float, 128>(a, st);
+  if (dtype == 0 && head_dim == 64) return launch_bwd_t<float, 64>(a, st);
+  return hipErrorInvalidValue;
+}
+
+bool tile_sizes(int dtype, int head_dim, int* fwd_bm, int* fwd_bn, int* bwd_bn, int* bwd_bm) {
+  if ((dtype != 0 && dtype != 1) || (head_dim != 64 && head_dim != 128)) return false;
+  using TL = Tiles<bf16, 128>;
+  *fwd_bm = TL::kFwdBM;
+  *fwd_bn = TL::kFwdBN;
+  *bwd_bn = TL::kBwdBN;
+  *bwd_bm = TL::kBwdBM;
+  return true;
+}
+
+}  // namespace swa

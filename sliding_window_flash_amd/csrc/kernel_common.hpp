@@ -1,0 +1,237 @@
+// Shared device building blocks for the gfx950 attention kernels.
+//
+// MFMA: every contraction uses the 32x32 result tile. bf16 operands use
+// v_mfma_f32_32x32x16_bf16 (one instruction per 16-deep step); fp32 operands
+// use eight v_mfma_f32_32x32x2_f32 (true fp32, no reduced-precision mode).
+//
+// Lane layouts (64 lanes; l32 = lane % 32, half = lane / 32):
+//   A operand (M x 16): lane holds row l32, 8 contraction elements
+//   B operand (16 x N): lane holds column l32, 8 contraction elements
+//   result (32 x 32 fp32, 16 registers): lane holds column l32; register r is
+//   row 8*(r/4) + 4*half + r%4.
+// Which 8 contraction indices a lane holds is free as long as A and B agree.
+// A result tile read back as an operand (P or dS) gives, for its 16-deep step
+// u in {0, 1}, the indices 16u + 4*half + {0..3} and 16u + 8 + 4*half + {0..3}
+// (registers 8u..8u+7). Every operand read along the rows of an LDS tile
+// (col_frag) therefore fetches those same indices.
+//
+// LDS tiles hold rows of head_dim elements, unpadded, with 16-byte chunks
+// XOR-swizzled per row so that (a) 16 lanes reading 16 consecutive rows at the
+// same chunk and (b) the 4-row x 4-chunk blocks of a transposing read both
+// touch distinct banks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---- operand fragments -------------------------------------------------
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { float v[8]; };
+
+__device__ __forceinline__ void mma(f32x16& c, const Frag<bf16>& a, const Frag<bf16>& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16& c, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[j], b.v[j], c, 0, 0, 0);
+}
+
+// Registers 8u..8u+7 of a result tile as an operand fragment (P or dS).
+template <typename T> __device__ __forceinline__ Frag<T> acc_frag(const f32x16& c, int u);
+template <> __device__ __forceinline__ Frag<bf16> acc_frag<bf16>(const f32x16& c, int u) {
+  Frag<bf16> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.v[j] = (bf16)c[8 * u + j];  // round to nearest even
+  return f;
+}
+template <> __device__ __forceinline__ Frag<float> acc_frag<float>(const f32x16& c, int u) {
+  Frag<float> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.v[j] = c[8 * u + j];
+  return f;
+}
+
+// Row of a result tile held by register r, for lane half `half`.
+__device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
+
+// ---- element conversion ---------------------------------------------------
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// ---- swizzled LDS tile ------------------------------------------------------
+// ROWS x D elements of T; rows are D*sizeof(T) bytes (a multiple of 16).
+template <typename T, int ROWS, int D> struct LdsTile {
+  static constexpr int kChunks = D * (int)sizeof(T) / 16;   // 16-byte chunks per row
+  static constexpr int kRowBytes = kChunks * 16;
+  static constexpr int kBytes = ROWS * kRowBytes;
+  static constexpr int kElemsPerChunk = 16 / (int)sizeof(T);
+  static_assert(kChunks == 8 || kChunks >= 16, "row must be 128 bytes or >= 256 bytes");
+
+  __device__ static __forceinline__ int swz(int r) {
+    return kChunks >= 16 ? (4 * (r & 3) + ((r >> 2) & 3)) : ((r >> 1) & 7);
+  }
+  // byte offset of chunk c of row r
+  __device__ static __forceinline__ int chunk_off(int r, int c) {
+    return r * kRowBytes + ((c ^ swz(r)) << 4);
+  }
+  // byte offset of element e of row r
+  __device__ static __forceinline__ int elem_off(int r, int e) {
+    const int byte = e * (int)sizeof(T);
+    return chunk_off(r, byte >> 4) + (byte & 15);
+  }
+};
+
+// Cooperative global -> LDS copy of `rows` rows (row r from src + r*stride
+// elements), zero-filling rows >= valid. 16-byte vector loads and stores.
+template <typename T, int ROWS, int D, int NTHREADS>
+__device__ __forceinline__ void load_tile(char* lds, const T* __restrict__ src, int64_t stride,
+                                          int valid, int tid) {
+  using Tile = LdsTile<T, ROWS, D>;
+  constexpr int kTotal = ROWS * Tile::kChunks;
+#pragma unroll
+  for (int idx = tid; idx < kTotal; idx += NTHREADS) {
+    const int r = idx / Tile::kChunks;
+    const int c = idx % Tile::kChunks;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (r < valid)
+      val = *reinterpret_cast<const u32x4*>(src + (int64_t)r * stride + c * Tile::kElemsPerChunk);
+    *reinterpret_cast<u32x4*>(lds + Tile::chunk_off(r, c)) = val;
+  }
+}
+
+// Operand fragment read along a row: row `row`, contraction elements
+// [8*k8, 8*k8+8) of that row.
+template <typename T, int ROWS, int D>
+__device__ __forceinline__ Frag<T> row_frag(const char* lds, int row, int k8) {
+  using Tile = LdsTile<T, ROWS, D>;
+  Frag<T> f;
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(lds + Tile::chunk_off(row, k8));
+    f.v = __builtin_bit_cast(bf16x8, raw);
+  } else {
+    // float vectors, not bit casts of u32x4 elements: the latter is folded to
+    // element 0 by this compiler.
+    const f32x4 a = *reinterpret_cast<const f32x4*>(lds + Tile::chunk_off(row, 2 * k8));
+    const f32x4 b = *reinterpret_cast<const f32x4*>(lds + Tile::chunk_off(row, 2 * k8 + 1));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f.v[j] = a[j];
+      f.v[4 + j] = b[j];
+    }
+  }
+  return f;
+}
+
+// Operand fragment read down a column: the lane's column is nbase + lane%32;
+// the contraction runs over rows kbase + (the 8 indices listed at the top for
+// lane half lane/32). kbase is a multiple of 16.
+template <typename T, int ROWS, int D>
+__device__ __forceinline__ Frag<T> col_frag(const char* lds, int kbase, int nbase, int lane) {
+  using Tile = LdsTile<T, ROWS, D>;
+  const int half = lane >> 5;
+  Frag<T> f;
+  if constexpr (sizeof(T) == 2) {
+    // ds_read_tr16_b64: in each 16-lane group, lane i receives element i%4 of
+    // the 8 bytes addressed by lanes 4e + i/4 (e = 0..3). Lane r of the group
+    // addresses row k0 + r/4 at columns n0 + 4*(r%4) .. +3, so lane i gets rows
+    // k0..k0+3 of column n0 + i.
+    const int r = lane & 15;
+    const int n0 = nbase + (lane & 16);
+    const int col = n0 + 4 * (r & 3);
+    i16x4 lo, hi;
+    {
+      const int row = kbase + 4 * half + (r >> 2);
+      lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(lds + Tile::elem_off(row, col)));
+    }
+    {
+      const int row = kbase + 8 + 4 * half + (r >> 2);
+      hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(lds + Tile::elem_off(row, col)));
+    }
+    short s8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.v[j] = __builtin_bit_cast(bf16, s8[j]);
+  } else {
+    const int n = nbase + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = kbase + (j < 4 ? 4 * half + j : 8 + 4 * half + (j - 4));
+      f.v[j] = *reinterpret_cast<const float*>(lds + Tile::elem_off(row, n));
+    }
+  }
+  return f;
+}
+
+// Fragment straight from global memory: 8 consecutive elements at p.
+template <typename T> __device__ __forceinline__ Frag<T> global_frag(const T* __restrict__ p) {
+  Frag<T> f;
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(p);
+    f.v = __builtin_bit_cast(bf16x8, raw);
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f.v[j] = a[j];
+      f.v[4 + j] = b[j];
+    }
+  }
+  return f;
+}
+template <typename T> __device__ __forceinline__ Frag<T> zero_frag() {
+  Frag<T> f;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.v[j] = (bf16)0.0f;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.v[j] = 0.0f;
+  }
+  return f;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Kernel argument block shared by all launches.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  void* out_o;
+  float* out_lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // D = rowsum(dO * O), [heads_q, total_q]
+  int32_t batch, heads_q, heads_kv, total_q, total_k, max_seqlen_q, max_seqlen_k;
+  int32_t window, causal;
+  float scale;
+};
+
+}  // namespace swa

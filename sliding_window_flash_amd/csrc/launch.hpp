@@ -1,0 +1,14 @@
+// Internal interface between the C ABI (api.hip) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "kernel_common.hpp"
+
+namespace swa {
+
+hipError_t launch_fwd(int dtype, int head_dim, const AttnArgs& a, hipStream_t st);
+hipError_t launch_bwd(int dtype, int head_dim, const AttnArgs& a, hipStream_t st);
+bool tile_sizes(int dtype, int head_dim, int* fwd_bm, int* fwd_bn, int* bwd_bn, int* bwd_bm);
+
+}  // namespace swa

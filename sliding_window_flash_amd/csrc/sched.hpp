@@ -1,0 +1,125 @@
+// Block-range scheduler: which tiles of the score matrix a kernel visits.
+//
+// "Off NVIDIA, you fix the platform yourself", section "What did fixing it
+// take?": the tiled backward must skip blocks lying entirely outside the
+// window and mask only the cells on its edge; the first block a query visits
+// is no longer block zero, and some key blocks are never visited.
+//
+// Integer code only, compiled for both the host (CPU tests and the C ABI's
+// inspection calls) and the device (every kernel). All position arithmetic is
+// int64 so that window = INT32_MAX and 32-bit lengths cannot overflow.
+//
+// Geometry of one sequence: L_q queries, L_k keys, delta = L_k - L_q >= 0;
+// query i sits at key position p = i + delta. Causal cell (i, j) is visible
+// iff j <= p and p - j < window; non-causal cells are all visible.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define SWA_HD __host__ __device__ inline
+#else
+#define SWA_HD inline
+#endif
+
+namespace swa {
+
+struct SeqGeom {
+  int64_t lq, lk, window;
+  bool causal;
+  SWA_HD int64_t delta() const { return lk - lq; }
+};
+
+struct TileRange {
+  int32_t lo, hi;            // visited tiles [lo, hi]; empty when lo > hi
+  int32_t full_lo, full_hi;  // tiles with every cell visible; empty when full_lo > full_hi
+};
+
+SWA_HD int64_t floor_div(int64_t a, int64_t b) {  // b > 0
+  return a >= 0 ? a / b : -((-a + b - 1) / b);
+}
+
+// Query tile qb (rows [qb*bm, min(lq, qb*bm+bm)) ) -> key tiles of size bn.
+SWA_HD TileRange query_tile_keys(const SeqGeom& s, int32_t qb, int32_t bm, int32_t bn) {
+  TileRange r{0, -1, 0, -1};
+  const int64_t i0 = (int64_t)qb * bm;
+  int64_t i1 = i0 + bm - 1;
+  if (i1 > s.lq - 1) i1 = s.lq - 1;
+  if (i0 > i1 || s.lk <= 0) return r;
+  int64_t jlo, jhi;
+  if (s.causal) {
+    const int64_t pmin = i0 + s.delta(), pmax = i1 + s.delta();
+    jlo = pmin - s.window + 1;
+    if (jlo < 0) jlo = 0;
+    jhi = pmax < s.lk - 1 ? pmax : s.lk - 1;
+    if (jlo > jhi) return r;
+    r.lo = (int32_t)(jlo / bn);
+    r.hi = (int32_t)(jhi / bn);
+    // full tile kb: kb*bn+bn-1 <= pmin (causal), pmax - kb*bn < window (window),
+    // kb*bn+bn <= lk (in bounds), and the query tile has all bm rows.
+    if (i1 - i0 + 1 == bm) {
+      const int64_t fhi_causal = floor_div(pmin + 1, bn) - 1;
+      const int64_t fhi_bound = s.lk / bn - 1;
+      int64_t fhi = fhi_causal < fhi_bound ? fhi_causal : fhi_bound;
+      // pmax - kb*bn < window  <=>  kb*bn > pmax - window  <=>  kb >= floor((pmax-window)/bn)+1
+      int64_t flo = floor_div(pmax - s.window, bn) + 1;
+      if (flo < r.lo) flo = r.lo;
+      if (fhi > r.hi) fhi = r.hi;
+      if (flo <= fhi) {
+        r.full_lo = (int32_t)flo;
+        r.full_hi = (int32_t)fhi;
+      }
+    }
+  } else {
+    jlo = 0;
+    jhi = s.lk - 1;
+    r.lo = 0;
+    r.hi = (int32_t)(jhi / bn);
+    if (i1 - i0 + 1 == bm && s.lk / bn - 1 >= 0) {
+      r.full_lo = 0;
+      r.full_hi = (int32_t)(s.lk / bn - 1);
+    }
+  }
+  return r;
+}
+
+// Key tile kb (cols [kb*bn, min(lk, kb*bn+bn)) ) -> query tiles of size bm that
+// see at least one of its cells. Empty (lo > hi) when no query sees it.
+SWA_HD TileRange key_tile_queries(const SeqGeom& s, int32_t kb, int32_t bn, int32_t bm) {
+  TileRange r{0, -1, 0, -1};
+  const int64_t j0 = (int64_t)kb * bn;
+  int64_t j1 = j0 + bn - 1;
+  if (j1 > s.lk - 1) j1 = s.lk - 1;
+  if (j0 > j1 || s.lq <= 0) return r;
+  int64_t ilo, ihi;
+  if (s.causal) {
+    // visible iff i >= j - delta and i <= j - delta + window - 1
+    ilo = j0 - s.delta();
+    if (ilo < 0) ilo = 0;
+    ihi = j1 - s.delta() + s.window - 1;
+    if (ihi > s.lq - 1) ihi = s.lq - 1;
+  } else {
+    ilo = 0;
+    ihi = s.lq - 1;
+  }
+  if (ilo > ihi) return r;
+  r.lo = (int32_t)(ilo / bm);
+  r.hi = (int32_t)(ihi / bm);
+  return r;
+}
+
+// Per-cell visibility, used inside edge tiles.
+SWA_HD bool cell_visible(const SeqGeom& s, int64_t i, int64_t j) {
+  if (i >= s.lq || j >= s.lk) return false;
+  if (!s.causal) return true;
+  const int64_t p = i + s.delta();
+  return j <= p && p - j < s.window;
+}
+
+// Is tile (query tile qb, key tile kb) free of masked cells?
+SWA_HD bool tile_is_full(const SeqGeom& s, int32_t qb, int32_t bm, int32_t kb, int32_t bn) {
+  const TileRange r = query_tile_keys(s, qb, bm, bn);
+  return r.full_lo <= kb && kb <= r.full_hi;
+}
+
+}  // namespace swa

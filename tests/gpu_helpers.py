@@ -1,0 +1,158 @@
+"""Shared helpers for the GPU parity tests: run the HIP path through the C ABI
+(via the binding) and compare with the fp64 oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import sliding_window_flash_amd as swa
+from oracle import dense
+from sliding_window_flash_amd.workloads import Workload
+
+# Tolerances: fp32 max-abs 1e-5; bf16 max-abs 2e-2 and relative Frobenius 1e-2.
+F32_MAX_ABS = 1e-5
+BF16_MAX_ABS = 2e-2
+BF16_REL_FRO = 1e-2
+# Where the exact result is identically zero (window 1: dQ, dK; scale 0), only
+# rounding is left; the bar is max-abs 1e-4 in bf16 and 1e-6 in fp32.
+ZERO_REF_ABS = {"bf16": 1e-4, "f32": 1e-6}
+
+
+def say(*args):
+    print(*args, flush=True)
+    sys.stdout.flush()
+
+
+def torch_dtype(w: Workload):
+    import torch
+    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+
+def to_device(w: Workload, x: dict) -> dict:
+    import torch
+    dt = torch_dtype(w)
+    out = {k: torch.from_numpy(x[k]).to(dt).cuda() for k in ("q", "k", "v", "do")}
+    out["cu_q"] = torch.from_numpy(x["cu_q"]).cuda()
+    out["cu_k"] = torch.from_numpy(x["cu_k"]).cuda()
+    return out
+
+
+def run_hip(w: Workload, dev: dict, *, window=None, poison=True, with_backward=True) -> dict:
+    """Forward then backward through the C ABI. Outputs and workspace are
+    filled with NaN first, so any element the kernels fail to write shows."""
+    import torch
+    window = w.window if window is None else window
+    kw = dict(max_seqlen_q=w.max_seqlen_q, max_seqlen_k=w.max_seqlen_k, window=window,
+              causal=w.causal, scale=w.scale)
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    if poison:
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+    o, lse = swa.fwd(q, k, v, dev["cu_q"], dev["cu_k"], out=o, lse=lse, **kw)
+    res = dict(o=o, lse=lse)
+    if with_backward:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        p = swa.params_for(q, k, dev["cu_q"], dev["cu_k"], **kw)
+        ws = torch.empty(swa.workspace_bytes(p), dtype=torch.uint8, device=q.device)
+        if poison:
+            for t in (dq, dk, dv):
+                t.fill_(float("nan"))
+            ws.fill_(0xFF)
+        swa.bwd(q, k, v, o, lse, do, dev["cu_q"], dev["cu_k"], dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+        res.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return res
+
+
+def host64(t) -> np.ndarray:
+    import torch
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def compare(name: str, got, ref, dtype: str, zero_ref: bool = False) -> dict:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin), f"{name}: non-finite pattern differs (unwritten output?)"
+    diff = np.abs(got[fin] - ref[fin])
+    max_abs = float(diff.max(initial=0.0))
+    nrm = float(np.linalg.norm(ref[fin]))
+    rel = float(np.linalg.norm(got[fin] - ref[fin]) / nrm) if nrm > 0 else 0.0
+    stats = dict(max_abs=max_abs, rel_fro=rel)
+    if zero_ref:
+        assert max_abs <= ZERO_REF_ABS[dtype], f"{name}: {stats} (zero reference)"
+    elif dtype == "f32":
+        assert max_abs <= F32_MAX_ABS, f"{name}: {stats}"
+    else:
+        assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_FRO, f"{name}: {stats}"
+    return stats
+
+
+def full_reference(w: Workload, x: dict, window=None) -> dict:
+    window = w.window if window is None else window
+    return dense.sdpa_reference(x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale,
+                                window, w.causal)
+
+
+def compare_full(w: Workload, x: dict, got: dict, window=None, zero=()) -> dict:
+    ref = full_reference(w, x, window)
+    out = {}
+    for key in ("o", "lse", "dq", "dk", "dv"):
+        if key in got:
+            out[key] = compare(f"{w.name} {key}", host64(got[key]), ref[key], w.dtype,
+                               zero_ref=key in zero)
+    return out
+
+
+def sample_rows(w: Workload, n_random: int, seed: int, tile: int = 128, few: bool = False):
+    """Packed token indices: each sequence's first and last rows, rows around
+    tile and window edges, and random rows (``few``: a smaller edge set)."""
+    rng = np.random.default_rng(seed)
+    toks = []
+    for b in range(w.batch):
+        start = int(sum(w.lengths_q[:b]))
+        L = w.lengths_q[b]
+        if L == 0:
+            continue
+        if few:
+            cand = {0, L - 1, tile, w.window}
+        else:
+            cand = {0, 1, L - 1, L - 2, tile - 1, tile, w.window - 1, w.window, w.window + 1}
+        cand |= set(int(c) for c in rng.integers(0, L, n_random))
+        toks += [start + c for c in sorted(cand) if 0 <= c < L]
+    return np.array(toks, np.int64)
+
+
+def compare_sampled(w: Workload, x: dict, got: dict, n_q: int = 6, n_k: int = 3, seed: int = 0,
+                    window=None) -> dict:
+    """Sampled query rows (O, LSE, dQ) and key rows (dK, dV) against the oracle
+    computed one row at a time."""
+    window = w.window if window is None else window
+    rng = np.random.default_rng(seed)
+    args = (x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale, window, w.causal)
+    qt = sample_rows(w, n_q, seed)
+    qh = rng.integers(0, w.heads_q, qt.size)
+    rq = dense.sdpa_query_rows(*args, qt, qh)
+    kt = sample_rows(w.replace(lengths_q=w.lengths_k), n_k, seed + 1, few=True)
+    kh = rng.integers(0, w.heads_kv, kt.size)
+    rk = dense.sdpa_key_rows(*args, kt, kh)
+
+    def pick(t, i0, i1):
+        return host64(t[index_tensor(i0), index_tensor(i1)])
+
+    stats = {}
+    stats["o"] = compare(f"{w.name} O rows", pick(got["o"], qt, qh), rq["o"], w.dtype)
+    stats["lse"] = compare(f"{w.name} LSE rows", pick(got["lse"], qh, qt), rq["lse"], w.dtype)
+    stats["dq"] = compare(f"{w.name} dQ rows", pick(got["dq"], qt, qh), rq["dq"], w.dtype)
+    stats["dk"] = compare(f"{w.name} dK rows", pick(got["dk"], kt, kh), rk["dk"], w.dtype)
+    stats["dv"] = compare(f"{w.name} dV rows", pick(got["dv"], kt, kh), rk["dv"], w.dtype)
+    return stats
+
+
+def index_tensor(a: np.ndarray):
+    import torch
+    return torch.from_numpy(np.asarray(a, np.int64)).cuda()

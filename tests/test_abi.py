@@ -1,0 +1,101 @@
+"""The C-ABI library loads without a GPU, exports what include/swa_attn.h
+declares, and refuses bad arguments up front (no launch is attempted)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sliding_window_flash_amd as swa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "swa_attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 8, names
+    L = swa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(swa.EXPORTED)
+
+
+def good(**kw):
+    base = dict(batch=1, heads_q=4, heads_kv=2, head_dim=128, total_q=100, total_k=100,
+                max_seqlen_q=100, max_seqlen_k=100, window=16, causal=True, scale=0.1,
+                dtype=swa.ATTN_BF16)
+    base.update(kw)
+    return swa.make_params(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 0),
+    (dict(batch=0), 2),
+    (dict(heads_q=3), 2),
+    (dict(heads_kv=0), 2),
+    (dict(total_q=-1), 2),
+    (dict(max_seqlen_q=101), 2),
+    (dict(window=0), 3),
+    (dict(window=-5), 3),
+    (dict(head_dim=96), 4),
+    (dict(head_dim=256), 4),
+    (dict(dtype=7), 4),
+    (dict(causal=False, window=50), 4),
+    (dict(causal=False, window=100), 0),
+    (dict(window=swa.INT32_MAX), 0),
+    (dict(dtype=swa.ATTN_F32, head_dim=64), 0),
+])
+def test_parameter_checks(kw, code):
+    assert swa.check_params(good(**kw)) == code
+
+
+def test_status_strings():
+    L = swa.lib()
+    for code in range(8):
+        s = L.attn_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert L.attn_status_str(99).decode() == "unknown status"
+
+
+def _fwd(p, q=16, k=16, v=16, cq=16, ck=16, o=16, lse=16):
+    L = swa.lib()
+    return L.attn_fwd(ctypes.byref(p) if p is not None else None, q, k, v, cq, ck, o, lse, None)
+
+
+def test_forward_refuses_before_launch():
+    assert _fwd(None) == 1
+    assert _fwd(good(window=0)) == 3
+    assert _fwd(good(), q=None) == 1
+    assert _fwd(good(), cq=None) == 1
+    assert _fwd(good(), lse=None) == 1
+    assert _fwd(good(), o=24) == 7       # not 16-byte aligned
+    assert _fwd(good(), cq=18) == 7      # int32 offsets need 4 bytes
+    assert _fwd(good(head_dim=32)) == 4
+
+
+def test_backward_refuses_before_launch():
+    L = swa.lib()
+    p = good()
+    need = swa.workspace_bytes(p)
+    assert need >= 4 * 4 * 100 and need % 256 == 0
+    args = [16] * 11
+    assert L.attn_bwd(ctypes.byref(p), *args, 16, need - 1, None) == 5
+    assert L.attn_bwd(ctypes.byref(p), *args, None, need, None) == 5
+    bad = list(args)
+    bad[8] = None  # dq
+    assert L.attn_bwd(ctypes.byref(p), *bad, 16, need, None) == 1
+    assert L.attn_bwd(ctypes.byref(good(causal=False, window=3)), *args, 16, need, None) == 4
+    assert swa.workspace_bytes(good(window=0)) == 0
+
+
+def test_tile_sizes():
+    bm, bn, kbn, kbm = swa.tile_sizes(128, swa.ATTN_BF16)
+    assert bm % 32 == 0 and bn % 32 == 0 and kbn % 32 == 0 and kbm % 32 == 0
+    with pytest.raises(swa.AttnError):
+        swa.tile_sizes(96, swa.ATTN_BF16)
