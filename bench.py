@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark: sliding-window attention forward + backward on one MI355X.
+
+A step is one pass of the whole path: attn_fwd (O, LSE) and the three backward
+stages (D, dQ, dK/dV) over the 32,768-token workload (batch 1, 32 query / 8 KV
+heads, head_dim 128, causal window 1,024, bf16), inputs resident in HBM.
+
+value = in-window FLOPs / time: 14 * head_dim FLOPs per visible (query, key)
+pair summed over query heads (forward Q K^T and P V; backward Q K^T, dO V^T,
+P^T dO, dS^T Q, dS K), counted cell-exact; the recompute a split backward does
+is not counted.
+
+Prints one JSON line. With --gpus N > 1 it exits: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_DENSE_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+HBM_PEAK_GBS = 8000.0             # MI355X HBM3E (published)
+SRC_FILES = ["sliding_window_flash_amd/csrc/attn_kernels.hip",
+             "sliding_window_flash_amd/csrc/kernel_common.hpp",
+             "sliding_window_flash_amd/csrc/sched.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bf16_n32768_w1024.json")
+
+
+def in_window_pairs(w) -> int:
+    """Visible (query, key) cells summed over query heads, cell-exact."""
+    total = 0
+    for lq, lk in zip(w.lengths_q, w.lengths_k):
+        delta = lk - lq
+        if not w.causal:
+            total += lq * lk
+            continue
+        # query i sees min(i + delta + 1, window) keys
+        c = [min(i + delta + 1, w.window) for i in range(lq)]
+        total += sum(c)
+    return total * w.heads_q
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in SRC_FILES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None if absent or taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except OSError:
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, rows: int):
+    """The fp64 oracle, untuned, on a bounded sample of the same workload:
+    query head 0, query rows [0, rows) of each sequence, full forward + backward."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import dense
+
+    t0 = time.perf_counter()
+    dense.sdpa_reference(x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale, w.window,
+                         w.causal, heads=[0], query_rows=(0, rows))
+    dt = time.perf_counter() - t0
+    pairs = 0
+    for lq, lk in zip(w.lengths_q, w.lengths_k):
+        delta = lk - lq
+        pairs += sum(min(i + delta + 1, w.window) for i in range(min(rows, lq)))
+    flops = 14 * w.head_dim * pairs
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"query head 0, query rows [0, {rows}) of each sequence; fp64 numpy dense "
+                      f"masked score panels, forward + backward; {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bf16_n32768_w1024_32q8kv_d128")
+    ap.add_argument("--cpu-rows", type=int, default=32768,
+                    help="query rows per sequence in the oracle's timing sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-memory-sweep", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the path runs on a single MI355X).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import sliding_window_flash_amd as swa
+    from sliding_window_flash_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    swa.lib()  # fails loudly if the HIP library is missing
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    x = W.make_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v, do = (torch.from_numpy(x[n]).to(dt).to(dev) for n in ("q", "k", "v", "do"))
+    cu_q = torch.from_numpy(x["cu_q"]).to(dev)
+    cu_k = torch.from_numpy(x["cu_k"]).to(dev)
+    kw = dict(max_seqlen_q=w.max_seqlen_q, max_seqlen_k=w.max_seqlen_k, window=w.window,
+              causal=w.causal, scale=w.scale)
+    p = swa.params_for(q, k, cu_q, cu_k, **kw)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.heads_q, w.total_q), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(swa.workspace_bytes(p), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    names = ["fwd", "bwd_delta", "bwd_dq", "bwd_dkdv"]
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        swa.fwd(q, k, v, cu_q, cu_k, out=o, lse=lse, **kw)
+        if evs is not None:
+            evs[1].record(stream)
+        for n, stage in enumerate((swa.BWD_DELTA, swa.BWD_DQ, swa.BWD_DKDV)):
+            swa.bwd(q, k, v, o, lse, do, cu_q, cu_k, dq=dq, dk=dk, dv=dv, workspace=ws,
+                    stages=stage, **kw)
+            if evs is not None:
+                evs[2 + n].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    kern_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+
+    d = w.head_dim
+    pairs = in_window_pairs(w)
+    flops_counted = 14 * d * pairs
+    value = flops_counted / (ms_per_step * 1e-3) / 1e12
+    # algorithmic work of each launch (per visible pair: fwd 2 contractions,
+    # dQ 3 (S, dP recomputed, dS K), dK/dV 4 (S, dP, P^T dO, dS^T Q); D reads O
+    # and dO and writes one fp32 per row)
+    esz = 2 if w.dtype == "bf16" else 4
+    algo = {
+        "fwd": ("mfma", 4 * d * pairs),
+        "bwd_dq": ("mfma", 6 * d * pairs),
+        "bwd_dkdv": ("mfma", 8 * d * pairs),
+        "bwd_delta": ("hbm", 2 * w.total_q * w.heads_q * d * esz + 4 * w.total_q * w.heads_q),
+    }
+    kernels = {}
+    for n in names:
+        bound, work = algo[n]
+        sec = kern_ms[n] * 1e-3
+        if bound == "mfma":
+            ach, peak, unit = work / sec / 1e12, BF16_DENSE_PEAK_TFLOPS, "TFLOP/s"
+        else:
+            ach, peak, unit = work / sec / 1e9, HBM_PEAK_GBS, "GB/s"
+        kernels[n] = {"ms": round(kern_ms[n], 4), "bound": bound, "achieved": round(ach, 2),
+                      "peak": peak, "unit": unit, "frac": round(ach / peak, 4)}
+    dom = max(("fwd", "bwd_dq", "bwd_dkdv"), key=lambda n: kern_ms[n])
+    traffic = load_traffic(dom)
+    roofline = dict(kernels[dom])
+    roofline.pop("ms")
+    roofline["kernel"] = dom
+    roofline["traffic"] = traffic
+
+    # peak device memory of one fwd + bwd (all buffers come from torch)
+    def peak_for(wl, xin=None):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        g = torch.Generator(device=dev).manual_seed(0)
+        qq = torch.randn((wl.total_q, wl.heads_q, d), generator=g, device=dev).to(dt)
+        kk = torch.randn((wl.total_k, wl.heads_kv, d), generator=g, device=dev).to(dt)
+        vv = torch.randn((wl.total_k, wl.heads_kv, d), generator=g, device=dev).to(dt)
+        dd = torch.randn((wl.total_q, wl.heads_q, d), generator=g, device=dev).to(dt) * 0.1
+        cq = torch.tensor(wl.cu_seqlens_q(), device=dev)
+        ck = torch.tensor(wl.cu_seqlens_k(), device=dev)
+        torch.cuda.synchronize()
+        inputs = torch.cuda.memory_allocated() - base
+        torch.cuda.reset_peak_memory_stats()
+        kk_ = dict(max_seqlen_q=wl.max_seqlen_q, max_seqlen_k=wl.max_seqlen_k, window=wl.window,
+                   causal=wl.causal, scale=wl.scale)
+        oo, ll = swa.fwd(qq, kk, vv, cq, ck, **kk_)
+        swa.bwd(qq, kk, vv, oo, ll, dd, cq, ck, **kk_)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        del qq, kk, vv, dd, oo, ll
+        return peak, inputs
+
+    del_list = [o, lse, dq, dk, dv, ws]
+    peak, inputs = peak_for(w)
+    mem = {"peak_gb": round(peak / 1e9, 4), "peak_above_inputs_gb": round((peak - inputs) / 1e9, 4)}
+    if not args.no_memory_sweep and w.batch == 1 and w.causal:
+        sweep = {}
+        for n in (8192, 16384, 32768):
+            wl = w.replace(lengths_q=(n,), lengths_k=(n,))
+            pk, inp = peak_for(wl)
+            sweep[str(n)] = round((pk - inp) / 1e9, 4)
+        mem["peak_above_inputs_gb_by_tokens"] = sweep
+        mem["peak_ratio_per_doubling"] = [round(sweep["16384"] / sweep["8192"], 3),
+                                          round(sweep["32768"] / sweep["16384"], 3)]
+    del del_list
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, x, args.cpu_rows)
+
+    line = {
+        "metric": "SWA fwd+bwd TFLOP/s (in-window) + % bf16 MFMA peak, N=32768 w=1024; peak GB",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "tokens": list(w.lengths_q),
+                   "heads_q": w.heads_q, "heads_kv": w.heads_kv, "head_dim": d,
+                   "window": w.window, "causal": w.causal, "in_window_pairs": pairs,
+                   "flops_counted": flops_counted},
+        "pct_bf16_peak": round(100 * value / BF16_DENSE_PEAK_TFLOPS, 2),
+        "fwd_ms": round(kern_ms["fwd"], 4),
+        "bwd_ms": round(kern_ms["bwd_delta"] + kern_ms["bwd_dq"] + kern_ms["bwd_dkdv"], 4),
+        "kernels": kernels,
+        "roofline": roofline,
+        "memory": mem,
+        "cpu_baseline": cpu,
+        "source_hash": source_hash(),
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

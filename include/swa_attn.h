@@ -116,6 +116,29 @@ attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, con
                        void* dk, void* dv, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* The backward's three stages, for callers that schedule them themselves:
+ *   ATTN_BWD_DELTA: D = rowsum(dO * O) into the workspace;
+ *   ATTN_BWD_DQ:    dQ (reads Q, K, V, dO, LSE and D);
+ *   ATTN_BWD_DKDV:  dK and dV (reads Q, K, V, dO, LSE and D).
+ * DQ and DKDV need a completed DELTA of the same call parameters and
+ * workspace; they are independent of each other, so they may run on two
+ * streams once DELTA is done. attn_bwd is attn_bwd_stages with all three, in
+ * this order, on one stream. Same arguments and checks as attn_bwd; pointers a
+ * selected stage does not read or write may be NULL (O is read only by DELTA,
+ * dQ written only by DQ, dK and dV only by DKDV). */
+typedef enum {
+  ATTN_BWD_DELTA = 1,
+  ATTN_BWD_DQ = 2,
+  ATTN_BWD_DKDV = 4,
+  ATTN_BWD_ALL = 7
+} attn_bwd_stage_t;
+
+attn_status_t attn_bwd_stages(const attn_params_t* p, int32_t stages, const void* q,
+                              const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, void* dq, void* dk, void* dv,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_str(attn_status_t s);
 

@@ -132,12 +132,18 @@ def _check_shapes(q, k, v, do, cu_q, cu_k):
 
 def sdpa_reference(q, k, v, do, cu_q, cu_k, scale: float, window: int, causal: bool, *,
                    with_backward: bool = True, panel_rows: int = 512,
-                   ram_ceiling: Optional[int] = None) -> dict:
+                   ram_ceiling: Optional[int] = None, heads: Optional[Iterable[int]] = None,
+                   query_rows: Optional[tuple] = None) -> dict:
     """Full forward (and backward) over a packed batch.
 
     q, do: [T_q, Hq, d]; k, v: [T_k, Hkv, d]; cu_q, cu_k: [B+1] offsets.
     Returns fp64 arrays: o [T_q, Hq, d], lse [Hq, T_q], and with the backward
     delta (= D) [Hq, T_q], dq [T_q, Hq, d], dk, dv [T_k, Hkv, d].
+
+    ``heads`` and ``query_rows`` = (r0, r1) restrict the work to those query
+    heads and to rows r0 <= i < r1 of every sequence (a timing sample; rows
+    and heads left out stay at their initial values, and dK/dV then hold only
+    the contributions of the rows computed).
     """
     tq, tk, hq, hkv, d = _check_shapes(q, k, v, do if with_backward else None, cu_q, cu_k)
     grp = hq // hkv
@@ -158,12 +164,14 @@ def sdpa_reference(q, k, v, do, cu_q, cu_k, scale: float, window: int, causal: b
         rows_per = max(1, min(panel_rows, lq))
         # ~8 panel-sized fp64 arrays live at once
         check_host_ram(8 * rows_per * max(lk, 1) * 8, ram_ceiling)
-        for h in range(hq):
+        row_lo, row_hi = (0, lq) if query_rows is None else (max(0, query_rows[0]),
+                                                            min(lq, query_rows[1]))
+        for h in (range(hq) if heads is None else heads):
             g = h // grp
             kg = _as64(k[k0:k1, g, :])
             vg = _as64(v[k0:k1, g, :])
-            for r0 in range(0, lq, rows_per):
-                r1 = min(lq, r0 + rows_per)
+            for r0 in range(row_lo, row_hi, rows_per):
+                r1 = min(row_hi, r0 + rows_per)
                 mask = visible_cells(lq, lk, window, causal, np.arange(r0, r1))
                 qh = _as64(q[q0 + r0:q0 + r1, h, :])
                 doh = _as64(do[q0 + r0:q0 + r1, h, :]) if with_backward else None

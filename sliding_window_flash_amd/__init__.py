@@ -23,7 +23,9 @@ STATUS = {
     4: "ATTN_ERR_UNSUPPORTED", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP", 7: "ATTN_ERR_ALIGN",
 }
 
-EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
+BWD_DELTA, BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 4, 7
+
+EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_stages", "attn_bwd_workspace_bytes", "attn_status_str",
             "attn_check_params", "attn_tile_sizes", "attn_query_tile_range",
             "attn_key_tile_range")
 
@@ -61,6 +63,9 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd.restype = ctypes.c_int
         L.attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.attn_bwd.restype = ctypes.c_int
+        L.attn_bwd_stages.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, vp, ctypes.c_size_t, vp]
+        L.attn_bwd_stages.restype = ctypes.c_int
         L.attn_bwd_workspace_bytes.argtypes = [P]
         L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.attn_status_str.argtypes = [ctypes.c_int]
@@ -189,8 +194,10 @@ def fwd(q, k, v, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=INT32_MAX, ca
 
 
 def bwd(q, k, v, o, lse, do, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=INT32_MAX,
-        causal=True, scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """dQ, dK, dV through attn_bwd (the VJP of sum(O * dO))."""
+        causal=True, scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None,
+        stages=BWD_ALL):
+    """dQ, dK, dV through attn_bwd_stages (the VJP of sum(O * dO)); ``stages``
+    selects a subset of the backward's launches (all three by default)."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (do, "do"),
                  (cu_q, "cu_q"), (cu_k, "cu_k")):
@@ -203,9 +210,10 @@ def bwd(q, k, v, o, lse, do, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=I
     nbytes = workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    st = lib().attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
-                        _ptr(cu_q), _ptr(cu_k), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                        workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    st = lib().attn_bwd_stages(ctypes.byref(p), int(stages), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                               _ptr(lse), _ptr(do), _ptr(cu_q), _ptr(cu_k), _ptr(dq), _ptr(dk),
+                               _ptr(dv), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream_ptr(stream))
     if st:
-        raise AttnError(st, "attn_bwd")
+        raise AttnError(st, "attn_bwd_stages")
     return dq, dk, dv

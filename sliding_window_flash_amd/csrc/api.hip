@@ -94,25 +94,32 @@ size_t attn_bwd_workspace_bytes(const attn_params_t* p) {
   return round_up(d_bytes > 0 ? d_bytes : 1, 256);
 }
 
-attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v,
-                       const void* o, const float* lse, const void* dout,
-                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dq,
-                       void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+attn_status_t attn_bwd_stages(const attn_params_t* p, int32_t stages, const void* q,
+                              const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, void* dq, void* dk, void* dv,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   attn_status_t s = attn_check_params(p);
   if (s != ATTN_OK) return s;
+  if (stages <= 0 || (stages & ~ATTN_BWD_ALL) != 0) return ATTN_ERR_SHAPE;
+  const bool st_delta = stages & ATTN_BWD_DELTA, st_dq = stages & ATTN_BWD_DQ,
+             st_dkdv = stages & ATTN_BWD_DKDV;
   if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return ATTN_ERR_NULL;
   if (!aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k)) return ATTN_ERR_ALIGN;
-  const int64_t nq = q_elems(p), nk = k_elems(p);
-  if ((s = check_tensor(q, nq, true)) != ATTN_OK) return s;
-  if ((s = check_tensor(k, nk, true)) != ATTN_OK) return s;
-  if ((s = check_tensor(v, nk, true)) != ATTN_OK) return s;
-  if ((s = check_tensor(o, nq, true)) != ATTN_OK) return s;
+  const int64_t nq = q_elems(p), nk = k_elems(p), nrow = (int64_t)p->total_q * p->heads_q;
+  if (st_dq || st_dkdv) {
+    if ((s = check_tensor(q, nq, true)) != ATTN_OK) return s;
+    if ((s = check_tensor(k, nk, true)) != ATTN_OK) return s;
+    if ((s = check_tensor(v, nk, true)) != ATTN_OK) return s;
+    if ((s = check_tensor(lse, nrow, false)) != ATTN_OK) return s;
+  }
+  if (st_delta && (s = check_tensor(o, nq, true)) != ATTN_OK) return s;
   if ((s = check_tensor(dout, nq, true)) != ATTN_OK) return s;
-  if ((s = check_tensor(lse, (int64_t)p->total_q * p->heads_q, false)) != ATTN_OK) return s;
-  if ((s = check_tensor(dq, nq, true)) != ATTN_OK) return s;
-  if ((s = check_tensor(dk, nk, true)) != ATTN_OK) return s;
-  if ((s = check_tensor(dv, nk, true)) != ATTN_OK) return s;
+  if (st_dq && (s = check_tensor(dq, nq, true)) != ATTN_OK) return s;
+  if (st_dkdv) {
+    if ((s = check_tensor(dk, nk, true)) != ATTN_OK) return s;
+    if ((s = check_tensor(dv, nk, true)) != ATTN_OK) return s;
+  }
   if (workspace == nullptr || workspace_bytes < attn_bwd_workspace_bytes(p)) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
   swa::AttnArgs a = base_args(p);
@@ -128,9 +135,18 @@ attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, con
   a.dk = dk;
   a.dv = dv;
   a.delta = static_cast<float*>(workspace);
-  if (swa::launch_bwd(p->dtype, p->head_dim, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (swa::launch_bwd(p->dtype, p->head_dim, stages, a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
+}
+
+attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v,
+                       const void* o, const float* lse, const void* dout,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dq,
+                       void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return attn_bwd_stages(p, ATTN_BWD_ALL, q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, dq,
+                         dk, dv, workspace, workspace_bytes, stream);
 }
 
 const char* attn_status_str(attn_status_t s) {

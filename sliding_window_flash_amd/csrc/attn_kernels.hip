@@ -415,29 +415,33 @@ static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
 }
 
 template <typename T, int D>
-static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t st) {
+static hipError_t launch_bwd_t(int stages, const AttnArgs& a, hipStream_t st) {
   using TL = Tiles<T, D>;
   const int64_t rows = (int64_t)a.total_q * a.heads_q;
-  if (rows > 0) {
+  if ((stages & 1) && rows > 0) {
     const int64_t g0 = (rows + (256 / (D / 8)) - 1) / (256 / (D / 8));
     hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)g0), dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (stages & 2) {
     const int64_t nqb = (a.max_seqlen_q + TL::kFwdBM - 1) / TL::kFwdBM;
     const int64_t g1 = nqb * a.heads_q * a.batch;
-    if (g1 > 0) {
+    if (g1 > 0 && rows > 0) {
       hipLaunchKernelGGL((bwd_dq_kernel<T, D, TL::kFwdBM, TL::kFwdBN>), dim3((unsigned)g1),
                          dim3(TL::kFwdBM * 2), 0, st, a);
-      e = hipGetLastError();
+      const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
-  const int64_t nkb = (a.max_seqlen_k + TL::kBwdBN - 1) / TL::kBwdBN;
-  const int64_t g2 = nkb * a.heads_kv * a.batch;
-  if (g2 > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, TL::kBwdBN, TL::kBwdBM>), dim3((unsigned)g2),
-                       dim3(TL::kBwdBN * 2), 0, st, a);
-    return hipGetLastError();
+  if (stages & 4) {
+    const int64_t nkb = (a.max_seqlen_k + TL::kBwdBN - 1) / TL::kBwdBN;
+    const int64_t g2 = nkb * a.heads_kv * a.batch;
+    if (g2 > 0) {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, TL::kBwdBN, TL::kBwdBM>), dim3((unsigned)g2),
+                         dim3(TL::kBwdBN * 2), 0, st, a);
+      return hipGetLastError();
+    }
   }
   return hipSuccess;
 }
@@ -450,11 +454,11 @@ hipError_t launch_fwd(int dtype, int head_dim, const AttnArgs& a, hipStream_t st
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd(int dtype, int head_dim, const AttnArgs& a, hipStream_t st) {
-  if (dtype == 1 && head_dim == 128) return launch_bwd_t<bf16, 128>(a, st);
-  if (dtype == 1 && head_dim == 64) return launch_bwd_t<bf16, 64>(a, st);
-  if (dtype == 0 && head_dim == 128) return launch_bwd_t<float, 128>(a, st);
-  if (dtype == 0 && head_dim == 64) return launch_bwd_t<float, 64>(a, st);
+hipError_t launch_bwd(int dtype, int head_dim, int stages, const AttnArgs& a, hipStream_t st) {
+  if (dtype == 1 && head_dim == 128) return launch_bwd_t<bf16, 128>(stages, a, st);
+  if (dtype == 1 && head_dim == 64) return launch_bwd_t<bf16, 64>(stages, a, st);
+  if (dtype == 0 && head_dim == 128) return launch_bwd_t<float, 128>(stages, a, st);
+  if (dtype == 0 && head_dim == 64) return launch_bwd_t<float, 64>(stages, a, st);
   return hipErrorInvalidValue;
 }
 

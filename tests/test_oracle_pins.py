@@ -63,3 +63,17 @@ def test_host_ram_guard_refuses_up_front():
     with pytest.raises(dense.HostRamExceeded):
         dense.sdpa_reference(x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale,
                              8, True, ram_ceiling=1024)
+
+
+def test_row_and_head_sample_matches_full_reference():
+    w = small_case([300, 40], [320, 40], heads_q=4, heads_kv=2, head_dim=8, window=30, seed=25)
+    x = make_inputs(w)
+    args = (x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale, w.window, w.causal)
+    full = dense.sdpa_reference(*args)
+    part = dense.sdpa_reference(*args, heads=[2], query_rows=(17, 250), panel_rows=50)
+    for b, (q0, q1) in enumerate(zip(x["cu_q"][:-1], x["cu_q"][1:])):
+        r = slice(q0 + 17, min(q1, q0 + 250))
+        np.testing.assert_allclose(part["o"][r, 2], full["o"][r, 2], atol=1e-13)
+        np.testing.assert_allclose(part["dq"][r, 2], full["dq"][r, 2], atol=1e-13)
+        np.testing.assert_allclose(part["lse"][2, r], full["lse"][2, r], atol=1e-13)
+    assert np.all(part["o"][:, [0, 1, 3]] == 0)
