@@ -103,6 +103,9 @@ def main() -> int:
                     help="query rows per sequence in the oracle's timing sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-memory-sweep", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device copy of this many MiB first (a known-size kernel for "
+                         "scaling hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -137,6 +140,13 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     names = ["fwd", "bwd_delta", "bwd_dq", "bwd_dkdv"]
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(evs=None):
         if evs is not None:

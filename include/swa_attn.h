@@ -75,7 +75,7 @@ typedef enum {
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
   ATTN_ERR_SHAPE = 2,       /* sizes inconsistent (batch < 1, heads_q % heads_kv, totals ...) */
   ATTN_ERR_WINDOW = 3,      /* window < 1 */
-  ATTN_ERR_UNSUPPORTED = 4, /* head_dim not 64/128, unknown dtype, window without causal */
+  ATTN_ERR_UNSUPPORTED = 4, /* head_dim not 64/128, unknown dtype, window without causal, scale <= 0 */
   ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than attn_bwd_workspace_bytes */
   ATTN_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
   ATTN_ERR_ALIGN = 7        /* a tensor pointer is not 16-byte aligned */
@@ -92,7 +92,7 @@ typedef struct {
   int32_t max_seqlen_k; /* >= every L_k */
   int32_t window;       /* >= 1; any value >= max_seqlen_k (e.g. INT32_MAX) is no window */
   int32_t causal;       /* 1 causal; 0 full attention (then window >= max_seqlen_k) */
-  float scale;          /* softmax scale, e.g. 1/sqrt(head_dim) */
+  float scale;          /* softmax scale, finite and > 0, e.g. 1/sqrt(head_dim) */
   int32_t dtype;        /* attn_dtype_t */
 } attn_params_t;
 

@@ -55,7 +55,9 @@ attn_status_t attn_check_params(const attn_params_t* p) {
   if (p->dtype != ATTN_F32 && p->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (p->causal != 0 && p->causal != 1) return ATTN_ERR_UNSUPPORTED;
   if (p->causal == 0 && p->window < p->max_seqlen_k) return ATTN_ERR_UNSUPPORTED;
-  if (!isfinite(p->scale)) return ATTN_ERR_SHAPE;
+  // the kernels fold the scale into exp2 arguments and take row maxima on raw
+  // scores, which needs a positive scale
+  if (!(p->scale > 0.f) || !isfinite(p->scale)) return ATTN_ERR_UNSUPPORTED;
   // packed element counts must stay addressable
   if ((int64_t)p->total_q * p->heads_q > INT32_MAX || (int64_t)p->total_k * p->heads_kv > INT32_MAX)
     return ATTN_ERR_SHAPE;

@@ -1,12 +1,12 @@
 // Forward and backward attention kernels for gfx950, and their launchers.
 //
 // Forward (per query tile of BM rows, one query head): S^T = K Q^T on MFMA,
-// scale, mask edge cells, online softmax per query (exp2 domain), O^T += V^T P^T
-// on MFMA; epilogue writes O and the natural-log LSE. The mlx-train-perf
-// README's flash-attention passage describes this saved state (O and the
-// log-sum-exp) and the tile recompute in the backward.
+// mask edge cells, online softmax per query in the exp2 domain, O^T += V^T P^T
+// on MFMA; the epilogue writes O and the natural-log LSE. The mlx-train-perf
+// README's flash-attention passage describes this saved state (the output and
+// the log-sum-exp) and the tile recompute in the backward.
 //
-// Backward, split into three launches on the caller's stream:
+// Backward, three launches on the caller's stream:
 //   delta: D = rowsum(dO * O) per (token, head), fp32 workspace.
 //   dq:    per query tile: recompute S^T, dP^T = V dO^T, P = exp(S - LSE),
 //          dS = P (dP - D), dQ^T += K^T dS^T. The accumulator is cleared
@@ -22,6 +22,11 @@
 // bf16 only as MFMA operands (the lab record's "Attention gradient error, real
 // Gemma 4 activations" entry: bf16 scratch scores cost about fourfold in dQ
 // error against fp32 score tiles).
+//
+// Every kernel streams its shared operand tiles (K/V, or Q/dO) through two LDS
+// stages: the next tile's global loads are issued into registers before the
+// current tile's MFMAs and written to the other stage after them, so one
+// barrier per step suffices.
 #include <math.h>
 
 #include "kernel_common.hpp"
@@ -56,21 +61,57 @@ __device__ __forceinline__ void store_acc_rows(T* row, const f32x16 (&acc)[D / 3
     }
 }
 
+// Register-staged copy of one ROWS x D tile: load() issues the global reads
+// (rows >= valid read as zero), store() writes the swizzled LDS stage.
+template <typename T, int ROWS, int D, int NT>
+struct TileStage {
+  using Tile = LdsTile<T, ROWS, D>;
+  static constexpr int kTotal = ROWS * Tile::kChunks;
+  static constexpr int kPer = kTotal / NT;
+  static_assert(kTotal % NT == 0, "tile must split evenly over the workgroup");
+  u32x4 r[kPer];
+  __device__ __forceinline__ void load(const T* __restrict__ src, int64_t stride, int valid, int tid) {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int idx = tid + e * NT;
+      const int row = idx / Tile::kChunks, c = idx % Tile::kChunks;
+      r[e] = u32x4{0u, 0u, 0u, 0u};
+      if (row < valid)
+        r[e] = *reinterpret_cast<const u32x4*>(src + (int64_t)row * stride + c * Tile::kElemsPerChunk);
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int idx = tid + e * NT;
+      const int row = idx / Tile::kChunks, c = idx % Tile::kChunks;
+      *reinterpret_cast<u32x4*>(lds + Tile::chunk_off(row, c)) = r[e];
+    }
+  }
+};
+
 struct QueryItem {
   int qb, h, b, q0, lq, k0, lk;
 };
 
-// Query-major work decode. Tiles with more rows of work come first (for the
-// causal mask, late query tiles see the most keys).
+// Query-major work decode. Logical order: KV head (outermost), sequence, query
+// tile (descending: for the causal mask later tiles see more keys, so the
+// longest run first), head within the KV group (innermost, so the G heads
+// sharing K/V run together). The launch id is remapped so that each XCD runs
+// a contiguous logical range.
 __device__ __forceinline__ QueryItem decode_query_item(const AttnArgs& a, int bm) {
   QueryItem it;
   const int nqb = (a.max_seqlen_q + bm - 1) / bm;
-  const int per = a.heads_q * a.batch;
-  const int id = blockIdx.x;
-  it.qb = nqb - 1 - id / per;
-  const int rest = id % per;
-  it.h = rest % a.heads_q;
-  it.b = rest / a.heads_q;
+  const int grp = a.heads_q / a.heads_kv;
+  const int n = nqb * a.heads_q * a.batch;
+  int L = xcd_remap((int)blockIdx.x, n);
+  const int hh = L % grp;
+  L /= grp;
+  it.qb = nqb - 1 - L % nqb;
+  L /= nqb;
+  it.b = L % a.batch;
+  const int g = L / a.batch;
+  it.h = g * grp + hh;
   it.q0 = a.cu_q[it.b];
   it.lq = a.cu_q[it.b + 1] - it.q0;
   it.k0 = a.cu_k[it.b];
@@ -79,13 +120,18 @@ __device__ __forceinline__ QueryItem decode_query_item(const AttnArgs& a, int bm
 }
 
 // ---------------------------------------------------------------- forward
+// Lazy rescaling: the running reference max m moves only when a row's max
+// exceeds it by more than kRescaleSlack (log2 units), so P = 2^(s*c - m) stays
+// below 2^kRescaleSlack and the O accumulator is rescaled rarely. The result
+// is the same softmax: O and LSE use the same reference at the end.
+constexpr float kRescaleSlack = 8.0f;
+
 template <typename T, int D, int BM, int BN>
 __global__ void __launch_bounds__(BM * 2) fwd_kernel(AttnArgs a) {
   constexpr int NT = BM * 2;
   using KTile = LdsTile<T, BN, D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * KTile::kBytes];
-  char* ks = smem;
-  char* vs = smem + KTile::kBytes;
+  constexpr int kStage = 2 * KTile::kBytes;  // K tile then V tile
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const QueryItem it = decode_query_item(a, BM);
@@ -97,8 +143,8 @@ __global__ void __launch_bounds__(BM * 2) fwd_kernel(AttnArgs a) {
   const int64_t qstride = (int64_t)a.heads_q * D;
   const int64_t kstride = (int64_t)a.heads_kv * D;
   const T* __restrict__ Q = static_cast<const T*>(a.q);
-  const T* __restrict__ K = static_cast<const T*>(a.k);
-  const T* __restrict__ V = static_cast<const T*>(a.v);
+  const T* __restrict__ K = static_cast<const T*>(a.k) + (int64_t)it.k0 * kstride + g * D;
+  const T* __restrict__ V = static_cast<const T*>(a.v) + (int64_t)it.k0 * kstride + g * D;
 
   const int i = it.qb * BM + w * 32 + l32;  // this lane's query row
   const bool row_ok = i < it.lq;
@@ -108,6 +154,11 @@ __global__ void __launch_bounds__(BM * 2) fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qf[s] = row_ok ? global_frag<T>(qrow + 16 * s) : zero_frag<T>();
   }
+  // Edge mask: visible iff (unsigned)(mpos - j) < mlim. Causal: mpos = p,
+  // mlim = window (covers j <= p and p - j < window). Full attention: mpos =
+  // L_k - 1, mlim = 2^31 - 1 (covers j < L_k).
+  const int mpos = a.causal ? i + (it.lk - it.lq) : it.lk - 1;
+  const uint32_t mlim = a.causal ? (uint32_t)a.window : 0x7fffffffu;
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -115,13 +166,26 @@ __global__ void __launch_bounds__(BM * 2) fwd_kernel(AttnArgs a) {
   float m = -INFINITY, lsum = 0.f;
   const float c = a.scale * kLog2e;
 
+  TileStage<T, BN, D, NT> sk, sv;
+  if (kr.lo <= kr.hi) {
+    const int kvalid = min(BN, it.lk - kr.lo * BN);
+    sk.load(K + (int64_t)kr.lo * BN * kstride, kstride, kvalid, tid);
+    sv.load(V + (int64_t)kr.lo * BN * kstride, kstride, kvalid, tid);
+    sk.store(smem, tid);
+    sv.store(smem + KTile::kBytes, tid);
+  }
+  __syncthreads();
+
   for (int kb = kr.lo; kb <= kr.hi; ++kb) {
-    __syncthreads();
-    const int kvalid = min(BN, it.lk - kb * BN);
-    const int64_t koff = (int64_t)(it.k0 + kb * BN) * kstride + g * D;
-    load_tile<T, BN, D, NT>(ks, K + koff, kstride, kvalid, tid);
-    load_tile<T, BN, D, NT>(vs, V + koff, kstride, kvalid, tid);
-    __syncthreads();
+    const int stage = (kb - kr.lo) & 1;
+    const char* ks = smem + stage * kStage;
+    const char* vs = ks + KTile::kBytes;
+    const bool more = kb < kr.hi;
+    if (more) {
+      const int kvalid = min(BN, it.lk - (kb + 1) * BN);
+      sk.load(K + (int64_t)(kb + 1) * BN * kstride, kstride, kvalid, tid);
+      sv.load(V + (int64_t)(kb + 1) * BN * kstride, kstride, kvalid, tid);
+    }
 
     f32x16 s[BN / 32];
 #pragma unroll
@@ -131,40 +195,53 @@ __global__ void __launch_bounds__(BM * 2) fwd_kernel(AttnArgs a) {
       for (int ss = 0; ss < D / 16; ++ss)
         mma(s[kt], row_frag<T, BN, D>(ks, 32 * kt + l32, 2 * ss + half), qf[ss]);
     }
-    const bool edge = !(kr.full_lo <= kb && kb <= kr.full_hi);
+    if (!(kr.full_lo <= kb && kb <= kr.full_hi)) {
+      const int mb = mpos - (kb * BN + 4 * half);
+#pragma unroll
+      for (int kt = 0; kt < BN / 32; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if ((uint32_t)(mb - (32 * kt + 8 * (r >> 2) + (r & 3))) >= mlim) s[kt][r] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[kt][r] * c;
-        if (edge && !cell_visible(sg, i, (int64_t)kb * BN + 32 * kt + acc_row(r, half))) x = -INFINITY;
-        s[kt][r] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
     mx = fmaxf(mx, xor32(mx));
-    const float mnew = fmaxf(m, mx);
-    const float mref = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = fast_exp2(m - mref);
+    const float mxs = mx == -INFINITY ? -INFINITY : mx * c;
+    const bool grow = mxs > m + kRescaleSlack;
+    if (__any(grow)) {
+      const float mnew = grow ? mxs : m;
+      const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+      m = mnew;
+    }
+    const float mu = m == -INFINITY ? 0.f : m;
     float rs = 0.f;
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(s[kt][r] - mref);
+        const float pv = fast_exp2(fmaf(s[kt][r], c, -mu));
         s[kt][r] = pv;
         rs += pv;
       }
-    lsum = lsum * alpha + rs;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
-    m = mnew;
+    lsum += rs;
 #pragma unroll
     for (int u = 0; u < BN / 16; ++u) {
       const Frag<T> pf = acc_frag<T>(s[u >> 1], u & 1);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) mma(acc[dt], col_frag<T, BN, D>(vs, 16 * u, 32 * dt, lane), pf);
     }
+    if (more) {
+      char* nk = smem + (stage ^ 1) * kStage;
+      sk.store(nk, tid);
+      sv.store(nk + KTile::kBytes, tid);
+    }
+    __syncthreads();
   }
 
   const float ltot = lsum + xor32(lsum);
@@ -205,9 +282,8 @@ template <typename T, int D, int BM, int BN>
 __global__ void __launch_bounds__(BM * 2) bwd_dq_kernel(AttnArgs a) {
   constexpr int NT = BM * 2;
   using KTile = LdsTile<T, BN, D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * KTile::kBytes];
-  char* ks = smem;
-  char* vs = smem + KTile::kBytes;
+  constexpr int kStage = 2 * KTile::kBytes;
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const QueryItem it = decode_query_item(a, BM);
@@ -218,8 +294,8 @@ __global__ void __launch_bounds__(BM * 2) bwd_dq_kernel(AttnArgs a) {
 
   const int64_t qstride = (int64_t)a.heads_q * D;
   const int64_t kstride = (int64_t)a.heads_kv * D;
-  const T* __restrict__ K = static_cast<const T*>(a.k);
-  const T* __restrict__ V = static_cast<const T*>(a.v);
+  const T* __restrict__ K = static_cast<const T*>(a.k) + (int64_t)it.k0 * kstride + g * D;
+  const T* __restrict__ V = static_cast<const T*>(a.v) + (int64_t)it.k0 * kstride + g * D;
 
   const int i = it.qb * BM + w * 32 + l32;
   const bool row_ok = i < it.lq;
@@ -240,44 +316,68 @@ __global__ void __launch_bounds__(BM * 2) bwd_dq_kernel(AttnArgs a) {
       dlt = a.delta[(int64_t)it.h * a.total_q + it.q0 + i];
     }
   }
+  const int mpos = a.causal ? i + (it.lk - it.lq) : it.lk - 1;
+  const uint32_t mlim = a.causal ? (uint32_t)a.window : 0x7fffffffu;
   // cleared before the first visited key tile (kr.lo), not on key tile zero
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
   const float c = a.scale * kLog2e;
 
-  for (int kb = kr.lo; kb <= kr.hi; ++kb) {
-    __syncthreads();
-    const int kvalid = min(BN, it.lk - kb * BN);
-    const int64_t koff = (int64_t)(it.k0 + kb * BN) * kstride + g * D;
-    load_tile<T, BN, D, NT>(ks, K + koff, kstride, kvalid, tid);
-    load_tile<T, BN, D, NT>(vs, V + koff, kstride, kvalid, tid);
-    __syncthreads();
+  TileStage<T, BN, D, NT> sk, sv;
+  if (kr.lo <= kr.hi) {
+    const int kvalid = min(BN, it.lk - kr.lo * BN);
+    sk.load(K + (int64_t)kr.lo * BN * kstride, kstride, kvalid, tid);
+    sv.load(V + (int64_t)kr.lo * BN * kstride, kstride, kvalid, tid);
+    sk.store(smem, tid);
+    sv.store(smem + KTile::kBytes, tid);
+  }
+  __syncthreads();
 
+  for (int kb = kr.lo; kb <= kr.hi; ++kb) {
+    const int stage = (kb - kr.lo) & 1;
+    const char* ks = smem + stage * kStage;
+    const char* vs = ks + KTile::kBytes;
+    const bool more = kb < kr.hi;
+    if (more) {
+      const int kvalid = min(BN, it.lk - (kb + 1) * BN);
+      sk.load(K + (int64_t)(kb + 1) * BN * kstride, kstride, kvalid, tid);
+      sv.load(V + (int64_t)(kb + 1) * BN * kstride, kstride, kvalid, tid);
+    }
     const bool edge = !(kr.full_lo <= kb && kb <= kr.full_hi);
-    f32x16 s[BN / 32];
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt) {
-      f32x16 dp = f32x16{};
-      s[kt] = f32x16{};
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ss = 0; ss < D / 16; ++ss) {
-        mma(s[kt], row_frag<T, BN, D>(ks, 32 * kt + l32, 2 * ss + half), qf[ss]);
+        mma(s, row_frag<T, BN, D>(ks, 32 * kt + l32, 2 * ss + half), qf[ss]);
         mma(dp, row_frag<T, BN, D>(vs, 32 * kt + l32, 2 * ss + half), df[ss]);
+      }
+      if (edge) {
+        const int mb = mpos - (kb * BN + 32 * kt + 4 * half);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if ((uint32_t)(mb - (8 * (r >> 2) + (r & 3))) >= mlim) s[r] = -INFINITY;
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = fast_exp2(s[kt][r] * c - lse2);
-        if (edge && !cell_visible(sg, i, (int64_t)kb * BN + 32 * kt + acc_row(r, half))) pv = 0.f;
-        s[kt][r] = pv * (dp[r] - dlt);  // dS
+        const float pv = fast_exp2(fmaf(s[r], c, -lse2));
+        s[r] = pv * (dp[r] - dlt);  // dS
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const Frag<T> dsf = acc_frag<T>(s, u);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          mma(acc[dt], col_frag<T, BN, D>(ks, 32 * kt + 16 * u, 32 * dt, lane), dsf);
       }
     }
-#pragma unroll
-    for (int u = 0; u < BN / 16; ++u) {
-      const Frag<T> dsf = acc_frag<T>(s[u >> 1], u & 1);
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) mma(acc[dt], col_frag<T, BN, D>(ks, 16 * u, 32 * dt, lane), dsf);
+    if (more) {
+      char* nk = smem + (stage ^ 1) * kStage;
+      sk.store(nk, tid);
+      sv.store(nk + KTile::kBytes, tid);
     }
+    __syncthreads();
   }
   if (row_ok) {
     T* row = static_cast<T*>(a.dq) + (int64_t)(it.q0 + i) * qstride + it.h * D;
@@ -286,24 +386,22 @@ __global__ void __launch_bounds__(BM * 2) bwd_dq_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------- backward: dK, dV
+// Key-major decode: KV head outermost, then sequence, then key tile ascending
+// (for the causal mask early key tiles are seen by the most queries).
 template <typename T, int D, int BN, int BM>
 __global__ void __launch_bounds__(BN * 2) bwd_dkdv_kernel(AttnArgs a) {
   constexpr int NT = BN * 2;
   using QTile = LdsTile<T, BM, D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * QTile::kBytes + 2 * BM * 4];
-  char* qs = smem;
-  char* dos = smem + QTile::kBytes;
-  float* lse2s = reinterpret_cast<float*>(smem + 2 * QTile::kBytes);
-  float* dlts = lse2s + BM;
+  constexpr int kStage = 2 * QTile::kBytes + 2 * BM * 4;  // Q, dO, LSE*log2e, D
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const int nkb = (a.max_seqlen_k + BN - 1) / BN;
-  (void)nkb;
-  const int per = a.heads_kv * a.batch;
-  const int kb = blockIdx.x / per;
-  const int rest = blockIdx.x % per;
-  const int g = rest % a.heads_kv;
-  const int b = rest / a.heads_kv;
+  int L = xcd_remap((int)blockIdx.x, nkb * a.heads_kv * a.batch);
+  const int kb = L % nkb;
+  L /= nkb;
+  const int b = L % a.batch;
+  const int g = L / a.batch;
   const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
   const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
   if (kb * BN >= lk) return;
@@ -333,59 +431,99 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv_kernel(AttnArgs a) {
     dva[dt] = f32x16{};
   }
   const float c = a.scale * kLog2e;
+  const bool causal = a.causal != 0;
+  const uint32_t wlim = (uint32_t)a.window;
   const T* __restrict__ Qg = static_cast<const T*>(a.q);
   const T* __restrict__ Dg = static_cast<const T*>(a.dout);
 
-  // An empty range (no query sees this key tile) skips both loops and writes zeros.
-  for (int h = g * grp; h < (g + 1) * grp; ++h) {
-    for (int qb = qr.lo; qb <= qr.hi; ++qb) {
-      __syncthreads();
-      const int qvalid = min(BM, lq - qb * BM);
-      const int64_t qoff = (int64_t)(q0 + qb * BM) * qstride + h * D;
-      load_tile<T, BM, D, NT>(qs, Qg + qoff, qstride, qvalid, tid);
-      load_tile<T, BM, D, NT>(dos, Dg + qoff, qstride, qvalid, tid);
-      for (int t = tid; t < BM; t += NT) {
-        float l2 = INFINITY, dl = 0.f;
-        if (t < qvalid) {
-          const int64_t idx = (int64_t)h * a.total_q + q0 + qb * BM + t;
-          const float l = a.lse[idx];
-          l2 = l == -INFINITY ? INFINITY : l * kLog2e;
-          dl = a.delta[idx];
-        }
-        lse2s[t] = l2;
-        dlts[t] = dl;
-      }
-      __syncthreads();
+  // Steps t = 0 .. grp * nq - 1 walk (head, query tile) pairs; an empty range
+  // (no query sees this key tile) has no steps and writes zeros.
+  const int nq = qr.hi >= qr.lo ? qr.hi - qr.lo + 1 : 0;
+  const int steps = grp * nq;
+  TileStage<T, BM, D, NT> sq, sd;
+  float l2v = INFINITY, dlv = 0.f;  // LSE*log2e and D of row tid (tid < BM)
+  auto issue = [&](int t) {
+    const int h = g * grp + t / nq;
+    const int qb = qr.lo + t % nq;
+    const int qvalid = min(BM, lq - qb * BM);
+    const int64_t qoff = (int64_t)(q0 + qb * BM) * qstride + h * D;
+    sq.load(Qg + qoff, qstride, qvalid, tid);
+    sd.load(Dg + qoff, qstride, qvalid, tid);
+    l2v = INFINITY;
+    dlv = 0.f;
+    if (tid < qvalid) {
+      const int64_t idx = (int64_t)h * a.total_q + q0 + qb * BM + tid;
+      const float l = a.lse[idx];
+      l2v = l == -INFINITY ? INFINITY : l * kLog2e;
+      dlv = a.delta[idx];
+    }
+  };
+  auto commit = [&](char* st) {
+    sq.store(st, tid);
+    sd.store(st + QTile::kBytes, tid);
+    if (tid < BM) {
+      reinterpret_cast<float*>(st + 2 * QTile::kBytes)[tid] = l2v;
+      reinterpret_cast<float*>(st + 2 * QTile::kBytes + BM * 4)[tid] = dlv;
+    }
+  };
+  if (steps > 0) {
+    issue(0);
+    commit(smem);
+  }
+  __syncthreads();
 
-      const bool edge = !tile_is_full(sg, qb, BM, kb, BN);
+  for (int t = 0; t < steps; ++t) {
+    const int stage = t & 1;
+    const char* qs = smem + stage * kStage;
+    const char* dos = qs + QTile::kBytes;
+    const float* lse2s = reinterpret_cast<const float*>(qs + 2 * QTile::kBytes);
+    const float* dlts = lse2s + BM;
+    const int qb = qr.lo + t % nq;
+    const bool more = t + 1 < steps;
+    if (more) issue(t + 1);
+    const bool edge = causal && !tile_is_full(sg, qb, BM, kb, BN);
 #pragma unroll
-      for (int mt = 0; mt < BM / 32; ++mt) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+    for (int mt = 0; mt < BM / 32; ++mt) {
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int ss = 0; ss < D / 16; ++ss) {
-          mma(s, row_frag<T, BM, D>(qs, 32 * mt + l32, 2 * ss + half), kf[ss]);
-          mma(dp, row_frag<T, BM, D>(dos, 32 * mt + l32, 2 * ss + half), vf[ss]);
-        }
+      for (int ss = 0; ss < D / 16; ++ss) {
+        mma(s, row_frag<T, BM, D>(qs, 32 * mt + l32, 2 * ss + half), kf[ss]);
+        mma(dp, row_frag<T, BM, D>(dos, 32 * mt + l32, 2 * ss + half), vf[ss]);
+      }
+      if (edge) {
+        // row r holds query qb*BM + 32mt + 8(r/4) + 4half + r%4; visible iff
+        // (unsigned)(p - j) < window with p = query + L_k - L_q
+        const int mb = qb * BM + 32 * mt + 4 * half + (lk - lq) - j;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rr = 32 * mt + acc_row(r, half);
-          float pv = fast_exp2(s[r] * c - lse2s[rr]);
-          if (edge && !cell_visible(sg, (int64_t)qb * BM + rr, j)) pv = 0.f;
+        for (int r = 0; r < 16; ++r)
+          if ((uint32_t)(mb + 8 * (r >> 2) + (r & 3)) >= wlim) s[r] = -INFINITY;
+      }
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int rr = 32 * mt + 8 * r4 + 4 * half;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + rr);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlts + rr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          const float pv = fast_exp2(fmaf(s[r], c, -l4[e]));
           s[r] = pv;
-          dp[r] = pv * (dp[r] - dlts[rr]);  // dS
+          dp[r] = pv * (dp[r] - d4[e]);  // dS
         }
+      }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const Frag<T> pf = acc_frag<T>(s, u);
-          const Frag<T> dsf = acc_frag<T>(dp, u);
+      for (int u = 0; u < 2; ++u) {
+        const Frag<T> pf = acc_frag<T>(s, u);
+        const Frag<T> dsf = acc_frag<T>(dp, u);
 #pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) {
-            mma(dva[dt], col_frag<T, BM, D>(dos, 32 * mt + 16 * u, 32 * dt, lane), pf);
-            mma(dka[dt], col_frag<T, BM, D>(qs, 32 * mt + 16 * u, 32 * dt, lane), dsf);
-          }
+        for (int dt = 0; dt < D / 32; ++dt) {
+          mma(dva[dt], col_frag<T, BM, D>(dos, 32 * mt + 16 * u, 32 * dt, lane), pf);
+          mma(dka[dt], col_frag<T, BM, D>(qs, 32 * mt + 16 * u, 32 * dt, lane), dsf);
         }
       }
     }
+    if (more) commit(smem + (stage ^ 1) * kStage);
+    __syncthreads();
   }
   if (key_ok) {
     const int64_t roff = (int64_t)(k0 + j) * kstride + g * D;
@@ -395,28 +533,25 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------- launchers
-template <typename T, int D> struct Tiles;
-// bf16 and fp32 share tile shapes: forward / dQ 128 query rows x 64 keys per
-// step (4 waves, 32 queries each); dK/dV 128 keys (4 waves, 32 keys each) x
-// 64 query rows per step.
-template <typename T, int D> struct Tiles {
+// Tile shapes (bf16 and fp32 alike): forward and dQ take 128 query rows (4
+// waves of 32) and step over keys 64 at a time; dK/dV takes 128 keys (4 waves
+// of 32) and steps over queries 64 at a time.
+struct Tiles {
   static constexpr int kFwdBM = 128, kFwdBN = 64, kBwdBN = 128, kBwdBM = 64;
 };
 
 template <typename T, int D>
 static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
-  using TL = Tiles<T, D>;
-  const int64_t nqb = (a.max_seqlen_q + TL::kFwdBM - 1) / TL::kFwdBM;
+  const int64_t nqb = (a.max_seqlen_q + Tiles::kFwdBM - 1) / Tiles::kFwdBM;
   const int64_t grid = nqb * a.heads_q * a.batch;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_kernel<T, D, TL::kFwdBM, TL::kFwdBN>), dim3((unsigned)grid),
-                     dim3(TL::kFwdBM * 2), 0, st, a);
+  hipLaunchKernelGGL((fwd_kernel<T, D, Tiles::kFwdBM, Tiles::kFwdBN>), dim3((unsigned)grid),
+                     dim3(Tiles::kFwdBM * 2), 0, st, a);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t launch_bwd_t(int stages, const AttnArgs& a, hipStream_t st) {
-  using TL = Tiles<T, D>;
   const int64_t rows = (int64_t)a.total_q * a.heads_q;
   if ((stages & 1) && rows > 0) {
     const int64_t g0 = (rows + (256 / (D / 8)) - 1) / (256 / (D / 8));
@@ -425,21 +560,21 @@ static hipError_t launch_bwd_t(int stages, const AttnArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if (stages & 2) {
-    const int64_t nqb = (a.max_seqlen_q + TL::kFwdBM - 1) / TL::kFwdBM;
+    const int64_t nqb = (a.max_seqlen_q + Tiles::kFwdBM - 1) / Tiles::kFwdBM;
     const int64_t g1 = nqb * a.heads_q * a.batch;
     if (g1 > 0 && rows > 0) {
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D, TL::kFwdBM, TL::kFwdBN>), dim3((unsigned)g1),
-                         dim3(TL::kFwdBM * 2), 0, st, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, Tiles::kFwdBM, Tiles::kFwdBN>), dim3((unsigned)g1),
+                         dim3(Tiles::kFwdBM * 2), 0, st, a);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
   if (stages & 4) {
-    const int64_t nkb = (a.max_seqlen_k + TL::kBwdBN - 1) / TL::kBwdBN;
+    const int64_t nkb = (a.max_seqlen_k + Tiles::kBwdBN - 1) / Tiles::kBwdBN;
     const int64_t g2 = nkb * a.heads_kv * a.batch;
     if (g2 > 0) {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, TL::kBwdBN, TL::kBwdBM>), dim3((unsigned)g2),
-                         dim3(TL::kBwdBN * 2), 0, st, a);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, Tiles::kBwdBN, Tiles::kBwdBM>), dim3((unsigned)g2),
+                         dim3(Tiles::kBwdBN * 2), 0, st, a);
       return hipGetLastError();
     }
   }
@@ -464,11 +599,10 @@ hipError_t launch_bwd(int dtype, int head_dim, int stages, const AttnArgs& a, hi
 
 bool tile_sizes(int dtype, int head_dim, int* fwd_bm, int* fwd_bn, int* bwd_bn, int* bwd_bm) {
   if ((dtype != 0 && dtype != 1) || (head_dim != 64 && head_dim != 128)) return false;
-  using TL = Tiles<bf16, 128>;
-  *fwd_bm = TL::kFwdBM;
-  *fwd_bn = TL::kFwdBN;
-  *bwd_bn = TL::kBwdBN;
-  *bwd_bm = TL::kBwdBM;
+  *fwd_bm = Tiles::kFwdBM;
+  *fwd_bn = Tiles::kFwdBN;
+  *bwd_bn = Tiles::kBwdBN;
+  *bwd_bm = Tiles::kBwdBM;
   return true;
 }
 

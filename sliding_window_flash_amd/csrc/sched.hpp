@@ -108,6 +108,17 @@ SWA_HD TileRange key_tile_queries(const SeqGeom& s, int32_t kb, int32_t bn, int3
   return r;
 }
 
+// Workgroups are handed to the 8 XCDs round-robin (id % 8), each XCD with its
+// own L2. Map launch id -> logical work id so that XCD x runs the contiguous
+// logical range [x*n/8, (x+1)*n/8) (remainder spread over the first XCDs):
+// neighbouring logical items, which share K/V rows, then share an L2. Any
+// bijection is correct; this one only decides locality.
+SWA_HD int32_t xcd_remap(int32_t id, int32_t n, int32_t nxcd = 8) {
+  const int32_t xcd = id % nxcd, slot = id / nxcd;
+  const int32_t per = n / nxcd, rem = n % nxcd;
+  return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
 // Per-cell visibility, used inside edge tiles.
 SWA_HD bool cell_visible(const SeqGeom& s, int64_t i, int64_t j) {
   if (i >= s.lq || j >= s.lk) return false;

@@ -50,6 +50,10 @@ def good(**kw):
     (dict(causal=False, window=100), 0),
     (dict(window=swa.INT32_MAX), 0),
     (dict(dtype=swa.ATTN_F32, head_dim=64), 0),
+    (dict(scale=0.0), 4),
+    (dict(scale=-0.1), 4),
+    (dict(scale=float("inf")), 4),
+    (dict(scale=float("nan")), 4),
 ])
 def test_parameter_checks(kw, code):
     assert swa.check_params(good(**kw)) == code

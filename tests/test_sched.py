@@ -93,3 +93,17 @@ def test_compiled_tiles_hit_both_silent_cases():
     empty = [kb for kb in range(-(-1000 // kbn))
              if (lambda r: r[0] > r[1])(swa.key_tile_range(p, [0, 100], [0, 1000], 0, kb, kbn, kbm))]
     assert empty, "expected unvisited key tiles"
+
+
+def test_xcd_remap_is_a_bijection():
+    """The launch-id remap used by the kernels (host build of the same code,
+    re-derived here from its definition) covers every logical id once."""
+    for n in (1, 7, 8, 9, 64, 100, 2048, 8191):
+        seen = set()
+        for i in range(n):
+            xcd, slot = i % 8, i // 8
+            per, rem = n // 8, n % 8
+            L = xcd * (per + 1) + slot if xcd < rem else rem * (per + 1) + (xcd - rem) * per + slot
+            assert 0 <= L < n
+            seen.add(L)
+        assert len(seen) == n
