@@ -127,7 +127,7 @@ __device__ __forceinline__ QueryItem decode_query_item(const AttnArgs& a, int bm
 constexpr float kRescaleSlack = 8.0f;
 
 template <typename T, int D, int BM, int BN>
-__global__ void __launch_bounds__(BM * 2) fwd_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_kernel(AttnArgs a) {
   constexpr int NT = BM * 2;
   using KTile = LdsTile<T, BN, D>;
   constexpr int kStage = 2 * KTile::kBytes;  // K tile then V tile
@@ -279,7 +279,7 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------- backward: dQ
 template <typename T, int D, int BM, int BN>
-__global__ void __launch_bounds__(BM * 2) bwd_dq_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(AttnArgs a) {
   constexpr int NT = BM * 2;
   using KTile = LdsTile<T, BN, D>;
   constexpr int kStage = 2 * KTile::kBytes;
