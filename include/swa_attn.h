@@ -102,8 +102,9 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o,
                        float* lse, void* stream);
 
-/* Bytes of device workspace attn_bwd needs for these parameters (D = rowsum(dO * O),
- * fp32 [heads_q, total_q], 256-byte aligned). 0 if the parameters are invalid. */
+/* Bytes of device workspace attn_bwd needs for these parameters: D =
+ * rowsum(dO * O) and LSE * log2(e), each fp32 [heads_q, total_q] and 256-byte
+ * aligned. 0 if the parameters are invalid. */
 size_t attn_bwd_workspace_bytes(const attn_params_t* p);
 
 /* Backward: the vector-Jacobian product of sum(O * dO). Reads Q, K, V, O, LSE
@@ -117,15 +118,15 @@ attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, con
                        void* stream);
 
 /* The backward's three stages, for callers that schedule them themselves:
- *   ATTN_BWD_DELTA: D = rowsum(dO * O) into the workspace;
- *   ATTN_BWD_DQ:    dQ (reads Q, K, V, dO, LSE and D);
- *   ATTN_BWD_DKDV:  dK and dV (reads Q, K, V, dO, LSE and D).
+ *   ATTN_BWD_DELTA: D = rowsum(dO * O) and LSE * log2(e) into the workspace;
+ *   ATTN_BWD_DQ:    dQ (reads Q, K, V, dO and the workspace);
+ *   ATTN_BWD_DKDV:  dK and dV (reads Q, K, V, dO and the workspace).
  * DQ and DKDV need a completed DELTA of the same call parameters and
  * workspace; they are independent of each other, so they may run on two
  * streams once DELTA is done. attn_bwd is attn_bwd_stages with all three, in
  * this order, on one stream. Same arguments and checks as attn_bwd; pointers a
- * selected stage does not read or write may be NULL (O is read only by DELTA,
- * dQ written only by DQ, dK and dV only by DKDV). */
+ * selected stage does not read or write may be NULL (O and LSE are read only
+ * by DELTA, dQ written only by DQ, dK and dV only by DKDV). */
 typedef enum {
   ATTN_BWD_DELTA = 1,
   ATTN_BWD_DQ = 2,

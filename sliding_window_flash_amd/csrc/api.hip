@@ -90,10 +90,16 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   return ATTN_OK;
 }
 
+// Workspace: D [heads_q, total_q] fp32, then LSE*log2(e) [heads_q, total_q]
+// fp32, each 256-byte aligned.
+static size_t ws_array_bytes(const attn_params_t* p) {
+  const size_t n = (size_t)p->heads_q * (size_t)p->total_q * sizeof(float);
+  return round_up(n > 0 ? n : 1, 256);
+}
+
 size_t attn_bwd_workspace_bytes(const attn_params_t* p) {
   if (attn_check_params(p) != ATTN_OK) return 0;
-  const size_t d_bytes = (size_t)p->heads_q * (size_t)p->total_q * sizeof(float);
-  return round_up(d_bytes > 0 ? d_bytes : 1, 256);
+  return 2 * ws_array_bytes(p);
 }
 
 attn_status_t attn_bwd_stages(const attn_params_t* p, int32_t stages, const void* q,
@@ -113,8 +119,8 @@ attn_status_t attn_bwd_stages(const attn_params_t* p, int32_t stages, const void
     if ((s = check_tensor(q, nq, true)) != ATTN_OK) return s;
     if ((s = check_tensor(k, nk, true)) != ATTN_OK) return s;
     if ((s = check_tensor(v, nk, true)) != ATTN_OK) return s;
-    if ((s = check_tensor(lse, nrow, false)) != ATTN_OK) return s;
   }
+  if (st_delta && (s = check_tensor(lse, nrow, false)) != ATTN_OK) return s;
   if (st_delta && (s = check_tensor(o, nq, true)) != ATTN_OK) return s;
   if ((s = check_tensor(dout, nq, true)) != ATTN_OK) return s;
   if (st_dq && (s = check_tensor(dq, nq, true)) != ATTN_OK) return s;
@@ -137,6 +143,7 @@ attn_status_t attn_bwd_stages(const attn_params_t* p, int32_t stages, const void
   a.dk = dk;
   a.dv = dv;
   a.delta = static_cast<float*>(workspace);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_array_bytes(p));
   if (swa::launch_bwd(p->dtype, p->head_dim, stages, a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;

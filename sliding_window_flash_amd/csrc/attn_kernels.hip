@@ -29,6 +29,8 @@
 // barrier per step suffices.
 #include <math.h>
 
+#include <type_traits>
+
 #include "kernel_common.hpp"
 #include "launch.hpp"
 #include "sched.hpp"
@@ -90,6 +92,16 @@ struct TileStage {
   }
 };
 
+// K and V key tile kb of one sequence into an LDS stage (K tile, then V tile).
+template <typename T, int BN, int D, int NT>
+__device__ __forceinline__ void fill_kv(char* st, const T* __restrict__ K, const T* __restrict__ V,
+                                        int64_t kstride, int kb, int lk, int wave, int lane) {
+  const int kvalid = min(BN, lk - kb * BN);
+  dma_tile<T, BN, D, NT>(st, K + (int64_t)kb * BN * kstride, kstride, kvalid, wave, lane);
+  dma_tile<T, BN, D, NT>(st + LdsTile<T, BN, D>::kBytes, V + (int64_t)kb * BN * kstride, kstride, kvalid,
+                         wave, lane);
+}
+
 struct QueryItem {
   int qb, h, b, q0, lq, k0, lk;
 };
@@ -126,12 +138,16 @@ __device__ __forceinline__ QueryItem decode_query_item(const AttnArgs& a, int bm
 // is the same softmax: O and LSE use the same reference at the end.
 constexpr float kRescaleSlack = 8.0f;
 
+template <int N> using ic = std::integral_constant<int, N>;
+
 template <typename T, int D, int BM, int BN>
 __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_kernel(AttnArgs a) {
   constexpr int NT = BM * 2;
   using KTile = LdsTile<T, BN, D>;
-  constexpr int kStage = 2 * KTile::kBytes;  // K tile then V tile
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  // two stages (K tile then V tile each), separate arrays so that reading one
+  // need not wait for the asynchronous fill of the other
+  __shared__ __attribute__((aligned(1024))) char st0[2 * KTile::kBytes];
+  __shared__ __attribute__((aligned(1024))) char st1[2 * KTile::kBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const QueryItem it = decode_query_item(a, BM);
@@ -154,9 +170,14 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qf[s] = row_ok ? global_frag<T>(qrow + 16 * s) : zero_frag<T>();
   }
+  RowReader<T, D> rrd;
+  rrd.init(l32, half);
+  ColReader<T, D> crd;
+  crd.init(lane);
   // Edge mask: visible iff (unsigned)(mpos - j) < mlim. Causal: mpos = p,
   // mlim = window (covers j <= p and p - j < window). Full attention: mpos =
-  // L_k - 1, mlim = 2^31 - 1 (covers j < L_k).
+  // L_k - 1, mlim = 2^31 - 1 (covers j < L_k). Key rows past L_k in the last
+  // tile hold copies of row L_k - 1 and are always masked.
   const int mpos = a.causal ? i + (it.lk - it.lq) : it.lk - 1;
   const uint32_t mlim = a.causal ? (uint32_t)a.window : 0x7fffffffu;
 
@@ -166,34 +187,21 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
   float m = -INFINITY, lsum = 0.f;
   const float c = a.scale * kLog2e;
 
-  TileStage<T, BN, D, NT> sk, sv;
-  if (kr.lo <= kr.hi) {
-    const int kvalid = min(BN, it.lk - kr.lo * BN);
-    sk.load(K + (int64_t)kr.lo * BN * kstride, kstride, kvalid, tid);
-    sv.load(V + (int64_t)kr.lo * BN * kstride, kstride, kvalid, tid);
-    sk.store(smem, tid);
-    sv.store(smem + KTile::kBytes, tid);
-  }
+  if (kr.lo <= kr.hi) fill_kv<T, BN, D, NT>(st0, K, V, kstride, kr.lo, it.lk, w, lane);
   __syncthreads();
 
-  for (int kb = kr.lo; kb <= kr.hi; ++kb) {
-    const int stage = (kb - kr.lo) & 1;
-    const char* ks = smem + stage * kStage;
+  // One key tile; `stage` (compile time) selects the LDS stage it reads.
+  auto step = [&](auto stage_c, int kb) {
+    constexpr int stage = decltype(stage_c)::value;
+    const char* ks = stage ? st1 : st0;
     const char* vs = ks + KTile::kBytes;
-    const bool more = kb < kr.hi;
-    if (more) {
-      const int kvalid = min(BN, it.lk - (kb + 1) * BN);
-      sk.load(K + (int64_t)(kb + 1) * BN * kstride, kstride, kvalid, tid);
-      sv.load(V + (int64_t)(kb + 1) * BN * kstride, kstride, kvalid, tid);
-    }
-
+    if (kb < kr.hi) fill_kv<T, BN, D, NT>(stage ? st0 : st1, K, V, kstride, kb + 1, it.lk, w, lane);
     f32x16 s[BN / 32];
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt) {
       s[kt] = f32x16{};
 #pragma unroll
-      for (int ss = 0; ss < D / 16; ++ss)
-        mma(s[kt], row_frag<T, BN, D>(ks, 32 * kt + l32, 2 * ss + half), qf[ss]);
+      for (int ss = 0; ss < D / 16; ++ss) mma(s[kt], rrd.read(ks, 32 * kt, ss), qf[ss]);
     }
     if (!(kr.full_lo <= kb && kb <= kr.full_hi)) {
       const int mb = mpos - (kb * BN + 4 * half);
@@ -234,14 +242,15 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
     for (int u = 0; u < BN / 16; ++u) {
       const Frag<T> pf = acc_frag<T>(s[u >> 1], u & 1);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) mma(acc[dt], col_frag<T, BN, D>(vs, 16 * u, 32 * dt, lane), pf);
-    }
-    if (more) {
-      char* nk = smem + (stage ^ 1) * kStage;
-      sk.store(nk, tid);
-      sv.store(nk + KTile::kBytes, tid);
+      for (int dt = 0; dt < D / 32; ++dt) mma(acc[dt], crd.read(vs, 16 * u, dt), pf);
     }
     __syncthreads();
+  };
+  for (int kb = kr.lo; kb <= kr.hi;) {
+    step(ic<0>{}, kb);
+    if (++kb > kr.hi) break;
+    step(ic<1>{}, kb);
+    ++kb;
   }
 
   const float ltot = lsum + xor32(lsum);
@@ -255,7 +264,10 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
   }
 }
 
-// ------------------------------------------------------ backward: D = rowsum(dO*O)
+// ------------------------------------------ backward: D = rowsum(dO*O), LSE*log2e
+// The second output lets the other backward kernels copy LSE into LDS raw:
+// P = 2^(S * scale * log2e - LSE * log2e); a row without visible keys
+// (LSE = -inf) gets +inf, so its P is 0.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_delta_kernel(AttnArgs a) {
   constexpr int LPR = D / 8;  // lanes per (token, head) row, 8 elements each
@@ -274,6 +286,8 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(AttnArgs a) {
   if (sub == 0 && row < rows) {
     const int64_t t = row / a.heads_q, h = row % a.heads_q;
     a.delta[h * a.total_q + t] = acc;
+    const float l = a.lse[h * a.total_q + t];
+    a.lse2[h * a.total_q + t] = l == -INFINITY ? INFINITY : l * kLog2e;
   }
 }
 
@@ -282,8 +296,8 @@ template <typename T, int D, int BM, int BN>
 __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(AttnArgs a) {
   constexpr int NT = BM * 2;
   using KTile = LdsTile<T, BN, D>;
-  constexpr int kStage = 2 * KTile::kBytes;
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  __shared__ __attribute__((aligned(1024))) char st0[2 * KTile::kBytes];
+  __shared__ __attribute__((aligned(1024))) char st1[2 * KTile::kBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const QueryItem it = decode_query_item(a, BM);
@@ -311,11 +325,14 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
       df[s] = row_ok ? global_frag<T>(drow + 16 * s) : zero_frag<T>();
     }
     if (row_ok) {
-      const float l = a.lse[(int64_t)it.h * a.total_q + it.q0 + i];
-      lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+      lse2 = a.lse2[(int64_t)it.h * a.total_q + it.q0 + i];
       dlt = a.delta[(int64_t)it.h * a.total_q + it.q0 + i];
     }
   }
+  RowReader<T, D> rrd;
+  rrd.init(l32, half);
+  ColReader<T, D> crd;
+  crd.init(lane);
   const int mpos = a.causal ? i + (it.lk - it.lq) : it.lk - 1;
   const uint32_t mlim = a.causal ? (uint32_t)a.window : 0x7fffffffu;
   // cleared before the first visited key tile (kr.lo), not on key tile zero
@@ -324,34 +341,22 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
   const float c = a.scale * kLog2e;
 
-  TileStage<T, BN, D, NT> sk, sv;
-  if (kr.lo <= kr.hi) {
-    const int kvalid = min(BN, it.lk - kr.lo * BN);
-    sk.load(K + (int64_t)kr.lo * BN * kstride, kstride, kvalid, tid);
-    sv.load(V + (int64_t)kr.lo * BN * kstride, kstride, kvalid, tid);
-    sk.store(smem, tid);
-    sv.store(smem + KTile::kBytes, tid);
-  }
+  if (kr.lo <= kr.hi) fill_kv<T, BN, D, NT>(st0, K, V, kstride, kr.lo, it.lk, w, lane);
   __syncthreads();
 
-  for (int kb = kr.lo; kb <= kr.hi; ++kb) {
-    const int stage = (kb - kr.lo) & 1;
-    const char* ks = smem + stage * kStage;
+  auto step = [&](auto stage_c, int kb) {
+    constexpr int stage = decltype(stage_c)::value;
+    const char* ks = stage ? st1 : st0;
     const char* vs = ks + KTile::kBytes;
-    const bool more = kb < kr.hi;
-    if (more) {
-      const int kvalid = min(BN, it.lk - (kb + 1) * BN);
-      sk.load(K + (int64_t)(kb + 1) * BN * kstride, kstride, kvalid, tid);
-      sv.load(V + (int64_t)(kb + 1) * BN * kstride, kstride, kvalid, tid);
-    }
+    if (kb < kr.hi) fill_kv<T, BN, D, NT>(stage ? st0 : st1, K, V, kstride, kb + 1, it.lk, w, lane);
     const bool edge = !(kr.full_lo <= kb && kb <= kr.full_hi);
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ss = 0; ss < D / 16; ++ss) {
-        mma(s, row_frag<T, BN, D>(ks, 32 * kt + l32, 2 * ss + half), qf[ss]);
-        mma(dp, row_frag<T, BN, D>(vs, 32 * kt + l32, 2 * ss + half), df[ss]);
+        mma(s, rrd.read(ks, 32 * kt, ss), qf[ss]);
+        mma(dp, rrd.read(vs, 32 * kt, ss), df[ss]);
       }
       if (edge) {
         const int mb = mpos - (kb * BN + 32 * kt + 4 * half);
@@ -368,16 +373,16 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
       for (int u = 0; u < 2; ++u) {
         const Frag<T> dsf = acc_frag<T>(s, u);
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-          mma(acc[dt], col_frag<T, BN, D>(ks, 32 * kt + 16 * u, 32 * dt, lane), dsf);
+        for (int dt = 0; dt < D / 32; ++dt) mma(acc[dt], crd.read(ks, 32 * kt + 16 * u, dt), dsf);
       }
     }
-    if (more) {
-      char* nk = smem + (stage ^ 1) * kStage;
-      sk.store(nk, tid);
-      sv.store(nk + KTile::kBytes, tid);
-    }
     __syncthreads();
+  };
+  for (int kb = kr.lo; kb <= kr.hi;) {
+    step(ic<0>{}, kb);
+    if (++kb > kr.hi) break;
+    step(ic<1>{}, kb);
+    ++kb;
   }
   if (row_ok) {
     T* row = static_cast<T*>(a.dq) + (int64_t)(it.q0 + i) * qstride + it.h * D;
@@ -386,10 +391,196 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
 }
 
 // ---------------------------------------------------------- backward: dK, dV
+// One workgroup per (KV head, sequence, key tile of BN = 128 keys), 8 waves:
+// wave w owns keys 32*(w%4) .. +31 and, in every BM = 64-row query step, the
+// query rows 32*(w/4) .. +31. K and V sit in LDS once per workgroup (the B
+// operands of S = Q K^T and dP = dO V^T), so the dK/dV accumulators fit beside
+// everything else at two waves per SIMD. The two query halves' partial dK/dV
+// are summed through LDS at the end.
 // Key-major decode: KV head outermost, then sequence, then key tile ascending
 // (for the causal mask early key tiles are seen by the most queries).
 template <typename T, int D, int BN, int BM>
-__global__ void __launch_bounds__(BN * 2) bwd_dkdv_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(BN * 4) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dkdv_kernel(AttnArgs a) {
+  constexpr int NT = BN * 4;  // 8 waves for BN = 128
+  static_assert(BN == 128 && BM == 64, "wave layout assumes 4 key blocks x 2 query halves");
+  using QTile = LdsTile<T, BM, D>;
+  using KTile = LdsTile<T, BN, D>;
+  constexpr int kStage = 2 * QTile::kBytes + 2 * BM * 4;  // Q, dO, LSE*log2e, D
+  constexpr int kRedBlock = 32 * D * 4;                   // fp32 partial of one 32-key block
+  static_assert(KTile::kBytes >= 2 * kRedBlock && kStage >= 2 * kRedBlock, "reduction reuse");
+  __shared__ __attribute__((aligned(1024))) char st0[kStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kStage];
+  __shared__ __attribute__((aligned(1024))) char klds[KTile::kBytes];
+  __shared__ __attribute__((aligned(1024))) char vlds[KTile::kBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
+  const int kt = w & 3, mh = w >> 2;
+  const int nkb = (a.max_seqlen_k + BN - 1) / BN;
+  int L = xcd_remap((int)blockIdx.x, nkb * a.heads_kv * a.batch);
+  const int kb = L % nkb;
+  L /= nkb;
+  const int b = L % a.batch;
+  const int g = L / a.batch;
+  const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
+  const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
+  if (kb * BN >= lk) return;
+  const int grp = a.heads_q / a.heads_kv;
+  const bool causal = a.causal != 0;
+  const SeqGeom sg{lq, lk, a.window, causal};
+  const TileRange qr = key_tile_queries(sg, kb, BN, BM);
+
+  const int64_t qstride = (int64_t)a.heads_q * D;
+  const int64_t kstride = (int64_t)a.heads_kv * D;
+  const int j = kb * BN + 32 * kt + l32;  // this lane's key (rows past L_k hold copies; not stored)
+  const bool key_ok = j < lk;
+  {
+    const int kvalid = min(BN, lk - kb * BN);
+    const int64_t koff = (int64_t)(k0 + kb * BN) * kstride + g * D;
+    dma_tile<T, BN, D, NT>(klds, static_cast<const T*>(a.k) + koff, kstride, kvalid, w, lane);
+    dma_tile<T, BN, D, NT>(vlds, static_cast<const T*>(a.v) + koff, kstride, kvalid, w, lane);
+  }
+  RowReader<T, D> rrd;
+  rrd.init(l32, half);
+  ColReader<T, D> crd;
+  crd.init(lane);
+  f32x16 dka[D / 32], dva[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    dka[dt] = f32x16{};
+    dva[dt] = f32x16{};
+  }
+  const float c = a.scale * kLog2e;
+  const uint32_t wlim = (uint32_t)a.window;
+  const T* __restrict__ Qg = static_cast<const T*>(a.q);
+  const T* __restrict__ Dg = static_cast<const T*>(a.dout);
+
+  // Steps walk (head, query tile) pairs: head g*grp .. g*grp+grp-1 outer,
+  // query tile qr.lo .. qr.hi inner. An empty range (no query sees this key
+  // tile) has no steps and writes zeros.
+  const int nq = qr.hi >= qr.lo ? qr.hi - qr.lo + 1 : 0;
+  const int steps = grp * nq;
+  int nh = g * grp, nqb = qr.lo;  // (head, query tile) of the next step to fill
+  // Query rows past L_q in a tile hold copies of row L_q - 1; they are masked.
+  auto fill = [&](char* st) {
+    const int qvalid = min(BM, lq - nqb * BM);
+    const int64_t qoff = (int64_t)(q0 + nqb * BM) * qstride + nh * D;
+    dma_tile<T, BM, D, NT>(st, Qg + qoff, qstride, qvalid, w, lane);
+    dma_tile<T, BM, D, NT>(st + QTile::kBytes, Dg + qoff, qstride, qvalid, w, lane);
+    if (w == 0) {
+      const int64_t idx = (int64_t)nh * a.total_q + q0 + nqb * BM + min(lane, qvalid - 1);
+      __builtin_amdgcn_global_load_lds(a.lse2 + idx,
+          (__attribute__((address_space(3))) void*)(st + 2 * QTile::kBytes), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.delta + idx,
+          (__attribute__((address_space(3))) void*)(st + 2 * QTile::kBytes + BM * 4), 4, 0, 0);
+    }
+    if (++nqb > qr.hi) {
+      nqb = qr.lo;
+      ++nh;
+    }
+  };
+  if (steps > 0) fill(st0);
+  __syncthreads();
+
+  int qb = qr.lo;  // query tile of the current step
+  auto step = [&](auto stage_c, int t) {
+    constexpr int stage = decltype(stage_c)::value;
+    const char* qs = stage ? st1 : st0;
+    const char* dos = qs + QTile::kBytes;
+    const float* lse2s = reinterpret_cast<const float*>(qs + 2 * QTile::kBytes);
+    const float* dlts = lse2s + BM;
+    if (t + 1 < steps) fill(stage ? st0 : st1);
+    const bool edge = !tile_full_i32(lq, lk, a.window, causal, qb, BM, kb, BN);
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int ss = 0; ss < D / 16; ++ss) {
+      mma(s, rrd.read(qs, 32 * mh, ss), rrd.read(klds, 32 * kt, ss));
+      mma(dp, rrd.read(dos, 32 * mh, ss), rrd.read(vlds, 32 * kt, ss));
+    }
+    if (edge) {
+      // row r holds query ib + 8(r/4) + r%4: visible iff it is a real row
+      // (< L_q) and, causal, (unsigned)(p - j) < window with p = query + L_k - L_q
+      const int ib = qb * BM + 32 * mh + 4 * half;
+      const int mb = ib + (lk - lq) - j;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        if (ib + off >= lq || (causal && (uint32_t)(mb + off) >= wlim)) s[r] = -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int rr = 32 * mh + 8 * r4 + 4 * half;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + rr);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlts + rr);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * r4 + e;
+        const float pv = fast_exp2(fmaf(s[r], c, -l4[e]));
+        s[r] = pv;
+        dp[r] = pv * (dp[r] - d4[e]);  // dS
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const Frag<T> pf = acc_frag<T>(s, u);
+      const Frag<T> dsf = acc_frag<T>(dp, u);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        mma(dva[dt], crd.read(dos, 32 * mh + 16 * u, dt), pf);
+        mma(dka[dt], crd.read(qs, 32 * mh + 16 * u, dt), dsf);
+      }
+    }
+    if (++qb > qr.hi) qb = qr.lo;
+    __syncthreads();
+  };
+  for (int t = 0; t < steps;) {
+    step(ic<0>{}, t);
+    if (++t >= steps) break;
+    step(ic<1>{}, t);
+    ++t;
+  }
+
+  // Sum the two query halves: half 1 hands its dK partial to half 0 and half 0
+  // hands its dV partial to half 1, through fp32 LDS in the accumulator layout
+  // (one 32-key block per wave, reusing the K/V tiles and the stages).
+  float* red_k = reinterpret_cast<float*>((kt < 2 ? klds : vlds) + (kt & 1) * kRedBlock);
+  float* red_v = reinterpret_cast<float*>((kt < 2 ? st0 : st1) + (kt & 1) * kRedBlock);
+  if (steps > 0) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int o = lane + (dt * 16 + r) * 64;
+        if (mh == 1) red_k[o] = dka[dt][r];
+        else red_v[o] = dva[dt][r];
+      }
+  }
+  __syncthreads();
+  if (steps > 0) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int o = lane + (dt * 16 + r) * 64;
+        if (mh == 0) dka[dt][r] += red_k[o];
+        else dva[dt][r] += red_v[o];
+      }
+  }
+  if (key_ok) {
+    const int64_t roff = (int64_t)(k0 + j) * kstride + g * D;
+    if (mh == 0) store_acc_rows<T, D>(static_cast<T*>(a.dk) + roff, dka, a.scale, half);
+    else store_acc_rows<T, D>(static_cast<T*>(a.dv) + roff, dva, 1.f, half);
+  }
+}
+
+// ------------------------------------------------ backward: dK, dV (4 waves)
+// The general dK/dV kernel (used for fp32, whose tiles are twice as large):
+// 4 waves of 32 keys, K and V in registers, 64-query steps.
+// Key-major decode: KV head outermost, then sequence, then key tile ascending
+// (for the causal mask early key tiles are seen by the most queries).
+template <typename T, int D, int BN, int BM>
+__global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
   constexpr int NT = BN * 2;
   using QTile = LdsTile<T, BM, D>;
   constexpr int kStage = 2 * QTile::kBytes + 2 * BM * 4;  // Q, dO, LSE*log2e, D
@@ -453,8 +644,7 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv_kernel(AttnArgs a) {
     dlv = 0.f;
     if (tid < qvalid) {
       const int64_t idx = (int64_t)h * a.total_q + q0 + qb * BM + tid;
-      const float l = a.lse[idx];
-      l2v = l == -INFINITY ? INFINITY : l * kLog2e;
+      l2v = a.lse2[idx];
       dlv = a.delta[idx];
     }
   };
@@ -534,8 +724,9 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- launchers
 // Tile shapes (bf16 and fp32 alike): forward and dQ take 128 query rows (4
-// waves of 32) and step over keys 64 at a time; dK/dV takes 128 keys (4 waves
-// of 32) and steps over queries 64 at a time.
+// waves of 32) and step over keys 64 at a time; dK/dV takes 128 keys (8
+// waves: 4 key blocks of 32 x 2 query halves) and steps over queries 64 at a
+// time.
 struct Tiles {
   static constexpr int kFwdBM = 128, kFwdBN = 64, kBwdBN = 128, kBwdBM = 64;
 };
@@ -573,8 +764,12 @@ static hipError_t launch_bwd_t(int stages, const AttnArgs& a, hipStream_t st) {
     const int64_t nkb = (a.max_seqlen_k + Tiles::kBwdBN - 1) / Tiles::kBwdBN;
     const int64_t g2 = nkb * a.heads_kv * a.batch;
     if (g2 > 0) {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, Tiles::kBwdBN, Tiles::kBwdBM>), dim3((unsigned)g2),
-                         dim3(Tiles::kBwdBN * 2), 0, st, a);
+      if constexpr (sizeof(T) == 2)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, Tiles::kBwdBN, Tiles::kBwdBM>), dim3((unsigned)g2),
+                           dim3(Tiles::kBwdBN * 4), 0, st, a);
+      else
+        hipLaunchKernelGGL((bwd_dkdv4_kernel<T, D, Tiles::kBwdBN, Tiles::kBwdBM>), dim3((unsigned)g2),
+                           dim3(Tiles::kBwdBN * 2), 0, st, a);
       return hipGetLastError();
     }
   }

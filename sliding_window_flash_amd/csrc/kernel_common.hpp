@@ -179,6 +179,112 @@ __device__ __forceinline__ Frag<T> col_frag(const char* lds, int kbase, int nbas
   return f;
 }
 
+// Row and column fragment readers with per-lane offsets computed once. The
+// swizzle depends only on row % 16, so for a row block starting at a multiple
+// of 16 rows every address is (block start x row bytes) + a per-lane offset:
+// with the block start and the LDS stage known at compile time, each read is
+// one register plus an immediate.
+template <typename T, int D>
+struct RowReader {
+  using Tile = LdsTile<T, 16, D>;
+  static constexpr int kSteps = D / 16;
+  static constexpr int kParts = sizeof(T) == 2 ? 1 : 2;  // 16-byte chunks per fragment
+  int off[kSteps][kParts];
+  __device__ __forceinline__ void init(int l32, int half) {
+#pragma unroll
+    for (int ss = 0; ss < kSteps; ++ss)
+#pragma unroll
+      for (int q = 0; q < kParts; ++q) off[ss][q] = Tile::chunk_off(l32, kParts * (2 * ss + half) + q);
+  }
+  // same as row_frag(base, row16 + lane%32, 2*ss + half); row16 % 16 == 0
+  __device__ __forceinline__ Frag<T> read(const char* base, int row16, int ss) const {
+    const char* p = base + row16 * Tile::kRowBytes;
+    Frag<T> f;
+    if constexpr (sizeof(T) == 2) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(p + off[ss][0]);
+      f.v = __builtin_bit_cast(bf16x8, raw);
+    } else {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(p + off[ss][0]);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(p + off[ss][1]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f.v[j] = a[j];
+        f.v[4 + j] = b[j];
+      }
+    }
+    return f;
+  }
+};
+
+template <typename T, int D>
+struct ColReader {
+  using Tile = LdsTile<T, 16, D>;
+  static constexpr int kBlocks = D / 32;
+  static constexpr int kParts = sizeof(T) == 2 ? 2 : 8;  // transposing reads / scalar reads
+  int off[kBlocks][kParts];
+  __device__ __forceinline__ void init(int lane) {
+    const int half = lane >> 5;
+#pragma unroll
+    for (int dt = 0; dt < kBlocks; ++dt) {
+      if constexpr (sizeof(T) == 2) {
+        const int r = lane & 15;
+        const int col = 32 * dt + (lane & 16) + 4 * (r & 3);
+        off[dt][0] = Tile::elem_off(4 * half + (r >> 2), col);
+        off[dt][1] = Tile::elem_off(8 + 4 * half + (r >> 2), col);
+      } else {
+        const int n = 32 * dt + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          off[dt][j] = Tile::elem_off(j < 4 ? 4 * half + j : 8 + 4 * half + (j - 4), n);
+      }
+    }
+  }
+  // same as col_frag(base, kbase, 32*dt, lane); kbase % 16 == 0
+  __device__ __forceinline__ Frag<T> read(const char* base, int kbase, int dt) const {
+    const char* p = base + kbase * Tile::kRowBytes;
+    Frag<T> f;
+    if constexpr (sizeof(T) == 2) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(p + off[dt][0]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(p + off[dt][1]));
+      short s8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f.v[j] = __builtin_bit_cast(bf16, s8[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f.v[j] = *reinterpret_cast<const float*>(p + off[dt][j]);
+    }
+    return f;
+  }
+};
+
+// Direct global -> LDS copy of a ROWS x D tile into the swizzled layout
+// (global_load_lds_dwordx4: each wave instruction writes 64 consecutive
+// 16-byte LDS slots; the lane of physical slot (row, pc) fetches logical chunk
+// pc ^ swz(row) of that row). Rows >= valid re-read row valid - 1, so every
+// address stays inside the tensor; callers mask those rows. No registers hold
+// the data: it lands in LDS asynchronously, and the compiler waits for it
+// (vmcnt) before the next barrier. `lds` is a stage of its own __shared__
+// array, so reads of the other stage need not wait.
+template <typename T, int ROWS, int D, int NT>
+__device__ __forceinline__ void dma_tile(char* lds, const T* __restrict__ src, int64_t stride, int valid,
+                                         int wave, int lane) {
+  using Tile = LdsTile<T, ROWS, D>;
+  constexpr int kInstr = ROWS * Tile::kChunks / 64;
+  constexpr int kPerWave = kInstr / (NT / 64);
+  static_assert(kInstr % (NT / 64) == 0, "tile must split evenly over the waves");
+#pragma unroll
+  for (int e = 0; e < kPerWave; ++e) {
+    const int slot = (wave * kPerWave + e) * 64 + lane;
+    const int row = slot / Tile::kChunks, pc = slot % Tile::kChunks;
+    const int rg = row < valid ? row : valid - 1;
+    const T* g = src + (int64_t)rg * stride + (pc ^ Tile::swz(row)) * Tile::kElemsPerChunk;
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds + (wave * kPerWave + e) * 1024),
+                                     16, 0, 0);
+  }
+}
+
 // Fragment straight from global memory: 8 consecutive elements at p.
 template <typename T> __device__ __forceinline__ Frag<T> global_frag(const T* __restrict__ p) {
   Frag<T> f;
@@ -229,6 +335,7 @@ struct AttnArgs {
   void* dk;
   void* dv;
   float* delta;  // D = rowsum(dO * O), [heads_q, total_q]
+  float* lse2;   // LSE * log2(e) (+inf where LSE = -inf), [heads_q, total_q]
   int32_t batch, heads_q, heads_kv, total_q, total_k, max_seqlen_q, max_seqlen_k;
   int32_t window, causal;
   float scale;

@@ -127,6 +127,19 @@ SWA_HD bool cell_visible(const SeqGeom& s, int64_t i, int64_t j) {
   return j <= p && p - j < s.window;
 }
 
+// The same test in int32 closed form, for the kernels' inner loops: every
+// cell of (query tile qb, key tile kb) is visible iff the query tile has all bm
+// rows, the key tile all bn keys, and (causal) its last key is <= the first
+// query's position and the last query's position minus its first key is
+// < window. Requires positions < 2^31 (guaranteed by the ABI's int32 sizes).
+SWA_HD bool tile_full_i32(int32_t lq, int32_t lk, int32_t window, bool causal, int32_t qb,
+                          int32_t bm, int32_t kb, int32_t bn) {
+  const int32_t i0 = qb * bm, j0 = kb * bn, delta = lk - lq;
+  if (i0 + bm > lq || j0 + bn > lk) return false;
+  if (!causal) return true;
+  return j0 + bn - 1 <= i0 + delta && (i0 + bm - 1 + delta) - j0 < window;
+}
+
 // Is tile (query tile qb, key tile kb) free of masked cells?
 SWA_HD bool tile_is_full(const SeqGeom& s, int32_t qb, int32_t bm, int32_t kb, int32_t bn) {
   const TileRange r = query_tile_keys(s, qb, bm, bn);
