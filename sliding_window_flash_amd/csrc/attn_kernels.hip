@@ -97,8 +97,8 @@ template <typename T, int BN, int D, int NT>
 __device__ __forceinline__ void fill_kv(char* st, const T* __restrict__ K, const T* __restrict__ V,
                                         int64_t kstride, int kb, int lk, int wave, int lane) {
   const int kvalid = min(BN, lk - kb * BN);
-  dma_tile<T, BN, D, NT>(st, K + (int64_t)kb * BN * kstride, kstride, kvalid, wave, lane);
-  dma_tile<T, BN, D, NT>(st + LdsTile<T, BN, D>::kBytes, V + (int64_t)kb * BN * kstride, kstride, kvalid,
+  DmaTile<T, BN, D, NT>::run(st, K + (int64_t)kb * BN * kstride, kstride, kvalid, wave, lane);
+  DmaTile<T, BN, D, NT>::run(st + LdsTile<T, BN, D>::kBytes, V + (int64_t)kb * BN * kstride, kstride, kvalid,
                          wave, lane);
 }
 
@@ -414,7 +414,8 @@ bwd_dkdv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char klds[KTile::kBytes];
   __shared__ __attribute__((aligned(1024))) char vlds[KTile::kBytes];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int w = wave_uniform(tid >> 6);
   const int kt = w & 3, mh = w >> 2;
   const int nkb = (a.max_seqlen_k + BN - 1) / BN;
   int L = xcd_remap((int)blockIdx.x, nkb * a.heads_kv * a.batch);
@@ -437,8 +438,8 @@ bwd_dkdv_kernel(AttnArgs a) {
   {
     const int kvalid = min(BN, lk - kb * BN);
     const int64_t koff = (int64_t)(k0 + kb * BN) * kstride + g * D;
-    dma_tile<T, BN, D, NT>(klds, static_cast<const T*>(a.k) + koff, kstride, kvalid, w, lane);
-    dma_tile<T, BN, D, NT>(vlds, static_cast<const T*>(a.v) + koff, kstride, kvalid, w, lane);
+    DmaTile<T, BN, D, NT>::run(klds, static_cast<const T*>(a.k) + koff, kstride, kvalid, w, lane);
+    DmaTile<T, BN, D, NT>::run(vlds, static_cast<const T*>(a.v) + koff, kstride, kvalid, w, lane);
   }
   RowReader<T, D> rrd;
   rrd.init(l32, half);
@@ -461,12 +462,14 @@ bwd_dkdv_kernel(AttnArgs a) {
   const int nq = qr.hi >= qr.lo ? qr.hi - qr.lo + 1 : 0;
   const int steps = grp * nq;
   int nh = g * grp, nqb = qr.lo;  // (head, query tile) of the next step to fill
+  DmaPlan<T, BM, D, NT> qplan;
+  qplan.init(qstride, w, lane);
   // Query rows past L_q in a tile hold copies of row L_q - 1; they are masked.
   auto fill = [&](char* st) {
     const int qvalid = min(BM, lq - nqb * BM);
     const int64_t qoff = (int64_t)(q0 + nqb * BM) * qstride + nh * D;
-    dma_tile<T, BM, D, NT>(st, Qg + qoff, qstride, qvalid, w, lane);
-    dma_tile<T, BM, D, NT>(st + QTile::kBytes, Dg + qoff, qstride, qvalid, w, lane);
+    qplan.issue(st, Qg + qoff, qstride, qvalid);
+    qplan.issue(st + QTile::kBytes, Dg + qoff, qstride, qvalid);
     if (w == 0) {
       const int64_t idx = (int64_t)nh * a.total_q + q0 + nqb * BM + min(lane, qvalid - 1);
       __builtin_amdgcn_global_load_lds(a.lse2 + idx,
@@ -744,11 +747,11 @@ static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
 template <typename T, int D>
 static hipError_t launch_bwd_t(int stages, const AttnArgs& a, hipStream_t st) {
   const int64_t rows = (int64_t)a.total_q * a.heads_q;
+  hipError_t e = hipSuccess;
   if ((stages & 1) && rows > 0) {
     const int64_t g0 = (rows + (256 / (D / 8)) - 1) / (256 / (D / 8));
     hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)g0), dim3(256), 0, st, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 2) {
     const int64_t nqb = (a.max_seqlen_q + Tiles::kFwdBM - 1) / Tiles::kFwdBM;
@@ -756,22 +759,19 @@ static hipError_t launch_bwd_t(int stages, const AttnArgs& a, hipStream_t st) {
     if (g1 > 0 && rows > 0) {
       hipLaunchKernelGGL((bwd_dq_kernel<T, D, Tiles::kFwdBM, Tiles::kFwdBN>), dim3((unsigned)g1),
                          dim3(Tiles::kFwdBM * 2), 0, st, a);
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
+      if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
-  if (stages & 4) {
-    const int64_t nkb = (a.max_seqlen_k + Tiles::kBwdBN - 1) / Tiles::kBwdBN;
-    const int64_t g2 = nkb * a.heads_kv * a.batch;
-    if (g2 > 0) {
-      if constexpr (sizeof(T) == 2)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, Tiles::kBwdBN, Tiles::kBwdBM>), dim3((unsigned)g2),
-                           dim3(Tiles::kBwdBN * 4), 0, st, a);
-      else
-        hipLaunchKernelGGL((bwd_dkdv4_kernel<T, D, Tiles::kBwdBN, Tiles::kBwdBM>), dim3((unsigned)g2),
-                           dim3(Tiles::kBwdBN * 2), 0, st, a);
-      return hipGetLastError();
-    }
+  const int64_t nkb = (a.max_seqlen_k + Tiles::kBwdBN - 1) / Tiles::kBwdBN;
+  const int64_t g2 = nkb * a.heads_kv * a.batch;
+  if ((stages & 4) && g2 > 0) {
+    if constexpr (sizeof(T) == 2)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, Tiles::kBwdBN, Tiles::kBwdBM>), dim3((unsigned)g2),
+                         dim3(Tiles::kBwdBN * 4), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv4_kernel<T, D, Tiles::kBwdBN, Tiles::kBwdBM>), dim3((unsigned)g2),
+                         dim3(Tiles::kBwdBN * 2), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
 }

@@ -268,22 +268,56 @@ struct ColReader {
 // (vmcnt) before the next barrier. `lds` is a stage of its own __shared__
 // array, so reads of the other stage need not wait.
 template <typename T, int ROWS, int D, int NT>
-__device__ __forceinline__ void dma_tile(char* lds, const T* __restrict__ src, int64_t stride, int valid,
-                                         int wave, int lane) {
-  using Tile = LdsTile<T, ROWS, D>;
-  constexpr int kInstr = ROWS * Tile::kChunks / 64;
-  constexpr int kPerWave = kInstr / (NT / 64);
-  static_assert(kInstr % (NT / 64) == 0, "tile must split evenly over the waves");
+struct DmaTile {
+  __device__ static __forceinline__ void run(char* lds, const T* __restrict__ src, int64_t stride, int valid,
+                                             int wave, int lane) {
+    using Tile = LdsTile<T, ROWS, D>;
+    constexpr int kInstr = ROWS * Tile::kChunks / 64;
+    constexpr int kPerWave = kInstr / (NT / 64);
+    static_assert(kInstr % (NT / 64) == 0, "tile must split evenly over the waves");
 #pragma unroll
-  for (int e = 0; e < kPerWave; ++e) {
-    const int slot = (wave * kPerWave + e) * 64 + lane;
-    const int row = slot / Tile::kChunks, pc = slot % Tile::kChunks;
-    const int rg = row < valid ? row : valid - 1;
-    const T* g = src + (int64_t)rg * stride + (pc ^ Tile::swz(row)) * Tile::kElemsPerChunk;
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds + (wave * kPerWave + e) * 1024),
-                                     16, 0, 0);
+    for (int e = 0; e < kPerWave; ++e) {
+      const int slot = (wave * kPerWave + e) * 64 + lane;
+      const int row = slot / Tile::kChunks, pc = slot % Tile::kChunks;
+      const int rg = row < valid ? row : valid - 1;
+      const T* g = src + (int64_t)rg * stride + (pc ^ Tile::swz(row)) * Tile::kElemsPerChunk;
+      __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds + (wave * kPerWave + e) * 1024),
+                                       16, 0, 0);
+    }
   }
-}
+};
+
+// dma_tile with the per-lane element offsets computed once: for a full tile
+// each load is one 64-bit add. A ragged tile (valid < ROWS) takes the clamped
+// path of dma_tile.
+template <typename T, int ROWS, int D, int NT>
+struct DmaPlan {
+  using Tile = LdsTile<T, ROWS, D>;
+  static constexpr int kInstr = ROWS * Tile::kChunks / 64;
+  static constexpr int kPerWave = kInstr / (NT / 64);
+  int off[kPerWave];  // element offset of this lane's chunk in each load
+  int wave, lane;
+  __device__ __forceinline__ void init(int64_t stride, int wave_, int lane_) {
+    wave = wave_;
+    lane = lane_;
+#pragma unroll
+    for (int e = 0; e < kPerWave; ++e) {
+      const int slot = (wave * kPerWave + e) * 64 + lane;
+      const int row = slot / Tile::kChunks, pc = slot % Tile::kChunks;
+      off[e] = (int)(row * stride) + (pc ^ Tile::swz(row)) * Tile::kElemsPerChunk;
+    }
+  }
+  __device__ __forceinline__ void issue(char* lds, const T* __restrict__ src, int64_t stride, int valid) const {
+    if (valid >= ROWS) {
+#pragma unroll
+      for (int e = 0; e < kPerWave; ++e)
+        __builtin_amdgcn_global_load_lds(src + off[e],
+            (__attribute__((address_space(3))) void*)(lds + (wave * kPerWave + e) * 1024), 16, 0, 0);
+    } else {
+      DmaTile<T, ROWS, D, NT>::run(lds, src, stride, valid, wave, lane);
+    }
+  }
+};
 
 // Fragment straight from global memory: 8 consecutive elements at p.
 template <typename T> __device__ __forceinline__ Frag<T> global_frag(const T* __restrict__ p) {
@@ -313,6 +347,9 @@ template <typename T> __device__ __forceinline__ Frag<T> zero_frag() {
   }
   return f;
 }
+
+// A wave-uniform value the compiler can keep in a scalar register.
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
