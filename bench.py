@@ -69,6 +69,56 @@ def load_traffic(kernel: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+KERNEL_NAMES = {"fwd_kernel": "fwd", "bwd_delta_kernel": "bwd_delta", "bwd_dq_kernel": "bwd_dq",
+                "bwd_dkdv_kernel": "bwd_dkdv", "bwd_dkdv4_kernel": "bwd_dkdv"}
+
+
+def write_traffic(fetch_csv: str, write_csv: str, copy_mib: int, commands: list) -> dict:
+    """Turn two rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
+    of a run made with --copy-calibration-mib into HBM bytes per launch of each
+    kernel. The counters' scale is taken from the calibration copy, a kernel
+    that reads and writes copy_mib MiB once: factor = known bytes / counted."""
+    import csv
+    import re
+    from collections import defaultdict
+
+    def read(path, counter):
+        out = []
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    out.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
+        return out
+
+    fetch, write = read(fetch_csv, "FETCH_SIZE"), read(write_csv, "WRITE_SIZE")
+    known = copy_mib << 20
+    # the calibration copy: the non-attention dispatch that reads the most (a
+    # fill writes as much but reads nothing), and the same kernel's write
+    cf = max((r for r in fetch if "swa" not in r[0]), key=lambda r: r[2])
+    cw = max((r for r in write if r[0] == cf[0] and r[1] == cf[1]), key=lambda r: r[2])
+    f_fetch, f_write = known / (cf[2] * 1024), known / (cw[2] * 1024)
+
+    def per_kernel(rows, factor):
+        acc = defaultdict(list)
+        for name, _, kib in rows:
+            m = re.search(r"swa\d+(bwd_dkdv4_kernel|bwd_dkdv_kernel|bwd_delta_kernel|bwd_dq_kernel|fwd_kernel)",
+                          name)
+            if m:
+                acc[KERNEL_NAMES[m.group(1)]].append(kib * 1024 * factor)
+        return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+    pf, pw = per_kernel(fetch, f_fetch), per_kernel(write, f_write)
+    kernels = {k: {"fetch_bytes_per_launch": round(pf[k][0]), "write_bytes_per_launch": round(pw[k][0]),
+                   "hbm_bytes_per_launch": round(pf[k][0] + pw[k][0]), "dispatches": pf[k][1]}
+               for k in pf if k in pw}
+    return {"source_hash": source_hash(), "workload": "bf16_n32768_w1024_32q8kv_d128",
+            "commands": commands,
+            "calibration": {"kernel": cw[0], "bytes_read_and_written": known,
+                            "fetch_kib": cf[2], "write_kib": cw[2],
+                            "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)},
+            "kernels": kernels}
+
+
 def cpu_baseline(w, x, rows: int):
     """The fp64 oracle, untuned, on a bounded sample of the same workload:
     query head 0, query rows [0, rows) of each sequence, full forward + backward."""
@@ -96,8 +146,8 @@ def cpu_baseline(w, x, rows: int):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="bf16_n32768_w1024_32q8kv_d128")
     ap.add_argument("--cpu-rows", type=int, default=32768,
                     help="query rows per sequence in the oracle's timing sample")
@@ -106,7 +156,23 @@ def main() -> int:
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (a known-size kernel for "
                          "scaling hardware byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: write the HBM traffic summary from two rocprofv3 --pmc CSVs "
+                         "of a run with --copy-calibration-mib, then exit")
+    ap.add_argument("--traffic-command", action="append", default=[],
+                    help="the rocprofv3 command lines that made the CSVs (recorded in the summary)")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        if args.copy_calibration_mib <= 0:
+            print("--traffic-from needs the --copy-calibration-mib of the profiled run", file=sys.stderr)
+            return 2
+        t = write_traffic(*args.traffic_from, args.copy_calibration_mib, args.traffic_command)
+        with open(TRAFFIC_FILE, "w") as fh:
+            json.dump(t, fh, indent=1)
+            fh.write("\n")
+        print(json.dumps(t["kernels"]))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "

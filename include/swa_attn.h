@@ -73,7 +73,7 @@ typedef enum {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
-  ATTN_ERR_SHAPE = 2,       /* sizes inconsistent (batch < 1, heads_q % heads_kv, heads_q > 65536, totals ...) */
+  ATTN_ERR_SHAPE = 2,       /* sizes inconsistent (batch < 1, heads_q % heads_kv, heads_q > 16384, totals ...) */
   ATTN_ERR_WINDOW = 3,      /* window < 1 */
   ATTN_ERR_UNSUPPORTED = 4, /* head_dim not 64/128, unknown dtype, window without causal, scale <= 0 */
   ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than attn_bwd_workspace_bytes */

@@ -58,8 +58,9 @@ attn_status_t attn_check_params(const attn_params_t* p) {
   // the kernels fold the scale into exp2 arguments and take row maxima on raw
   // scores, which needs a positive scale
   if (!(p->scale > 0.f) || !isfinite(p->scale)) return ATTN_ERR_UNSUPPORTED;
-  // tile offsets (128 rows x heads x head_dim elements) are int32 in the kernels
-  if (p->heads_q > 65536) return ATTN_ERR_SHAPE;
+  // tile loads address a 128-row tile with 32-bit byte offsets (128 rows x
+  // heads x head_dim x 4 bytes < 2^31)
+  if (p->heads_q > 16384) return ATTN_ERR_SHAPE;
   // packed element counts must stay addressable
   if ((int64_t)p->total_q * p->heads_q > INT32_MAX || (int64_t)p->total_k * p->heads_kv > INT32_MAX)
     return ATTN_ERR_SHAPE;

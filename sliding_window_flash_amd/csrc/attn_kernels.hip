@@ -94,12 +94,13 @@ struct TileStage {
 
 // K and V key tile kb of one sequence into an LDS stage (K tile, then V tile).
 template <typename T, int BN, int D, int NT>
-__device__ __forceinline__ void fill_kv(char* st, const T* __restrict__ K, const T* __restrict__ V,
-                                        int64_t kstride, int kb, int lk, int wave, int lane) {
+__device__ __forceinline__ void fill_kv(const TileLoader<T, BN, D, NT>& ld, char* st, const T* K, const T* V,
+                                        int64_t kstride, int kb, int lk) {
   const int kvalid = min(BN, lk - kb * BN);
-  DmaTile<T, BN, D, NT>::run(st, K + (int64_t)kb * BN * kstride, kstride, kvalid, wave, lane);
-  DmaTile<T, BN, D, NT>::run(st + LdsTile<T, BN, D>::kBytes, V + (int64_t)kb * BN * kstride, kstride, kvalid,
-                         wave, lane);
+  const int64_t o = (int64_t)kb * BN * kstride;
+  const uint32_t sb = (uint32_t)(kstride * sizeof(T));
+  ld.issue(st, K + o, sb, kvalid);
+  ld.issue(st + LdsTile<T, BN, D>::kBytes, V + o, sb, kvalid);
 }
 
 struct QueryItem {
@@ -149,7 +150,8 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
   __shared__ __attribute__((aligned(1024))) char st0[2 * KTile::kBytes];
   __shared__ __attribute__((aligned(1024))) char st1[2 * KTile::kBytes];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int w = wave_uniform(tid >> 6);
   const QueryItem it = decode_query_item(a, BM);
   if (it.qb * BM >= it.lq) return;
   const int g = it.h / (a.heads_q / a.heads_kv);
@@ -187,7 +189,9 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
   float m = -INFINITY, lsum = 0.f;
   const float c = a.scale * kLog2e;
 
-  if (kr.lo <= kr.hi) fill_kv<T, BN, D, NT>(st0, K, V, kstride, kr.lo, it.lk, w, lane);
+  TileLoader<T, BN, D, NT> kvld;
+  kvld.init((uint32_t)(kstride * sizeof(T)), w, lane);
+  if (kr.lo <= kr.hi) fill_kv(kvld, st0, K, V, kstride, kr.lo, it.lk);
   __syncthreads();
 
   // One key tile; `stage` (compile time) selects the LDS stage it reads.
@@ -195,7 +199,7 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
     constexpr int stage = decltype(stage_c)::value;
     const char* ks = stage ? st1 : st0;
     const char* vs = ks + KTile::kBytes;
-    if (kb < kr.hi) fill_kv<T, BN, D, NT>(stage ? st0 : st1, K, V, kstride, kb + 1, it.lk, w, lane);
+    if (kb < kr.hi) fill_kv(kvld, stage ? st0 : st1, K, V, kstride, kb + 1, it.lk);
     f32x16 s[BN / 32];
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt) {
@@ -299,7 +303,8 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
   __shared__ __attribute__((aligned(1024))) char st0[2 * KTile::kBytes];
   __shared__ __attribute__((aligned(1024))) char st1[2 * KTile::kBytes];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int w = wave_uniform(tid >> 6);
   const QueryItem it = decode_query_item(a, BM);
   if (it.qb * BM >= it.lq) return;
   const int g = it.h / (a.heads_q / a.heads_kv);
@@ -341,14 +346,16 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
   const float c = a.scale * kLog2e;
 
-  if (kr.lo <= kr.hi) fill_kv<T, BN, D, NT>(st0, K, V, kstride, kr.lo, it.lk, w, lane);
+  TileLoader<T, BN, D, NT> kvld;
+  kvld.init((uint32_t)(kstride * sizeof(T)), w, lane);
+  if (kr.lo <= kr.hi) fill_kv(kvld, st0, K, V, kstride, kr.lo, it.lk);
   __syncthreads();
 
   auto step = [&](auto stage_c, int kb) {
     constexpr int stage = decltype(stage_c)::value;
     const char* ks = stage ? st1 : st0;
     const char* vs = ks + KTile::kBytes;
-    if (kb < kr.hi) fill_kv<T, BN, D, NT>(stage ? st0 : st1, K, V, kstride, kb + 1, it.lk, w, lane);
+    if (kb < kr.hi) fill_kv(kvld, stage ? st0 : st1, K, V, kstride, kb + 1, it.lk);
     const bool edge = !(kr.full_lo <= kb && kb <= kr.full_hi);
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt) {
@@ -438,8 +445,11 @@ bwd_dkdv_kernel(AttnArgs a) {
   {
     const int kvalid = min(BN, lk - kb * BN);
     const int64_t koff = (int64_t)(k0 + kb * BN) * kstride + g * D;
-    DmaTile<T, BN, D, NT>::run(klds, static_cast<const T*>(a.k) + koff, kstride, kvalid, w, lane);
-    DmaTile<T, BN, D, NT>::run(vlds, static_cast<const T*>(a.v) + koff, kstride, kvalid, w, lane);
+    const uint32_t sb = (uint32_t)(kstride * sizeof(T));
+    TileLoader<T, BN, D, NT> kvld;
+    kvld.init(sb, w, lane);
+    kvld.issue(klds, static_cast<const T*>(a.k) + koff, sb, kvalid);
+    kvld.issue(vlds, static_cast<const T*>(a.v) + koff, sb, kvalid);
   }
   RowReader<T, D> rrd;
   rrd.init(l32, half);
@@ -462,20 +472,20 @@ bwd_dkdv_kernel(AttnArgs a) {
   const int nq = qr.hi >= qr.lo ? qr.hi - qr.lo + 1 : 0;
   const int steps = grp * nq;
   int nh = g * grp, nqb = qr.lo;  // (head, query tile) of the next step to fill
-  DmaPlan<T, BM, D, NT> qplan;
-  qplan.init(qstride, w, lane);
-  // Query rows past L_q in a tile hold copies of row L_q - 1; they are masked.
+  const uint32_t qsb = (uint32_t)(qstride * sizeof(T));
+  TileLoader<T, BM, D, NT> qld;
+  qld.init(qsb, w, lane);
+  // Query rows past L_q in a tile arrive as zeros (LSE*log2e and D too); they are masked.
   auto fill = [&](char* st) {
     const int qvalid = min(BM, lq - nqb * BM);
     const int64_t qoff = (int64_t)(q0 + nqb * BM) * qstride + nh * D;
-    qplan.issue(st, Qg + qoff, qstride, qvalid);
-    qplan.issue(st + QTile::kBytes, Dg + qoff, qstride, qvalid);
+    qld.issue(st, Qg + qoff, qsb, qvalid);
+    qld.issue(st + QTile::kBytes, Dg + qoff, qsb, qvalid);
     if (w == 0) {
-      const int64_t idx = (int64_t)nh * a.total_q + q0 + nqb * BM + min(lane, qvalid - 1);
-      __builtin_amdgcn_global_load_lds(a.lse2 + idx,
-          (__attribute__((address_space(3))) void*)(st + 2 * QTile::kBytes), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds(a.delta + idx,
-          (__attribute__((address_space(3))) void*)(st + 2 * QTile::kBytes + BM * 4), 4, 0, 0);
+      const int64_t idx = (int64_t)nh * a.total_q + q0 + nqb * BM;
+      buffer_to_lds4(buffer_rsrc(a.lse2 + idx, (uint32_t)qvalid * 4u), st + 2 * QTile::kBytes, (uint32_t)lane * 4u);
+      buffer_to_lds4(buffer_rsrc(a.delta + idx, (uint32_t)qvalid * 4u), st + 2 * QTile::kBytes + BM * 4,
+                       (uint32_t)lane * 4u);
     }
     if (++nqb > qr.hi) {
       nqb = qr.lo;
@@ -508,7 +518,7 @@ bwd_dkdv_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int off = 8 * (r >> 2) + (r & 3);
-        if (ib + off >= lq || (causal && (uint32_t)(mb + off) >= wlim)) s[r] = -INFINITY;
+        if ((ib + off >= lq) | (causal & ((uint32_t)(mb + off) >= wlim))) s[r] = -INFINITY;
       }
     }
 #pragma unroll

@@ -259,63 +259,58 @@ struct ColReader {
   }
 };
 
-// Direct global -> LDS copy of a ROWS x D tile into the swizzled layout
-// (global_load_lds_dwordx4: each wave instruction writes 64 consecutive
-// 16-byte LDS slots; the lane of physical slot (row, pc) fetches logical chunk
-// pc ^ swz(row) of that row). Rows >= valid re-read row valid - 1, so every
-// address stays inside the tensor; callers mask those rows. No registers hold
-// the data: it lands in LDS asynchronously, and the compiler waits for it
-// (vmcnt) before the next barrier. `lds` is a stage of its own __shared__
-// array, so reads of the other stage need not wait.
-template <typename T, int ROWS, int D, int NT>
-struct DmaTile {
-  __device__ static __forceinline__ void run(char* lds, const T* __restrict__ src, int64_t stride, int valid,
-                                             int wave, int lane) {
-    using Tile = LdsTile<T, ROWS, D>;
-    constexpr int kInstr = ROWS * Tile::kChunks / 64;
-    constexpr int kPerWave = kInstr / (NT / 64);
-    static_assert(kInstr % (NT / 64) == 0, "tile must split evenly over the waves");
-#pragma unroll
-    for (int e = 0; e < kPerWave; ++e) {
-      const int slot = (wave * kPerWave + e) * 64 + lane;
-      const int row = slot / Tile::kChunks, pc = slot % Tile::kChunks;
-      const int rg = row < valid ? row : valid - 1;
-      const T* g = src + (int64_t)rg * stride + (pc ^ Tile::swz(row)) * Tile::kElemsPerChunk;
-      __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds + (wave * kPerWave + e) * 1024),
-                                       16, 0, 0);
-    }
-  }
-};
+// Raw buffer resource over [base, base + bytes): loads through it are
+// range-checked on their byte offset, so an offset at or past `bytes` returns
+// zero and touches no memory. Word 3 is the gfx9 raw-buffer format word
+// (32-bit data format, no swizzle, no stride).
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
 
-// dma_tile with the per-lane element offsets computed once: for a full tile
-// each load is one 64-bit add. A ragged tile (valid < ROWS) takes the clamped
-// path of dma_tile.
+// One buffer load per lane into LDS, 16 or 4 bytes: lane l's data lands at
+// lds + l * bytes (lds wave-uniform).
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t rsrc, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
+}
+
+// Direct global -> LDS copy of a ROWS x D tile into the swizzled layout
+// (buffer_load_dwordx4 ... lds: each wave instruction writes 64 consecutive
+// 16-byte LDS slots; the lane of physical slot (row, pc) fetches logical chunk
+// pc ^ swz(row) of that row). The per-lane byte offsets are fixed for a
+// kernel, so a tile costs one descriptor and kPerWave loads per wave. Rows at
+// or past `valid` lie outside the descriptor's range and arrive as zeros; no
+// address outside the sequence's rows is read. No registers hold the data: it
+// lands in LDS asynchronously, and the compiler waits for it (vmcnt) before
+// the next barrier. Buffer loads, unlike the flat-segment global_load_lds,
+// leave the compiler's LDS read counting exact, so reads can run ahead of the
+// MFMAs that consume them.
 template <typename T, int ROWS, int D, int NT>
-struct DmaPlan {
+struct TileLoader {
   using Tile = LdsTile<T, ROWS, D>;
   static constexpr int kInstr = ROWS * Tile::kChunks / 64;
   static constexpr int kPerWave = kInstr / (NT / 64);
-  int off[kPerWave];  // element offset of this lane's chunk in each load
-  int wave, lane;
-  __device__ __forceinline__ void init(int64_t stride, int wave_, int lane_) {
-    wave = wave_;
-    lane = lane_;
+  static_assert(kInstr % (NT / 64) == 0, "tile must split evenly over the waves");
+  uint32_t off[kPerWave];  // byte offset of this lane's chunk from the tile's first row
+  int lds0;                // byte offset of this wave's first LDS slot (wave-uniform)
+  // stride_bytes: bytes between consecutive rows; ROWS * stride_bytes < 2^31
+  __device__ __forceinline__ void init(uint32_t stride_bytes, int wave, int lane) {
+    lds0 = wave * kPerWave * 1024;
 #pragma unroll
     for (int e = 0; e < kPerWave; ++e) {
       const int slot = (wave * kPerWave + e) * 64 + lane;
       const int row = slot / Tile::kChunks, pc = slot % Tile::kChunks;
-      off[e] = (int)(row * stride) + (pc ^ Tile::swz(row)) * Tile::kElemsPerChunk;
+      off[e] = (uint32_t)row * stride_bytes + (uint32_t)(pc ^ Tile::swz(row)) * 16u;
     }
   }
-  __device__ __forceinline__ void issue(char* lds, const T* __restrict__ src, int64_t stride, int valid) const {
-    if (valid >= ROWS) {
+  // src: first element of the tile's first row; valid in [1, ROWS] rows exist
+  __device__ __forceinline__ void issue(char* lds, const T* src, uint32_t stride_bytes, int valid) const {
+    const __amdgpu_buffer_rsrc_t rsrc = buffer_rsrc(src, (uint32_t)valid * stride_bytes);
 #pragma unroll
-      for (int e = 0; e < kPerWave; ++e)
-        __builtin_amdgcn_global_load_lds(src + off[e],
-            (__attribute__((address_space(3))) void*)(lds + (wave * kPerWave + e) * 1024), 16, 0, 0);
-    } else {
-      DmaTile<T, ROWS, D, NT>::run(lds, src, stride, valid, wave, lane);
-    }
+    for (int e = 0; e < kPerWave; ++e) buffer_to_lds16(rsrc, lds + lds0 + e * 1024, off[e]);
   }
 };
 

@@ -54,6 +54,8 @@ def good(**kw):
     (dict(scale=-0.1), 4),
     (dict(scale=float("inf")), 4),
     (dict(scale=float("nan")), 4),
+    (dict(heads_q=16384, heads_kv=16384), 0),
+    (dict(heads_q=16386, heads_kv=2), 2),
 ])
 def test_parameter_checks(kw, code):
     assert swa.check_params(good(**kw)) == code
