@@ -220,7 +220,7 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
     for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx = fmaxf(mx, xor32(mx));
+    mx = max_halves(mx);
     const float mxs = mx == -INFINITY ? -INFINITY : mx * c;
     const bool grow = mxs > m + kRescaleSlack;
     if (__any(grow)) {
@@ -239,15 +239,18 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
       for (int r = 0; r < 16; ++r) {
         const float pv = fast_exp2(fmaf(s[kt][r], c, -mu));
         s[kt][r] = pv;
-        rs += pv;
+        if constexpr (sizeof(T) == 4) rs += pv;
       }
-    lsum += rs;
+    // bf16: the row sum is taken over the rounded P that the MFMA multiplies,
+    // so O's weights sum to exactly the normaliser
 #pragma unroll
     for (int u = 0; u < BN / 16; ++u) {
       const Frag<T> pf = acc_frag<T>(s[u >> 1], u & 1);
+      if constexpr (sizeof(T) == 2) rs = frag_sum(pf, rs);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) mma(acc[dt], crd.read(vs, 16 * u, dt), pf);
     }
+    lsum += rs;
     __syncthreads();
   };
   for (int kb = kr.lo; kb <= kr.hi;) {
@@ -257,7 +260,7 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
     ++kb;
   }
 
-  const float ltot = lsum + xor32(lsum);
+  const float ltot = sum_halves(lsum);
   if (row_ok) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     T* orow = static_cast<T*>(a.out_o) + (int64_t)(it.q0 + i) * qstride + it.h * D;

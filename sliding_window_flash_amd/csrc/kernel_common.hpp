@@ -349,7 +349,31 @@ __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_rea
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Sum of the 8 bf16 values of a fragment added to `acc` (four v_dot2 against
+// (1, 1); products by one are exact, the sum is accumulated in fp32).
+__device__ __forceinline__ float frag_sum(const Frag<bf16>& f, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.v, f.v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.v, f.v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.v, f.v, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.v, f.v, 6, 7), one, acc, false);
+}
+
+// Reductions over lanes l and l ^ 32 (the two halves of a wave hold the two
+// 8-row halves of each score column), left in every lane. One
+// v_permlane32_swap with both operands x yields, in every lane, the lower
+// half's value (first result) and the upper half's (second result), so no LDS
+// round trip is needed.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return a > b ? a : b;
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Kernel argument block shared by all launches.
 struct AttnArgs {
