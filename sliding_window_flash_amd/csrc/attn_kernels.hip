@@ -200,6 +200,13 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
     const char* ks = stage ? st1 : st0;
     const char* vs = ks + KTile::kBytes;
     if (kb < kr.hi) fill_kv(kvld, stage ? st0 : st1, K, V, kstride, kb + 1, it.lk);
+    // an edge tile whose cells are all masked for this wave's 32 rows adds
+    // nothing (P = 0): the wave skips it but still loads its share and syncs
+    const bool edge = !(kr.full_lo <= kb && kb <= kr.full_hi);
+    if (edge && block_masked(it.lq, it.lk, a.window, a.causal != 0, it.qb * BM + 32 * w, 32, kb * BN, BN)) {
+      __syncthreads();
+      return;
+    }
     f32x16 s[BN / 32];
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt) {
@@ -207,7 +214,7 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
       for (int ss = 0; ss < D / 16; ++ss) mma(s[kt], rrd.read(ks, 32 * kt, ss), qf[ss]);
     }
-    if (!(kr.full_lo <= kb && kb <= kr.full_hi)) {
+    if (edge) {
       const int mb = mpos - (kb * BN + 4 * half);
 #pragma unroll
       for (int kt = 0; kt < BN / 32; ++kt)
@@ -360,6 +367,11 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
     const char* vs = ks + KTile::kBytes;
     if (kb < kr.hi) fill_kv(kvld, stage ? st0 : st1, K, V, kstride, kb + 1, it.lk);
     const bool edge = !(kr.full_lo <= kb && kb <= kr.full_hi);
+    // all cells masked for this wave's 32 rows: dS = 0, nothing to add
+    if (edge && block_masked(it.lq, it.lk, a.window, a.causal != 0, it.qb * BM + 32 * w, 32, kb * BN, BN)) {
+      __syncthreads();
+      return;
+    }
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt) {
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -507,6 +519,12 @@ bwd_dkdv_kernel(AttnArgs a) {
     const float* dlts = lse2s + BM;
     if (t + 1 < steps) fill(stage ? st0 : st1);
     const bool edge = !tile_full_i32(lq, lk, a.window, causal, qb, BM, kb, BN);
+    // this wave's 32 keys x 32 queries all masked: P = dS = 0, nothing to add
+    if (edge && block_masked(lq, lk, a.window, causal, qb * BM + 32 * mh, 32, kb * BN + 32 * kt, 32)) {
+      if (++qb > qr.hi) qb = qr.lo;
+      __syncthreads();
+      return;
+    }
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ss = 0; ss < D / 16; ++ss) {

@@ -140,6 +140,22 @@ SWA_HD bool tile_full_i32(int32_t lq, int32_t lk, int32_t window, bool causal, i
   return j0 + bn - 1 <= i0 + delta && (i0 + bm - 1 + delta) - j0 < window;
 }
 
+// Is every cell of the block (queries [a, a + rows), keys [b, b + cols)) of one
+// sequence masked? Then the block contributes nothing (P = 0, dS = 0) and a
+// wave may skip it. Causal: the block's first key lies after its last query's
+// position, or its last key lies at or beyond the window of its first query.
+// Rows past L_q and keys past L_k are masked. int64 arithmetic: window may be
+// INT32_MAX.
+SWA_HD bool block_masked(int32_t lq, int32_t lk, int32_t window, bool causal, int32_t a, int32_t rows,
+                         int32_t b, int32_t cols) {
+  if (a >= lq || b >= lk) return true;
+  if (!causal) return false;
+  const int64_t delta = (int64_t)lk - lq;
+  const int64_t p_last = (int64_t)(a + rows - 1 < lq - 1 ? a + rows - 1 : lq - 1) + delta;
+  const int64_t p_first = (int64_t)a + delta;
+  return (int64_t)b > p_last || p_first - ((int64_t)b + cols - 1) >= (int64_t)window;
+}
+
 // Is tile (query tile qb, key tile kb) free of masked cells?
 SWA_HD bool tile_is_full(const SeqGeom& s, int32_t qb, int32_t bm, int32_t kb, int32_t bn) {
   const TileRange r = query_tile_keys(s, qb, bm, bn);

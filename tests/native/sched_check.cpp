@@ -31,6 +31,34 @@ int main() {
                   }
                 }
         }
+  // block_masked against cell-by-cell enumeration (the kernels' per-wave skip)
+  long bchecked = 0, bbad = 0;
+  for (int lq = 1; lq <= 140; lq += 9)
+    for (int dl = 0; dl <= 70; dl += 35)
+      for (int w : wins)
+        for (int causal = 0; causal <= 1; ++causal) {
+          const int lk = lq + dl;
+          if (!causal && w < lk) continue;
+          const swa::SeqGeom g{lq, lk, w, causal != 0};
+          for (int rows : {32})
+            for (int cols : {32, 64})
+              for (int a = 0; a < lq + rows; a += 16)
+                for (int b = 0; b < lk + cols; b += 16) {
+                  bool any = false;
+                  for (int i = a; i < a + rows && !any; ++i)
+                    for (int j = b; j < b + cols && !any; ++j) any = swa::cell_visible(g, i, j);
+                  const bool m = swa::block_masked(lq, lk, w, causal != 0, a, rows, b, cols);
+                  ++bchecked;
+                  if (m == any) {
+                    if (bbad < 5)
+                      printf("block mismatch lq=%d lk=%d w=%d causal=%d a=%d b=%d rows=%d cols=%d: masked=%d visible=%d\n",
+                             lq, lk, w, causal, a, b, rows, cols, m, any);
+                    ++bbad;
+                  }
+                }
+        }
+  printf("blocks checked %ld, mismatches %ld\n", bchecked, bbad);
+  bad += bbad;
   printf("checked %ld, mismatches %ld\n", checked, bad);
   return bad != 0;
 }
