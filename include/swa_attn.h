@@ -67,7 +67,8 @@ extern "C" {
 
 typedef enum {
   ATTN_F32 = 0,  /* Q, K, V, O, dO, dQ, dK, dV are float32 */
-  ATTN_BF16 = 1  /* ... are bfloat16; accumulation and score tiles stay fp32 */
+  ATTN_BF16 = 1, /* ... are bfloat16; accumulation and score tiles stay fp32 */
+  ATTN_F16 = 2   /* ... are IEEE half; accumulation and score tiles stay fp32 */
 } attn_dtype_t;
 
 typedef enum {

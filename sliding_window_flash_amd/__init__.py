@@ -15,7 +15,7 @@ from typing import Optional, Tuple
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libswa_attn.so")
 
-ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
 INT32_MAX = 2**31 - 1
 
 STATUS = {
@@ -158,7 +158,7 @@ def _stream_ptr(stream) -> int:
 def params_for(q, k, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=INT32_MAX, causal=True,
                scale=None) -> AttnParams:
     torch = _torch()
-    dt = {torch.bfloat16: ATTN_BF16, torch.float32: ATTN_F32}.get(q.dtype)
+    dt = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16, torch.float32: ATTN_F32}.get(q.dtype)
     if dt is None:
         raise AttnError(4, f"dtype {q.dtype}")
     return make_params(batch=cu_q.numel() - 1, heads_q=q.shape[1], heads_kv=k.shape[1],

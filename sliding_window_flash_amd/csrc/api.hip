@@ -52,7 +52,7 @@ attn_status_t attn_check_params(const attn_params_t* p) {
     return ATTN_ERR_SHAPE;
   if (p->window < 1) return ATTN_ERR_WINDOW;
   if (p->head_dim != 64 && p->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
-  if (p->dtype != ATTN_F32 && p->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (p->dtype != ATTN_F32 && p->dtype != ATTN_BF16 && p->dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
   if (p->causal != 0 && p->causal != 1) return ATTN_ERR_UNSUPPORTED;
   if (p->causal == 0 && p->window < p->max_seqlen_k) return ATTN_ERR_UNSUPPORTED;
   // the kernels fold the scale into exp2 arguments and take row maxima on raw

@@ -37,12 +37,17 @@
 
 namespace swa {
 
-// Store 4 consecutive fp32 values as T (8 bytes for bf16, 16 for fp32).
+// Store 4 consecutive fp32 values as T (8 bytes for bf16 and fp16, 16 for fp32).
 template <typename T> __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
 template <> __device__ __forceinline__ void store4<bf16>(bf16* p, float a, float b, float c, float d) {
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
   *reinterpret_cast<bf16x4*>(p) = v;
+}
+template <> __device__ __forceinline__ void store4<fp16>(fp16* p, float a, float b, float c, float d) {
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  f16x4 v = {(fp16)a, (fp16)b, (fp16)c, (fp16)d};
+  *reinterpret_cast<f16x4*>(p) = v;
 }
 template <> __device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
   f32x4 v = {a, b, c, d};
@@ -808,6 +813,8 @@ static hipError_t launch_bwd_t(int stages, const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_fwd(int dtype, int head_dim, const AttnArgs& a, hipStream_t st) {
+  if (dtype == 2 && head_dim == 128) return launch_fwd_t<fp16, 128>(a, st);
+  if (dtype == 2 && head_dim == 64) return launch_fwd_t<fp16, 64>(a, st);
   if (dtype == 1 && head_dim == 128) return launch_fwd_t<bf16, 128>(a, st);
   if (dtype == 1 && head_dim == 64) return launch_fwd_t<bf16, 64>(a, st);
   if (dtype == 0 && head_dim == 128) return launch_fwd_t<float, 128>(a, st);
@@ -816,6 +823,8 @@ hipError_t launch_fwd(int dtype, int head_dim, const AttnArgs& a, hipStream_t st
 }
 
 hipError_t launch_bwd(int dtype, int head_dim, int stages, const AttnArgs& a, hipStream_t st) {
+  if (dtype == 2 && head_dim == 128) return launch_bwd_t<fp16, 128>(stages, a, st);
+  if (dtype == 2 && head_dim == 64) return launch_bwd_t<fp16, 64>(stages, a, st);
   if (dtype == 1 && head_dim == 128) return launch_bwd_t<bf16, 128>(stages, a, st);
   if (dtype == 1 && head_dim == 64) return launch_bwd_t<bf16, 64>(stages, a, st);
   if (dtype == 0 && head_dim == 128) return launch_bwd_t<float, 128>(stages, a, st);
@@ -824,7 +833,7 @@ hipError_t launch_bwd(int dtype, int head_dim, int stages, const AttnArgs& a, hi
 }
 
 bool tile_sizes(int dtype, int head_dim, int* fwd_bm, int* fwd_bn, int* bwd_bn, int* bwd_bm) {
-  if ((dtype != 0 && dtype != 1) || (head_dim != 64 && head_dim != 128)) return false;
+  if ((dtype != 0 && dtype != 1 && dtype != 2) || (head_dim != 64 && head_dim != 128)) return false;
   *fwd_bm = Tiles::kFwdBM;
   *fwd_bn = Tiles::kFwdBN;
   *bwd_bn = Tiles::kBwdBN;

@@ -1,8 +1,9 @@
 // Shared device building blocks for the gfx950 attention kernels.
 //
-// MFMA: every contraction uses the 32x32 result tile. bf16 operands use
-// v_mfma_f32_32x32x16_bf16 (one instruction per 16-deep step); fp32 operands
-// use eight v_mfma_f32_32x32x2_f32 (true fp32, no reduced-precision mode).
+// MFMA: every contraction uses the 32x32 result tile. bf16 and fp16 operands
+// use v_mfma_f32_32x32x16_{bf16,f16} (one instruction per 16-deep step, the
+// same lane layout); fp32 operands use eight v_mfma_f32_32x32x2_f32 (true
+// fp32, no reduced-precision mode).
 //
 // Lane layouts (64 lanes; l32 = lane % 32, half = lane / 32):
 //   A operand (M x 16): lane holds row l32, 8 contraction elements
@@ -28,6 +29,8 @@ namespace swa {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 fp16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -39,10 +42,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 // ---- operand fragments -------------------------------------------------
 template <typename T> struct Frag;
 template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<fp16> { f16x8 v; };
 template <> struct Frag<float> { float v[8]; };
 
 __device__ __forceinline__ void mma(f32x16& c, const Frag<bf16>& a, const Frag<bf16>& b) {
   c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16& c, const Frag<fp16>& a, const Frag<fp16>& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a.v, b.v, c, 0, 0, 0);
 }
 __device__ __forceinline__ void mma(f32x16& c, const Frag<float>& a, const Frag<float>& b) {
 #pragma unroll
@@ -57,6 +64,12 @@ template <> __device__ __forceinline__ Frag<bf16> acc_frag<bf16>(const f32x16& c
   for (int j = 0; j < 8; ++j) f.v[j] = (bf16)c[8 * u + j];  // round to nearest even
   return f;
 }
+template <> __device__ __forceinline__ Frag<fp16> acc_frag<fp16>(const f32x16& c, int u) {
+  Frag<fp16> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.v[j] = (fp16)c[8 * u + j];  // round to nearest even
+  return f;
+}
 template <> __device__ __forceinline__ Frag<float> acc_frag<float>(const f32x16& c, int u) {
   Frag<float> f;
 #pragma unroll
@@ -69,9 +82,11 @@ __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 
 
 // ---- element conversion ---------------------------------------------------
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(fp16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ fp16 from_f32<fp16>(float x) { return (fp16)x; }
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 
 // ---- swizzled LDS tile ------------------------------------------------------
@@ -123,7 +138,7 @@ __device__ __forceinline__ Frag<T> row_frag(const char* lds, int row, int k8) {
   Frag<T> f;
   if constexpr (sizeof(T) == 2) {
     const u32x4 raw = *reinterpret_cast<const u32x4*>(lds + Tile::chunk_off(row, k8));
-    f.v = __builtin_bit_cast(bf16x8, raw);
+    f.v = __builtin_bit_cast(decltype(f.v), raw);
   } else {
     // float vectors, not bit casts of u32x4 elements: the latter is folded to
     // element 0 by this compiler.
@@ -167,7 +182,7 @@ __device__ __forceinline__ Frag<T> col_frag(const char* lds, int kbase, int nbas
     }
     short s8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) f.v[j] = __builtin_bit_cast(bf16, s8[j]);
+    for (int j = 0; j < 8; ++j) f.v[j] = __builtin_bit_cast(T, s8[j]);
   } else {
     const int n = nbase + (lane & 31);
 #pragma unroll
@@ -202,7 +217,7 @@ struct RowReader {
     Frag<T> f;
     if constexpr (sizeof(T) == 2) {
       const u32x4 raw = *reinterpret_cast<const u32x4*>(p + off[ss][0]);
-      f.v = __builtin_bit_cast(bf16x8, raw);
+      f.v = __builtin_bit_cast(decltype(f.v), raw);
     } else {
       const f32x4 a = *reinterpret_cast<const f32x4*>(p + off[ss][0]);
       const f32x4 b = *reinterpret_cast<const f32x4*>(p + off[ss][1]);
@@ -250,7 +265,7 @@ struct ColReader {
           (__attribute__((address_space(3))) i16x4*)(p + off[dt][1]));
       short s8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) f.v[j] = __builtin_bit_cast(bf16, s8[j]);
+      for (int j = 0; j < 8; ++j) f.v[j] = __builtin_bit_cast(T, s8[j]);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) f.v[j] = *reinterpret_cast<const float*>(p + off[dt][j]);
@@ -319,7 +334,7 @@ template <typename T> __device__ __forceinline__ Frag<T> global_frag(const T* __
   Frag<T> f;
   if constexpr (sizeof(T) == 2) {
     const u32x4 raw = *reinterpret_cast<const u32x4*>(p);
-    f.v = __builtin_bit_cast(bf16x8, raw);
+    f.v = __builtin_bit_cast(decltype(f.v), raw);
   } else {
     const f32x4 a = *reinterpret_cast<const f32x4*>(p);
     const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
@@ -335,7 +350,7 @@ template <typename T> __device__ __forceinline__ Frag<T> zero_frag() {
   Frag<T> f;
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) f.v[j] = (bf16)0.0f;
+    for (int j = 0; j < 8; ++j) f.v[j] = (T)0.0f;
   } else {
 #pragma unroll
     for (int j = 0; j < 8; ++j) f.v[j] = 0.0f;
@@ -349,8 +364,16 @@ __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_rea
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Sum of the 8 bf16 values of a fragment added to `acc` (four v_dot2 against
-// (1, 1); products by one are exact, the sum is accumulated in fp32).
+// Sum of the 8 values of a 16-bit fragment added to `acc` (four v_dot2
+// against (1, 1); products by one are exact, the sum is accumulated in fp32).
+__device__ __forceinline__ float frag_sum(const Frag<fp16>& f, float acc) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 one = {(fp16)1.0f, (fp16)1.0f};
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f.v, f.v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f.v, f.v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f.v, f.v, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2(__builtin_shufflevector(f.v, f.v, 6, 7), one, acc, false);
+}
 __device__ __forceinline__ float frag_sum(const Frag<bf16>& f, float acc) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};

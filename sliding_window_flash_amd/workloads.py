@@ -50,7 +50,7 @@ class Workload:
     head_dim: int
     window: int               # >= 1; INT32_MAX or >= every key length means none
     causal: bool
-    dtype: str                # "f32" or "bf16"
+    dtype: str                # "f32", "bf16" or "fp16"
     scale: float
     do_scale: float
     seed: int
@@ -123,16 +123,18 @@ WORKLOADS = {w.name: w for w in (TINY_F32, GQA_2K, CAUSAL_8K, SWA_32K, VARLEN_4)
 VARLEN_SWEEP_WINDOWS = (1, 127, 128, 129, max(VARLEN_4.lengths_k))
 
 
-def _round_bf16(x: np.ndarray) -> np.ndarray:
-    import torch  # plumbing only: torch's fp32 -> bf16 cast rounds to nearest even
+def _round_16(x: np.ndarray, dtype: str) -> np.ndarray:
+    import torch  # plumbing only: torch's fp32 -> bf16 / fp16 casts round to nearest even
 
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    return t.to(torch.bfloat16).to(torch.float32).numpy()
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    return t.to(dt).to(torch.float32).numpy()
 
 
 def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
-    """Draw Q, K, V, dO for workload ``w`` (fp32 arrays; bf16-representable
-    values when ``w.dtype == 'bf16'``) plus the int32 cumulative offsets.
+    """Draw Q, K, V, dO for workload ``w`` (fp32 arrays; bf16- or
+    fp16-representable values for those dtypes) plus the int32 cumulative
+    offsets.
 
     The ragged length draw (step 1) is made by :func:`varlen_workload`, with the
     same generator state the tensors then continue from, so that a ragged
@@ -150,8 +152,8 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
     do = rng.standard_normal((tq, hq, d), dtype=np.float32)
     if w.do_scale != 1.0:
         do *= np.float32(w.do_scale)
-    if w.dtype == "bf16":
-        q, k, v, do = (_round_bf16(a) for a in (q, k, v, do))
+    if w.dtype in ("bf16", "fp16"):
+        q, k, v, do = (_round_16(a, w.dtype) for a in (q, k, v, do))
     return dict(q=q, k=k, v=v, do=do, cu_q=w.cu_seqlens_q(), cu_k=w.cu_seqlens_k())
 
 

@@ -50,6 +50,8 @@ def good(**kw):
     (dict(causal=False, window=100), 0),
     (dict(window=swa.INT32_MAX), 0),
     (dict(dtype=swa.ATTN_F32, head_dim=64), 0),
+    (dict(dtype=swa.ATTN_F16), 0),
+    (dict(dtype=3), 4),
     (dict(scale=0.0), 4),
     (dict(scale=-0.1), 4),
     (dict(scale=float("inf")), 4),
@@ -103,5 +105,6 @@ def test_backward_refuses_before_launch():
 def test_tile_sizes():
     bm, bn, kbn, kbm = swa.tile_sizes(128, swa.ATTN_BF16)
     assert bm % 32 == 0 and bn % 32 == 0 and kbn % 32 == 0 and kbm % 32 == 0
+    assert swa.tile_sizes(128, swa.ATTN_F16) == (bm, bn, kbn, kbm)
     with pytest.raises(swa.AttnError):
         swa.tile_sizes(96, swa.ATTN_BF16)

@@ -54,6 +54,9 @@ SMALL = [
     ([200, 333], None, 4, 2, 128, INT32_MAX, False, "bf16"),  # full (non-causal)
     ([257], None, 2, 2, 128, 1000, True, "f32"),
     ([190, 70], None, 6, 3, 64, 50, True, "bf16"),
+    ([300, 1, 517, 64], None, 8, 2, 128, 129, True, "fp16"),  # fp16: ragged, windowed
+    ([100, 40], [700, 300], 4, 1, 64, 16, True, "fp16"),
+    ([200, 333], None, 4, 2, 128, INT32_MAX, False, "fp16"),
 ]
 
 
@@ -61,23 +64,24 @@ SMALL = [
 def test_small_cases_full_oracle(case):
     lq, lk, hq, hkv, d, win, causal, dt = case
     w = small_case(lq, lk, heads_q=hq, heads_kv=hkv, head_dim=d, window=win, causal=causal,
-                   dtype=dt, do_scale=0.1 if dt == "bf16" else 1.0, seed=zlib.crc32(repr(case).encode()) % 1000)
+                   dtype=dt, do_scale=1.0 if dt == "f32" else 0.1, seed=zlib.crc32(repr(case).encode()) % 1000)
     _run_full(w)
 
 
-@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("fp16", 64), ("f32", 64)])
 def test_window_one_closed_form(dt, d):
     w = small_case([300, 130], [300, 200], heads_q=4, heads_kv=2, head_dim=d, window=1, dtype=dt,
                    do_scale=0.1, seed=31)
     x, dev, got = _run_full(w, zero=("dq", "dk"))
-    # each query sees only its own key: O = V. In bf16 exactly; in fp32 within
-    # an ulp (P = 2^(s*c - m) with m the rounded s*c is 1 only up to rounding).
+    # each query sees only its own key: O = V. In bf16 and fp16 exactly (P
+    # rounds to 1 and the normaliser sums the rounded P); in fp32 within an ulp
+    # (P = 2^(s*c - m) with m the rounded s*c is 1 only up to rounding).
     o = H.host64(got["o"])
     for b in range(w.batch):
         q0, k0 = int(x["cu_q"][b]), int(x["cu_k"][b])
         lq, lk = w.lengths_q[b], w.lengths_k[b]
         kv = np.repeat(x["v"][k0 + lk - lq:k0 + lk], 2, axis=1).astype(np.float64)
-        if dt == "bf16":
+        if dt in ("bf16", "fp16"):
             assert np.array_equal(o[q0:q0 + lq], kv)
         else:
             assert np.all(np.abs(o[q0:q0 + lq] - kv) <= 1e-6 * np.maximum(1.0, np.abs(kv)))
