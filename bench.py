@@ -153,6 +153,9 @@ def main() -> int:
                     help="query rows per sequence in the oracle's timing sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-memory-sweep", action="store_true")
+    ap.add_argument("--no-gemma", action="store_true",
+                    help="skip the head_dim-256 memory-probe shape (timing and peak-bytes sweep)")
+    ap.add_argument("--gemma-steps", type=int, default=10)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (a known-size kernel for "
                          "scaling hardware byte counters)")
@@ -271,24 +274,31 @@ def main() -> int:
     roofline["kernel"] = dom
     roofline["traffic"] = traffic
 
+    # synthetic device inputs of a workload (N(0,1); dO scaled like the workloads)
+    def device_inputs(wl):
+        g = torch.Generator(device=dev).manual_seed(0)
+        t = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        dh = wl.head_dim
+        qq = torch.randn((wl.total_q, wl.heads_q, dh), generator=g, device=dev).to(t)
+        kk = torch.randn((wl.total_k, wl.heads_kv, dh), generator=g, device=dev).to(t)
+        vv = torch.randn((wl.total_k, wl.heads_kv, dh), generator=g, device=dev).to(t)
+        dd = (torch.randn((wl.total_q, wl.heads_q, dh), generator=g, device=dev) * wl.do_scale).to(t)
+        cq = torch.tensor(wl.cu_seqlens_q(), device=dev)
+        ck = torch.tensor(wl.cu_seqlens_k(), device=dev)
+        kw_ = dict(max_seqlen_q=wl.max_seqlen_q, max_seqlen_k=wl.max_seqlen_k, window=wl.window,
+                   causal=wl.causal, scale=wl.scale)
+        return (qq, kk, vv, dd, cq, ck), kw_
+
     # peak device memory of one fwd + bwd (all buffers come from torch)
     def peak_for(wl, xin=None):
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         torch.cuda.reset_peak_memory_stats()
         base = torch.cuda.memory_allocated()
-        g = torch.Generator(device=dev).manual_seed(0)
-        qq = torch.randn((wl.total_q, wl.heads_q, d), generator=g, device=dev).to(dt)
-        kk = torch.randn((wl.total_k, wl.heads_kv, d), generator=g, device=dev).to(dt)
-        vv = torch.randn((wl.total_k, wl.heads_kv, d), generator=g, device=dev).to(dt)
-        dd = torch.randn((wl.total_q, wl.heads_q, d), generator=g, device=dev).to(dt) * 0.1
-        cq = torch.tensor(wl.cu_seqlens_q(), device=dev)
-        ck = torch.tensor(wl.cu_seqlens_k(), device=dev)
+        (qq, kk, vv, dd, cq, ck), kk_ = device_inputs(wl)
         torch.cuda.synchronize()
         inputs = torch.cuda.memory_allocated() - base
         torch.cuda.reset_peak_memory_stats()
-        kk_ = dict(max_seqlen_q=wl.max_seqlen_q, max_seqlen_k=wl.max_seqlen_k, window=wl.window,
-                   causal=wl.causal, scale=wl.scale)
         oo, ll = swa.fwd(qq, kk, vv, cq, ck, **kk_)
         swa.bwd(qq, kk, vv, oo, ll, dd, cq, ck, **kk_)
         torch.cuda.synchronize()
@@ -309,6 +319,45 @@ def main() -> int:
         mem["peak_ratio_per_doubling"] = [round(sweep["16384"] / sweep["8192"], 3),
                                           round(sweep["32768"] / sweep["16384"], 3)]
     del del_list
+
+    # The memory-probe shape (head_dim 256, 32 query / 16 KV heads, w 1024):
+    # fwd + bwd throughput at 32K tokens and peak bytes above inputs at 8K,
+    # 16K and 32K tokens.
+    gemma = None
+    if not args.no_gemma:
+        gw = W.GEMMA_32K
+        (qq, kk, vv, dd, cq, ck), gkw = device_inputs(gw)
+        oo, ll = torch.empty_like(qq), torch.empty((gw.heads_q, gw.total_q), dtype=torch.float32, device=dev)
+        dq2, dk2, dv2 = torch.empty_like(qq), torch.empty_like(kk), torch.empty_like(vv)
+        ws2 = torch.empty(swa.workspace_bytes(swa.params_for(qq, kk, cq, ck, **gkw)), dtype=torch.uint8,
+                          device=dev)
+
+        def gstep():
+            swa.fwd(qq, kk, vv, cq, ck, out=oo, lse=ll, **gkw)
+            swa.bwd(qq, kk, vv, oo, ll, dd, cq, ck, dq=dq2, dk=dk2, dv=dv2, workspace=ws2, **gkw)
+
+        for _ in range(3):
+            gstep()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.gemma_steps):
+            gstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        g_ms = e0.elapsed_time(e1) / args.gemma_steps
+        g_flops = 14 * gw.head_dim * in_window_pairs(gw)
+        del qq, kk, vv, dd, oo, ll, dq2, dk2, dv2, ws2
+        gsweep = {}
+        for n in (8192, 16384, 32768):
+            pk, inp = peak_for(gw.replace(lengths_q=(n,), lengths_k=(n,)))
+            gsweep[str(n)] = round((pk - inp) / 1e9, 4)
+        gemma = {"workload": gw.name, "ms_per_step": round(g_ms, 4), "steps": args.gemma_steps,
+                 "tflops": round(g_flops / (g_ms * 1e-3) / 1e12, 2),
+                 "pct_bf16_peak": round(100 * g_flops / (g_ms * 1e-3) / 1e12 / BF16_DENSE_PEAK_TFLOPS, 2),
+                 "peak_above_inputs_gb_by_tokens": gsweep,
+                 "peak_ratio_per_doubling": [round(gsweep["16384"] / gsweep["8192"], 3),
+                                             round(gsweep["32768"] / gsweep["16384"], 3)]}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -337,6 +386,7 @@ def main() -> int:
         "kernels": kernels,
         "roofline": roofline,
         "memory": mem,
+        "memory_probe_shape": gemma,
         "cpu_baseline": cpu,
         "source_hash": source_hash(),
         "device": torch.cuda.get_device_name(0),

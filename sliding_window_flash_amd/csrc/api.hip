@@ -51,8 +51,11 @@ attn_status_t attn_check_params(const attn_params_t* p) {
       p->max_seqlen_q > p->total_q || p->max_seqlen_k > p->total_k)
     return ATTN_ERR_SHAPE;
   if (p->window < 1) return ATTN_ERR_WINDOW;
-  if (p->head_dim != 64 && p->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   if (p->dtype != ATTN_F32 && p->dtype != ATTN_BF16 && p->dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
+  // head_dim 256 is built for the 16-bit types (fp32 at 256 would need twice
+  // the registers and LDS of the 16-bit kernels)
+  if (p->head_dim != 64 && p->head_dim != 128 && !(p->head_dim == 256 && p->dtype != ATTN_F32))
+    return ATTN_ERR_UNSUPPORTED;
   if (p->causal != 0 && p->causal != 1) return ATTN_ERR_UNSUPPORTED;
   if (p->causal == 0 && p->window < p->max_seqlen_k) return ATTN_ERR_UNSUPPORTED;
   // the kernels fold the scale into exp2 arguments and take row maxima on raw

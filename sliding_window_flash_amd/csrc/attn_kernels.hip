@@ -146,8 +146,15 @@ constexpr float kRescaleSlack = 8.0f;
 
 template <int N> using ic = std::integral_constant<int, N>;
 
+// Waves per SIMD of the query-major kernels: two up to head_dim 128 (256
+// registers each; one wave's softmax overlaps the other's MFMAs); one at
+// head_dim 256, whose accumulator and Q fragments need the 512-register budget
+// (the 128 KB of K/V stages leave room for one workgroup per CU anyway).
+constexpr int waves_per_simd(int d) { return d > 128 ? 1 : 2; }
+
 template <typename T, int D, int BM, int BN>
-__global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
+fwd_kernel(AttnArgs a) {
   constexpr int NT = BM * 2;
   using KTile = LdsTile<T, BN, D>;
   // two stages (K tile then V tile each), separate arrays so that reading one
@@ -312,7 +319,8 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------- backward: dQ
 template <typename T, int D, int BM, int BN>
-__global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
+bwd_dq_kernel(AttnArgs a) {
   constexpr int NT = BM * 2;
   using KTile = LdsTile<T, BN, D>;
   __shared__ __attribute__((aligned(1024))) char st0[2 * KTile::kBytes];
@@ -613,6 +621,168 @@ bwd_dkdv_kernel(AttnArgs a) {
   }
 }
 
+// ------------------------------------------ backward: dK, dV at head_dim 256
+// One workgroup per (KV head, sequence, key tile of BN = 64 keys), 4 waves, one
+// per SIMD: wave w owns keys 32*(w%2) .. +31 and head dims 128*(w/2) .. +127
+// of dK and dV. Each wave forms S and dP for its 32 keys over all 256 dims in
+// every BM = 32-query step (the two dim halves of a key block compute them
+// alike), then adds its dims' share of P^T dO and dS^T Q. K and V stay in LDS;
+// query tiles stream through two stages. LDS: 2 x 32 KB for K, V and 2 x 33 KB
+// for the stages; the accumulators take 128 registers.
+template <typename T, int D, int BN, int BM>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+bwd_dkdv_wide_kernel(AttnArgs a) {
+  constexpr int NT = 256;
+  static_assert(D == 256 && BN == 64 && BM == 32, "wave layout assumes 2 key blocks x 2 dim halves");
+  constexpr int DH = D / 2;                               // dims per wave
+  using QTile = LdsTile<T, BM, D>;
+  using KTile = LdsTile<T, BN, D>;
+  constexpr int kStats = 64 * 4;                          // one 64-lane 4-byte load's worth
+  constexpr int kStage = 2 * QTile::kBytes + 2 * kStats;  // Q, dO, LSE*log2e, D
+  __shared__ __attribute__((aligned(1024))) char st0[kStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kStage];
+  __shared__ __attribute__((aligned(1024))) char klds[KTile::kBytes];
+  __shared__ __attribute__((aligned(1024))) char vlds[KTile::kBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int w = wave_uniform(tid >> 6);
+  const int kt = w & 1, dh = w >> 1;
+  const int nkb = (a.max_seqlen_k + BN - 1) / BN;
+  int L = xcd_remap((int)blockIdx.x, nkb * a.heads_kv * a.batch);
+  const int kb = L % nkb;
+  L /= nkb;
+  const int b = L % a.batch;
+  const int g = L / a.batch;
+  const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
+  const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
+  if (kb * BN >= lk) return;
+  const int grp = a.heads_q / a.heads_kv;
+  const bool causal = a.causal != 0;
+  const SeqGeom sg{lq, lk, a.window, causal};
+  const TileRange qr = key_tile_queries(sg, kb, BN, BM);
+
+  const int64_t qstride = (int64_t)a.heads_q * D;
+  const int64_t kstride = (int64_t)a.heads_kv * D;
+  const int j = kb * BN + 32 * kt + l32;  // this lane's key (rows past L_k arrive as zeros; not stored)
+  const bool key_ok = j < lk;
+  {
+    const int kvalid = min(BN, lk - kb * BN);
+    const int64_t koff = (int64_t)(k0 + kb * BN) * kstride + g * D;
+    const uint32_t sb = (uint32_t)(kstride * sizeof(T));
+    TileLoader<T, BN, D, NT> kvld;
+    kvld.init(sb, w, lane);
+    kvld.issue(klds, static_cast<const T*>(a.k) + koff, sb, kvalid);
+    kvld.issue(vlds, static_cast<const T*>(a.v) + koff, sb, kvalid);
+  }
+  RowReader<T, D> rrd;
+  rrd.init(l32, half);
+  ColReader<T, D> crd;
+  crd.init(lane);
+  f32x16 dka[DH / 32], dva[DH / 32];
+#pragma unroll
+  for (int dt = 0; dt < DH / 32; ++dt) {
+    dka[dt] = f32x16{};
+    dva[dt] = f32x16{};
+  }
+  const float c = a.scale * kLog2e;
+  const uint32_t wlim = (uint32_t)a.window;
+  const T* __restrict__ Qg = static_cast<const T*>(a.q);
+  const T* __restrict__ Dg = static_cast<const T*>(a.dout);
+
+  // (head, query tile) steps as in the 128-key kernel; an empty range writes zeros
+  const int nq = qr.hi >= qr.lo ? qr.hi - qr.lo + 1 : 0;
+  const int steps = grp * nq;
+  int nh = g * grp, nqb = qr.lo;
+  const uint32_t qsb = (uint32_t)(qstride * sizeof(T));
+  TileLoader<T, BM, D, NT> qld;
+  qld.init(qsb, w, lane);
+  auto fill = [&](char* st) {
+    const int qvalid = min(BM, lq - nqb * BM);
+    const int64_t qoff = (int64_t)(q0 + nqb * BM) * qstride + nh * D;
+    qld.issue(st, Qg + qoff, qsb, qvalid);
+    qld.issue(st + QTile::kBytes, Dg + qoff, qsb, qvalid);
+    if (w == 0) {  // 64 lanes, BM = 32 rows: lanes past qvalid read zeros
+      const int64_t idx = (int64_t)nh * a.total_q + q0 + nqb * BM;
+      buffer_to_lds4(buffer_rsrc(a.lse2 + idx, (uint32_t)qvalid * 4u), st + 2 * QTile::kBytes, (uint32_t)lane * 4u);
+      buffer_to_lds4(buffer_rsrc(a.delta + idx, (uint32_t)qvalid * 4u), st + 2 * QTile::kBytes + kStats,
+                     (uint32_t)lane * 4u);
+    }
+    if (++nqb > qr.hi) {
+      nqb = qr.lo;
+      ++nh;
+    }
+  };
+  if (steps > 0) fill(st0);
+  __syncthreads();
+
+  int qb = qr.lo;
+  auto step = [&](auto stage_c, int t) {
+    constexpr int stage = decltype(stage_c)::value;
+    const char* qs = stage ? st1 : st0;
+    const char* dos = qs + QTile::kBytes;
+    const float* lse2s = reinterpret_cast<const float*>(qs + 2 * QTile::kBytes);
+    const float* dlts = reinterpret_cast<const float*>(qs + 2 * QTile::kBytes + kStats);
+    if (t + 1 < steps) fill(stage ? st0 : st1);
+    const bool edge = !tile_full_i32(lq, lk, a.window, causal, qb, BM, kb, BN);
+    if (edge && block_masked(lq, lk, a.window, causal, qb * BM, BM, kb * BN + 32 * kt, 32)) {
+      if (++qb > qr.hi) qb = qr.lo;
+      __syncthreads();
+      return;
+    }
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int ss = 0; ss < D / 16; ++ss) {
+      mma(s, rrd.read(qs, 0, ss), rrd.read(klds, 32 * kt, ss));
+      mma(dp, rrd.read(dos, 0, ss), rrd.read(vlds, 32 * kt, ss));
+    }
+    if (edge) {
+      const int ib = qb * BM + 4 * half;
+      const int mb = ib + (lk - lq) - j;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        if ((ib + off >= lq) | (causal & ((uint32_t)(mb + off) >= wlim))) s[r] = -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int rr = 8 * r4 + 4 * half;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + rr);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlts + rr);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * r4 + e;
+        const float pv = fast_exp2(fmaf(s[r], c, -l4[e]));
+        s[r] = pv;
+        dp[r] = pv * (dp[r] - d4[e]);  // dS
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const Frag<T> pf = acc_frag<T>(s, u);
+      const Frag<T> dsf = acc_frag<T>(dp, u);
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt) {
+        mma(dva[dt], crd.read(dos, 16 * u, (DH / 32) * dh + dt), pf);
+        mma(dka[dt], crd.read(qs, 16 * u, (DH / 32) * dh + dt), dsf);
+      }
+    }
+    if (++qb > qr.hi) qb = qr.lo;
+    __syncthreads();
+  };
+  for (int t = 0; t < steps;) {
+    step(ic<0>{}, t);
+    if (++t >= steps) break;
+    step(ic<1>{}, t);
+    ++t;
+  }
+  if (key_ok) {
+    const int64_t roff = (int64_t)(k0 + j) * kstride + g * D + DH * dh;
+    store_acc_rows<T, DH>(static_cast<T*>(a.dk) + roff, dka, a.scale, half);
+    store_acc_rows<T, DH>(static_cast<T*>(a.dv) + roff, dva, 1.f, half);
+  }
+}
+
 // ------------------------------------------------ backward: dK, dV (4 waves)
 // The general dK/dV kernel (used for fp32, whose tiles are twice as large):
 // 4 waves of 32 keys, K and V in registers, 64-query steps.
@@ -762,26 +932,30 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------- launchers
-// Tile shapes (bf16 and fp32 alike): forward and dQ take 128 query rows (4
-// waves of 32) and step over keys 64 at a time; dK/dV takes 128 keys (8
-// waves: 4 key blocks of 32 x 2 query halves) and steps over queries 64 at a
-// time.
-struct Tiles {
-  static constexpr int kFwdBM = 128, kFwdBN = 64, kBwdBN = 128, kBwdBM = 64;
+// Tile shapes (every dtype): forward and dQ take 128 query rows (4 waves of
+// 32) and step over keys 64 at a time. dK/dV takes 128 keys (8 waves: 4 key
+// blocks of 32 x 2 query halves; fp32: 4 waves) and steps over queries 64 at a
+// time; at head_dim 256 it takes 64 keys (4 waves: 2 key blocks x 2 dim
+// halves) and steps over queries 32 at a time.
+template <int D> struct Tiles {
+  static constexpr int kFwdBM = 128, kFwdBN = 64;
+  static constexpr int kBwdBN = D > 128 ? 64 : 128, kBwdBM = D > 128 ? 32 : 64;
 };
 
 template <typename T, int D>
 static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
-  const int64_t nqb = (a.max_seqlen_q + Tiles::kFwdBM - 1) / Tiles::kFwdBM;
+  using TL = Tiles<D>;
+  const int64_t nqb = (a.max_seqlen_q + TL::kFwdBM - 1) / TL::kFwdBM;
   const int64_t grid = nqb * a.heads_q * a.batch;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_kernel<T, D, Tiles::kFwdBM, Tiles::kFwdBN>), dim3((unsigned)grid),
-                     dim3(Tiles::kFwdBM * 2), 0, st, a);
+  hipLaunchKernelGGL((fwd_kernel<T, D, TL::kFwdBM, TL::kFwdBN>), dim3((unsigned)grid), dim3(TL::kFwdBM * 2), 0,
+                     st, a);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t launch_bwd_t(int stages, const AttnArgs& a, hipStream_t st) {
+  using TL = Tiles<D>;
   const int64_t rows = (int64_t)a.total_q * a.heads_q;
   hipError_t e = hipSuccess;
   if ((stages & 1) && rows > 0) {
@@ -790,31 +964,37 @@ static hipError_t launch_bwd_t(int stages, const AttnArgs& a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 2) {
-    const int64_t nqb = (a.max_seqlen_q + Tiles::kFwdBM - 1) / Tiles::kFwdBM;
+    const int64_t nqb = (a.max_seqlen_q + TL::kFwdBM - 1) / TL::kFwdBM;
     const int64_t g1 = nqb * a.heads_q * a.batch;
     if (g1 > 0 && rows > 0) {
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D, Tiles::kFwdBM, Tiles::kFwdBN>), dim3((unsigned)g1),
-                         dim3(Tiles::kFwdBM * 2), 0, st, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, TL::kFwdBM, TL::kFwdBN>), dim3((unsigned)g1), dim3(TL::kFwdBM * 2),
+                         0, st, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
-  const int64_t nkb = (a.max_seqlen_k + Tiles::kBwdBN - 1) / Tiles::kBwdBN;
+  const int64_t nkb = (a.max_seqlen_k + TL::kBwdBN - 1) / TL::kBwdBN;
   const int64_t g2 = nkb * a.heads_kv * a.batch;
   if ((stages & 4) && g2 > 0) {
-    if constexpr (sizeof(T) == 2)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, Tiles::kBwdBN, Tiles::kBwdBM>), dim3((unsigned)g2),
-                         dim3(Tiles::kBwdBN * 4), 0, st, a);
+    if constexpr (D > 128)
+      hipLaunchKernelGGL((bwd_dkdv_wide_kernel<T, D, TL::kBwdBN, TL::kBwdBM>), dim3((unsigned)g2), dim3(256), 0,
+                         st, a);
+    else if constexpr (sizeof(T) == 2)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, TL::kBwdBN, TL::kBwdBM>), dim3((unsigned)g2),
+                         dim3(TL::kBwdBN * 4), 0, st, a);
     else
-      hipLaunchKernelGGL((bwd_dkdv4_kernel<T, D, Tiles::kBwdBN, Tiles::kBwdBM>), dim3((unsigned)g2),
-                         dim3(Tiles::kBwdBN * 2), 0, st, a);
+      hipLaunchKernelGGL((bwd_dkdv4_kernel<T, D, TL::kBwdBN, TL::kBwdBM>), dim3((unsigned)g2),
+                         dim3(TL::kBwdBN * 2), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
+// head_dim 256 exists for the 16-bit types only (the C ABI refuses fp32 there)
 hipError_t launch_fwd(int dtype, int head_dim, const AttnArgs& a, hipStream_t st) {
+  if (dtype == 2 && head_dim == 256) return launch_fwd_t<fp16, 256>(a, st);
   if (dtype == 2 && head_dim == 128) return launch_fwd_t<fp16, 128>(a, st);
   if (dtype == 2 && head_dim == 64) return launch_fwd_t<fp16, 64>(a, st);
+  if (dtype == 1 && head_dim == 256) return launch_fwd_t<bf16, 256>(a, st);
   if (dtype == 1 && head_dim == 128) return launch_fwd_t<bf16, 128>(a, st);
   if (dtype == 1 && head_dim == 64) return launch_fwd_t<bf16, 64>(a, st);
   if (dtype == 0 && head_dim == 128) return launch_fwd_t<float, 128>(a, st);
@@ -823,8 +1003,10 @@ hipError_t launch_fwd(int dtype, int head_dim, const AttnArgs& a, hipStream_t st
 }
 
 hipError_t launch_bwd(int dtype, int head_dim, int stages, const AttnArgs& a, hipStream_t st) {
+  if (dtype == 2 && head_dim == 256) return launch_bwd_t<fp16, 256>(stages, a, st);
   if (dtype == 2 && head_dim == 128) return launch_bwd_t<fp16, 128>(stages, a, st);
   if (dtype == 2 && head_dim == 64) return launch_bwd_t<fp16, 64>(stages, a, st);
+  if (dtype == 1 && head_dim == 256) return launch_bwd_t<bf16, 256>(stages, a, st);
   if (dtype == 1 && head_dim == 128) return launch_bwd_t<bf16, 128>(stages, a, st);
   if (dtype == 1 && head_dim == 64) return launch_bwd_t<bf16, 64>(stages, a, st);
   if (dtype == 0 && head_dim == 128) return launch_bwd_t<float, 128>(stages, a, st);
@@ -832,12 +1014,19 @@ hipError_t launch_bwd(int dtype, int head_dim, int stages, const AttnArgs& a, hi
   return hipErrorInvalidValue;
 }
 
+template <int D> static void tiles_of(int* fwd_bm, int* fwd_bn, int* bwd_bn, int* bwd_bm) {
+  *fwd_bm = Tiles<D>::kFwdBM;
+  *fwd_bn = Tiles<D>::kFwdBN;
+  *bwd_bn = Tiles<D>::kBwdBN;
+  *bwd_bm = Tiles<D>::kBwdBM;
+}
+
 bool tile_sizes(int dtype, int head_dim, int* fwd_bm, int* fwd_bn, int* bwd_bn, int* bwd_bm) {
-  if ((dtype != 0 && dtype != 1 && dtype != 2) || (head_dim != 64 && head_dim != 128)) return false;
-  *fwd_bm = Tiles::kFwdBM;
-  *fwd_bn = Tiles::kFwdBN;
-  *bwd_bn = Tiles::kBwdBN;
-  *bwd_bm = Tiles::kBwdBM;
+  if (dtype != 0 && dtype != 1 && dtype != 2) return false;
+  if (head_dim == 64) tiles_of<64>(fwd_bm, fwd_bn, bwd_bn, bwd_bm);
+  else if (head_dim == 128) tiles_of<128>(fwd_bm, fwd_bn, bwd_bn, bwd_bm);
+  else if (head_dim == 256 && dtype != 0) tiles_of<256>(fwd_bm, fwd_bn, bwd_bn, bwd_bm);
+  else return false;
   return true;
 }
 

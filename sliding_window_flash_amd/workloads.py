@@ -106,6 +106,11 @@ CAUSAL_8K = _fixed("bf16_n8192_causal_32q8kv_d128", 8192, 32, 8, 128, 8192, "bf1
                    1 / math.sqrt(128), 0.1, 3)
 SWA_32K = _fixed("bf16_n32768_w1024_32q8kv_d128", 32768, 32, 8, 128, 1024, "bf16",
                  1 / math.sqrt(128), 0.1, 4)
+# The memory-probe shape of one sliding-window layer (head_dim 256, 32 query /
+# 16 KV heads, window 1024, bf16), at its longest length; 8K and 16K are the
+# same workload with shorter sequences.
+GEMMA_32K = _fixed("bf16_n32768_w1024_32q16kv_d256", 32768, 32, 16, 256, 1024, "bf16",
+                   1 / math.sqrt(256), 0.1, 6)
 
 
 def varlen_workload(seed: int = 5, window: int = 1024) -> Workload:
@@ -116,7 +121,7 @@ def varlen_workload(seed: int = 5, window: int = 1024) -> Workload:
 
 VARLEN_4 = varlen_workload()
 
-WORKLOADS = {w.name: w for w in (TINY_F32, GQA_2K, CAUSAL_8K, SWA_32K, VARLEN_4)}
+WORKLOADS = {w.name: w for w in (TINY_F32, GQA_2K, CAUSAL_8K, SWA_32K, VARLEN_4, GEMMA_32K)}
 
 # Edge sweep windows for the ragged batch: 1, around one 128-key tile, and the
 # longest sequence (equivalent to plain causal).

@@ -44,13 +44,16 @@ def good(**kw):
     (dict(window=0), 3),
     (dict(window=-5), 3),
     (dict(head_dim=96), 4),
-    (dict(head_dim=256), 4),
+    (dict(head_dim=512), 4),
     (dict(dtype=7), 4),
     (dict(causal=False, window=50), 4),
     (dict(causal=False, window=100), 0),
     (dict(window=swa.INT32_MAX), 0),
     (dict(dtype=swa.ATTN_F32, head_dim=64), 0),
     (dict(dtype=swa.ATTN_F16), 0),
+    (dict(head_dim=256), 0),
+    (dict(head_dim=256, dtype=swa.ATTN_F16), 0),
+    (dict(head_dim=256, dtype=swa.ATTN_F32), 4),
     (dict(dtype=3), 4),
     (dict(scale=0.0), 4),
     (dict(scale=-0.1), 4),
@@ -106,5 +109,8 @@ def test_tile_sizes():
     bm, bn, kbn, kbm = swa.tile_sizes(128, swa.ATTN_BF16)
     assert bm % 32 == 0 and bn % 32 == 0 and kbn % 32 == 0 and kbm % 32 == 0
     assert swa.tile_sizes(128, swa.ATTN_F16) == (bm, bn, kbn, kbm)
+    assert swa.tile_sizes(256, swa.ATTN_BF16)[2:] == (64, 32)
+    with pytest.raises(swa.AttnError):
+        swa.tile_sizes(256, swa.ATTN_F32)
     with pytest.raises(swa.AttnError):
         swa.tile_sizes(96, swa.ATTN_BF16)

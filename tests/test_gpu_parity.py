@@ -57,6 +57,9 @@ SMALL = [
     ([300, 1, 517, 64], None, 8, 2, 128, 129, True, "fp16"),  # fp16: ragged, windowed
     ([100, 40], [700, 300], 4, 1, 64, 16, True, "fp16"),
     ([200, 333], None, 4, 2, 128, INT32_MAX, False, "fp16"),
+    ([300, 1, 517, 64], None, 8, 4, 256, 129, True, "bf16"),  # head_dim 256: ragged, windowed
+    ([100, 40], [700, 300], 4, 2, 256, 16, True, "fp16"),   # L_q < L_k at 256
+    ([200, 333], None, 4, 2, 256, INT32_MAX, False, "bf16"),  # full attention at 256
 ]
 
 
@@ -68,7 +71,7 @@ def test_small_cases_full_oracle(case):
     _run_full(w)
 
 
-@pytest.mark.parametrize("dt,d", [("bf16", 128), ("fp16", 64), ("f32", 64)])
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("fp16", 64), ("bf16", 256), ("f32", 64)])
 def test_window_one_closed_form(dt, d):
     w = small_case([300, 130], [300, 200], heads_q=4, heads_kv=2, head_dim=d, window=1, dtype=dt,
                    do_scale=0.1, seed=31)
@@ -138,7 +141,7 @@ def _invariants(w, x, got):
             assert np.all(np.abs(sk) <= 0.05 * nk + 1e-6), (b, g)
 
 
-@pytest.mark.parametrize("w", [W.CAUSAL_8K, W.SWA_32K, W.VARLEN_4], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [W.CAUSAL_8K, W.SWA_32K, W.VARLEN_4, W.GEMMA_32K], ids=lambda w: w.name)
 def test_measured_workloads_sampled(w):
     H.say(f"case {w.name}: sampled rows at full size")
     x = make_inputs(w)

@@ -80,11 +80,12 @@ def test_int32_max_window_does_not_overflow():
     assert (lo, hi) == (0, (40000 - 1) // 64)
 
 
-def test_compiled_tiles_hit_both_silent_cases():
+@pytest.mark.parametrize("head_dim", [128, 256])
+def test_compiled_tiles_hit_both_silent_cases(head_dim):
     """With the tile sizes the kernels use, N=1024 / w=32 has query tiles whose
     first visited key tile is not tile zero, and L_q < L_k with a short window
     has key tiles that no query visits."""
-    bm, bn, kbn, kbm = swa.tile_sizes(128, swa.ATTN_BF16)
+    bm, bn, kbn, kbm = swa.tile_sizes(head_dim, swa.ATTN_BF16)
     p = params(1024, 1024, 32, True)
     los = [swa.query_tile_range(p, [0, 1024], [0, 1024], 0, qb, bm, bn)[0]
            for qb in range(1024 // bm)]

@@ -17,6 +17,12 @@ def test_window_and_token_counts_come_from_the_pages():
     assert (c.batch, c.heads_q, c.heads_kv, c.max_seqlen_q, c.head_dim) == (
         op["batch"], op["heads_q"], op["heads_kv"], op["tokens"], op["head_dim"])
     assert c.window >= c.max_seqlen_k  # plain causal
+    probe = GOLDEN["memory_probe_heads"]["value"]
+    g = W.GEMMA_32K
+    assert (g.heads_q, g.heads_kv, g.head_dim, g.dtype) == (
+        probe["heads_q"], probe["heads_kv"], probe["head_dim"], probe["dtype"])
+    assert g.max_seqlen_q == max(GOLDEN["memory_probe_tokens"]["value"])
+    assert g.window == GOLDEN["sliding_window_tokens"]["value"]
 
 
 def test_ragged_lengths_follow_the_corpus_statistics():
@@ -40,3 +46,6 @@ def test_inputs_are_seeded_and_bf16_representable():
     for k in ("q", "k", "v", "do"):
         bits = x[k].view(np.uint32)
         assert np.all(bits & 0xFFFF == 0), k
+    x = W.make_inputs(w.replace(dtype="fp16"))
+    for k in ("q", "k", "v", "do"):
+        assert np.array_equal(x[k].astype(np.float16).astype(np.float32), x[k]), k
