@@ -1,0 +1,67 @@
+"""Parity-sweep grid on the GPU: many small shapes against the fp64 oracle,
+element by element (the lab record's gradient-parity entry sweeps dtypes,
+head dims, grouped-query ratios, queries shorter than keys, windows from 1 up,
+causal and not). The cases are a fixed, seeded draw from that grid plus its
+corners; each case spans several tiles with ragged tails."""
+import zlib
+
+import numpy as np
+import pytest
+
+import gpu_helpers as H
+from sliding_window_flash_amd.workloads import INT32_MAX, make_inputs, small_case
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ("f32", "bf16", "fp16")
+WINDOWS = (1, 2, 7, 31, 64, 100, 128, 129, 300, 1000, INT32_MAX)
+
+
+def _grid(n=60, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        dt = DTYPES[rng.integers(3)]
+        d = int(rng.choice([64, 128, 256] if dt != "f32" else [64, 128]))
+        hkv = int(rng.choice([1, 2]))
+        g = int(rng.choice([1, 2, 4]))
+        nseq = int(rng.integers(1, 4))
+        lq = [int(x) for x in rng.integers(1, 300, nseq)]
+        shorter = rng.random() < 0.35          # queries shorter than keys
+        lk = [q + int(rng.integers(1, 200)) for q in lq] if shorter else None
+        causal = rng.random() < 0.8
+        window = int(WINDOWS[rng.integers(len(WINDOWS))]) if causal else INT32_MAX
+        cases.append((tuple(lq), None if lk is None else tuple(lk), hkv * g, hkv, d, window, causal, dt))
+    return cases
+
+
+CASES = _grid()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def test_grid_covers_its_corners():
+    seen = {(c[7], c[4]) for c in CASES}
+    assert {("f32", 64), ("bf16", 128), ("fp16", 256)} <= seen
+    assert any(c[5] == 1 for c in CASES) and any(not c[6] for c in CASES)
+    assert any(c[1] is not None for c in CASES) and any(c[2] // c[3] == 4 for c in CASES)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[7]}-d{c[4]}-g{c[2] // c[3]}-w{c[5]}-{'c' if c[6] else 'nc'}-{len(c[0])}seq")
+def test_sweep_case(case):
+    lq, lk, hq, hkv, d, win, causal, dt = case
+    # dO at 0.1 as in the bench workloads: at window 1 the exact dQ and dK are
+    # zero and what remains is rounding of dP - D, which scales with |dO| |V|;
+    # the zero-reference bars are set for that scale
+    w = small_case(lq, lk, heads_q=hq, heads_kv=hkv, head_dim=d, window=win, causal=causal, dtype=dt,
+                   do_scale=0.1, seed=zlib.crc32(repr(case).encode()) % 10000)
+    H.say(f"sweep case {case}")
+    x = make_inputs(w)
+    got = H.run_hip(w, H.to_device(w, x))
+    zero = ("dq", "dk") if win == 1 else ()
+    H.compare_full(w, x, got, zero=zero)
