@@ -17,7 +17,10 @@ G = Hq / Hkv), query row i and key j:
                visible iff j <= p and p - j < w: w keys counting the token
                itself, so w = 1 sees only itself (the record entry "Gradient
                parity, small shapes": at window 1 the true gradient is zero).
-               Non-causal without a window: every key is visible.
+               Without the causal mask (the same entry sweeps windows "causal
+               and not"), the window is two-sided: visible iff |p - j| < w, so
+               w = 1 again sees only the token itself and any w >= L_k sees
+               every key (plain non-causal attention).
   forward      s_ij = scale * q_i . k_j on visible cells, -inf elsewhere;
                LSE_i = log sum_j exp(s_ij) (natural log); P_ij = exp(s_ij - LSE_i);
                O_i = sum_j P_ij v_j. The saved state is O and LSE (mlx-train-perf
@@ -84,13 +87,11 @@ def check_host_ram(nbytes: int, ceiling: Optional[int] = None) -> None:
 def visible_cells(lq: int, lk: int, window: int, causal: bool,
                   rows: Optional[np.ndarray] = None) -> np.ndarray:
     """Boolean [len(rows), lk] mask of visible (query, key) cells."""
-    if not causal and window < lk:
-        raise ValueError("a window is defined only for causal attention")
     i = np.arange(lq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
     j = np.arange(lk, dtype=np.int64)
-    if not causal:
-        return np.ones((i.size, lk), dtype=bool)
     pos = (i + (lk - lq))[:, None]
+    if not causal:
+        return np.abs(pos - j[None, :]) < window
     return (j[None, :] <= pos) & (pos - j[None, :] < window)
 
 

@@ -47,7 +47,7 @@ def sdpa_loop(q, k, v, do, cu_q, cu_k, scale, window, causal) -> dict:
                     if causal:
                         if j <= me and me - j < window:
                             keys.append(j)
-                    else:
+                    elif -window < me - j < window:  # two-sided window
                         keys.append(j)
                 if not keys:
                     continue

@@ -14,7 +14,11 @@ AssertionError if the module disagrees with:
     (sum_j dK_j = 0); shifting all values shifts O (sum_j dV_j = sum_i dO_i);
     grouped-query = multi-head with repeated K/V; a packed batch = independent
     runs; a window w query = plain causal attention over its last w keys;
-    window >= N is plain causal.
+    window >= N is plain causal,
+  * two-sided windows (no causal mask): window 1 sees only the token itself;
+    reversing the token order reverses every output (the window is
+    symmetric); a row equals full attention over the keys within w - 1 of its
+    position; window >= L_k is full attention.
 """
 from __future__ import annotations
 
@@ -52,6 +56,8 @@ FD_CASES = [
     ([5, 7], None, 2, 1, 3, INT32_MAX, True),
     ([3, 4], [5, 7], 2, 1, 2, 2, True),
     ([4], None, 2, 2, 2, INT32_MAX, False),
+    ([6, 5], None, 2, 1, 2, 2, False),                 # two-sided windows
+    ([3, 4], [5, 7], 2, 1, 2, 3, False),
 ]
 
 
@@ -254,6 +260,60 @@ def pin_wide_window_is_causal(ref):
         assert np.array_equal(a[key], c[key]), f"window >= N vs causal {key}"
 
 
+def pin_two_sided_window_one(ref):
+    w = small_case([6, 9], [8, 11], heads_q=4, heads_kv=2, head_dim=5, window=1, causal=False, seed=13)
+    x = make_inputs(w)
+    out = _call(ref, w, x)
+    grp = w.heads_q // w.heads_kv
+    for b in range(w.batch):
+        lq, lk = w.lengths_q[b], w.lengths_k[b]
+        for i in range(lq):
+            t, kt = x["cu_q"][b] + i, x["cu_k"][b] + i + lk - lq
+            for h in range(w.heads_q):
+                _close(out["o"][t, h], x["v"][kt, h // grp], 1e-13, "two-sided window 1: O = V")
+    _close(out["dq"], np.zeros_like(out["dq"]), 1e-12, "two-sided window 1: dQ = 0")
+    _close(out["dk"], np.zeros_like(out["dk"]), 1e-12, "two-sided window 1: dK = 0")
+
+
+def pin_two_sided_flip(ref):
+    """With L_q = L_k, reversing the token order maps |p - j| < w onto itself,
+    so every output comes back reversed."""
+    w = small_case([11], heads_q=2, heads_kv=1, head_dim=3, window=3, causal=False, seed=14)
+    x = make_inputs(w)
+    a = _call(ref, w, x)
+    r = {n: x[n][::-1].copy() for n in ("q", "k", "v", "do")}
+    b = _call(ref, w, x, **r)
+    for key in ("o", "dq", "dk", "dv"):
+        _close(a[key], b[key][::-1], 1e-13, f"two-sided flip {key}")
+    _close(a["lse"], b["lse"][:, ::-1], 1e-13, "two-sided flip lse")
+
+
+def pin_two_sided_is_local(ref):
+    wnd = 3
+    n = 12
+    w = small_case([n], heads_q=1, heads_kv=1, head_dim=3, window=wnd, causal=False, seed=15)
+    x = make_inputs(w)
+    out = _call(ref, w, x)
+    for i in range(n):
+        lo, hi = max(0, i - wnd + 1), min(n, i + wnd)
+        cu = np.array([0, hi - lo], np.int32)
+        part = ref.sdpa_reference(x["q"][lo:hi], x["k"][lo:hi], x["v"][lo:hi], x["do"][lo:hi], cu, cu,
+                                  w.scale, INT32_MAX, False)
+        _close(out["o"][i], part["o"][i - lo], 1e-13, "two-sided row = full attention over |p - j| < w")
+        _close(out["lse"][:, i], part["lse"][:, i - lo], 1e-13, "two-sided LSE = full over the band")
+
+
+def pin_wide_two_sided_is_full(ref):
+    w = small_case([9, 6], [9, 10], heads_q=2, heads_kv=1, head_dim=3, window=10, causal=False, seed=16)
+    x = make_inputs(w)
+    a = _call(ref, w, x)
+    c = _call(ref, w, x, window=INT32_MAX)
+    for key in a:
+        assert np.array_equal(a[key], c[key]), f"two-sided window >= L_k vs full {key}"
+
+
 ALL_PINS = [pin_finite_differences, pin_loop, pin_window_one, pin_scale_zero,
             pin_hand_example, pin_softmax_rows, pin_shift_identities, pin_gqa_is_repeated_mha,
-            pin_packed_is_concatenation, pin_window_is_local, pin_wide_window_is_causal]
+            pin_packed_is_concatenation, pin_window_is_local, pin_wide_window_is_causal,
+            pin_two_sided_window_one, pin_two_sided_flip, pin_two_sided_is_local,
+            pin_wide_two_sided_is_full]

@@ -23,6 +23,9 @@ MUTANTS = {
     "interleaved head groups": ("g = h // grp\n            kg", "g = h % hkv\n            kg"),
     "log base 2 in LSE": ("lse = np.where(has_key, m + np.log(zs)", "lse = np.where(has_key, m + np.log2(zs)"),
     "dK from dO instead of Q": ("scale * (ds.T @ qh)", "scale * (ds.T @ doh)"),
+    "two-sided window one-sided": ("return np.abs(pos - j[None, :]) < window", "return (pos - j[None, :]) < window"),
+    "two-sided window one key wider": ("return np.abs(pos - j[None, :]) < window",
+                                       "return np.abs(pos - j[None, :]) <= window"),
 }
 
 

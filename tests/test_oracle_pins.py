@@ -52,9 +52,11 @@ def test_empty_rows_convention():
     assert np.all(out["o"] == 0) and np.all(np.isneginf(out["lse"])) and np.all(out["dq"] == 0)
 
 
-def test_window_without_causal_is_refused():
-    with pytest.raises(ValueError):
-        dense.visible_cells(4, 4, 2, False)
+def test_two_sided_mask_is_the_band():
+    m = dense.visible_cells(5, 7, 2, False)
+    for i in range(5):
+        p = i + 2
+        assert [j for j in range(7) if m[i, j]] == [j for j in (p - 1, p, p + 1) if 0 <= j < 7]
 
 
 def test_host_ram_guard_refuses_up_front():
