@@ -16,8 +16,10 @@
  *
  *   Visibility. Sequence b has L_q query and L_k key tokens, L_q <= L_k;
  *   query i sits at key position p = i + L_k - L_q. Key j is visible to query
- *   i iff j <= p and p - j < window (causal), or always (non-causal, which
- *   requires window >= max_seqlen_k). window = 1 sees only the token itself.
+ *   i iff j <= p and p - j < window (causal), or iff |p - j| < window (non-causal:
+ *   a two-sided window; any window >= L_k is full attention). window = 1 sees
+ *   only the token itself (the lab record's gradient-parity sweep runs windows
+ *   causal and not).
  *   Key tiles lying wholly outside a query tile's window are skipped; cells on
  *   the window edge are masked ("What did fixing it take?": skip blocks
  *   entirely outside the window, mask the cells at its edge). A query tile's
@@ -76,7 +78,8 @@ typedef enum {
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
   ATTN_ERR_SHAPE = 2,       /* sizes inconsistent (batch < 1, heads_q % heads_kv, heads_q > 16384, totals ...) */
   ATTN_ERR_WINDOW = 3,      /* window < 1 */
-  ATTN_ERR_UNSUPPORTED = 4, /* head_dim not 64/128, unknown dtype, window without causal, scale <= 0 */
+  ATTN_ERR_UNSUPPORTED = 4, /* head_dim not 64/128 (256: 16-bit dtypes only), unknown dtype, scale <= 0,
+                               a two-sided window with max_seqlen_k > 2^30 */
   ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than attn_bwd_workspace_bytes */
   ATTN_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
   ATTN_ERR_ALIGN = 7        /* a tensor pointer is not 16-byte aligned */
@@ -92,7 +95,7 @@ typedef struct {
   int32_t max_seqlen_q; /* >= every L_q; sizes the launch grid (no device reads) */
   int32_t max_seqlen_k; /* >= every L_k */
   int32_t window;       /* >= 1; any value >= max_seqlen_k (e.g. INT32_MAX) is no window */
-  int32_t causal;       /* 1 causal; 0 full attention (then window >= max_seqlen_k) */
+  int32_t causal;       /* 1 causal; 0 two-sided window (full attention if window >= max_seqlen_k) */
   float scale;          /* softmax scale, finite and > 0, e.g. 1/sqrt(head_dim) */
   int32_t dtype;        /* attn_dtype_t */
 } attn_params_t;

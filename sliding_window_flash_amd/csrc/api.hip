@@ -57,7 +57,9 @@ attn_status_t attn_check_params(const attn_params_t* p) {
   if (p->head_dim != 64 && p->head_dim != 128 && !(p->head_dim == 256 && p->dtype != ATTN_F32))
     return ATTN_ERR_UNSUPPORTED;
   if (p->causal != 0 && p->causal != 1) return ATTN_ERR_UNSUPPORTED;
-  if (p->causal == 0 && p->window < p->max_seqlen_k) return ATTN_ERR_UNSUPPORTED;
+  // a two-sided window (no causal mask, window < max_seqlen_k) forms p + window
+  // - 1 in 32 bits in the kernels' masks
+  if (p->causal == 0 && p->window < p->max_seqlen_k && p->max_seqlen_k > (1 << 30)) return ATTN_ERR_UNSUPPORTED;
   // the kernels fold the scale into exp2 arguments and take row maxima on raw
   // scores, which needs a positive scale
   if (!(p->scale > 0.f) || !isfinite(p->scale)) return ATTN_ERR_UNSUPPORTED;
@@ -170,7 +172,7 @@ const char* attn_status_str(attn_status_t s) {
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "inconsistent sizes";
     case ATTN_ERR_WINDOW: return "window must be >= 1";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration (head_dim, dtype, or a window without the causal mask)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration (head_dim, dtype, scale, or a two-sided window over sequences longer than 2^30)";
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_HIP: return "HIP launch error";
     case ATTN_ERR_ALIGN: return "pointer not aligned (tensors need 16 bytes)";

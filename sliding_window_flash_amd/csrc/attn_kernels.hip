@@ -146,6 +146,39 @@ constexpr float kRescaleSlack = 8.0f;
 
 template <int N> using ic = std::integral_constant<int, N>;
 
+// Per-query visibility as one unsigned range test with a wave-uniform limit:
+// key j is visible to the query at key position p iff
+// (unsigned)(mpos - j) < mlim, i.e. j lies in [mpos - mlim + 1, mpos].
+// Causal: mpos = p, mlim = w. Full attention: mpos = L_k - 1, mlim = 2^31 - 1.
+// Two-sided (w < L_k; the C ABI limits L_k to 2^30 so that mpos = p + w - 1
+// fits for every real row): mlim = 2w - 1, and keys at or past L_k (the
+// padding rows of a sequence's last tile) must be masked as well (pad_keys).
+// Only mpos is per lane, so the limit stays in a scalar register.
+struct RowWindow {
+  uint32_t mpos, mlim;
+  bool pad_keys;
+};
+__device__ __forceinline__ RowWindow row_window(int p, int lk, int window, bool causal) {
+  if (causal) return {(uint32_t)p, (uint32_t)window, false};
+  if (window >= lk) return {(uint32_t)(lk - 1), 0x7fffffffu, false};
+  return {(uint32_t)p + (uint32_t)(window - 1), 2u * (uint32_t)window - 1u, true};
+}
+
+// The same rule per (query position p, key j) pair for the key-major kernels,
+// where registers run over queries: masked iff windowed and
+// (unsigned)(p - j + off) >= lim. Causal: off 0, lim w. Two-sided (w < L_k):
+// off w - 1, lim 2w - 1. Full attention: not windowed.
+struct PairWindow {
+  bool windowed;
+  int off;
+  uint32_t lim;
+};
+__device__ __forceinline__ PairWindow pair_window(int lk, int window, bool causal) {
+  if (causal) return {true, 0, (uint32_t)window};
+  if (window >= lk) return {false, 0, 0u};
+  return {true, window - 1, 2u * (uint32_t)window - 1u};
+}
+
 // Waves per SIMD of the query-major kernels: two up to head_dim 128 (256
 // registers each; one wave's softmax overlaps the other's MFMAs); one at
 // head_dim 256, whose accumulator and Q fragments need the 512-register budget
@@ -188,12 +221,10 @@ fwd_kernel(AttnArgs a) {
   rrd.init(l32, half);
   ColReader<T, D> crd;
   crd.init(lane);
-  // Edge mask: visible iff (unsigned)(mpos - j) < mlim. Causal: mpos = p,
-  // mlim = window (covers j <= p and p - j < window). Full attention: mpos =
-  // L_k - 1, mlim = 2^31 - 1 (covers j < L_k). Key rows past L_k in the last
-  // tile hold copies of row L_k - 1 and are always masked.
-  const int mpos = a.causal ? i + (it.lk - it.lq) : it.lk - 1;
-  const uint32_t mlim = a.causal ? (uint32_t)a.window : 0x7fffffffu;
+  // Edge mask: visible iff (unsigned)(mpos - j) < mlim (row_window). Key rows
+  // past L_k in the last tile arrive as zeros and are always masked.
+  const RowWindow rw = row_window(i + (it.lk - it.lq), it.lk, a.window, a.causal != 0);
+  const uint32_t mpos = rw.mpos, mlim = rw.mlim;
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -227,12 +258,20 @@ fwd_kernel(AttnArgs a) {
       for (int ss = 0; ss < D / 16; ++ss) mma(s[kt], rrd.read(ks, 32 * kt, ss), qf[ss]);
     }
     if (edge) {
-      const int mb = mpos - (kb * BN + 4 * half);
+      const uint32_t mb = mpos - (uint32_t)(kb * BN + 4 * half);
 #pragma unroll
       for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if ((uint32_t)(mb - (32 * kt + 8 * (r >> 2) + (r & 3))) >= mlim) s[kt][r] = -INFINITY;
+          if (mb - (uint32_t)(32 * kt + 8 * (r >> 2) + (r & 3)) >= mlim) s[kt][r] = -INFINITY;
+      if (rw.pad_keys && kb * BN + BN > it.lk) {  // two-sided: the keys past L_k
+        const int jb = kb * BN + 4 * half;
+#pragma unroll
+        for (int kt = 0; kt < BN / 32; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (jb + 32 * kt + 8 * (r >> 2) + (r & 3) >= it.lk) s[kt][r] = -INFINITY;
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -361,8 +400,8 @@ bwd_dq_kernel(AttnArgs a) {
   rrd.init(l32, half);
   ColReader<T, D> crd;
   crd.init(lane);
-  const int mpos = a.causal ? i + (it.lk - it.lq) : it.lk - 1;
-  const uint32_t mlim = a.causal ? (uint32_t)a.window : 0x7fffffffu;
+  const RowWindow rw = row_window(i + (it.lk - it.lq), it.lk, a.window, a.causal != 0);
+  const uint32_t mpos = rw.mpos, mlim = rw.mlim;
   // cleared before the first visited key tile (kr.lo), not on key tile zero
   f32x16 acc[D / 32];
 #pragma unroll
@@ -394,10 +433,16 @@ bwd_dq_kernel(AttnArgs a) {
         mma(dp, rrd.read(vs, 32 * kt, ss), df[ss]);
       }
       if (edge) {
-        const int mb = mpos - (kb * BN + 32 * kt + 4 * half);
+        const uint32_t mb = mpos - (uint32_t)(kb * BN + 32 * kt + 4 * half);
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if ((uint32_t)(mb - (8 * (r >> 2) + (r & 3))) >= mlim) s[r] = -INFINITY;
+          if (mb - (uint32_t)(8 * (r >> 2) + (r & 3)) >= mlim) s[r] = -INFINITY;
+        if (rw.pad_keys && kb * BN + BN > it.lk) {  // two-sided: the keys past L_k
+          const int jb = kb * BN + 32 * kt + 4 * half;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (jb + 8 * (r >> 2) + (r & 3) >= it.lk) s[r] = -INFINITY;
+        }
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -490,7 +535,7 @@ bwd_dkdv_kernel(AttnArgs a) {
     dva[dt] = f32x16{};
   }
   const float c = a.scale * kLog2e;
-  const uint32_t wlim = (uint32_t)a.window;
+  const PairWindow pw = pair_window(lk, a.window, causal);
   const T* __restrict__ Qg = static_cast<const T*>(a.q);
   const T* __restrict__ Dg = static_cast<const T*>(a.dout);
 
@@ -546,13 +591,13 @@ bwd_dkdv_kernel(AttnArgs a) {
     }
     if (edge) {
       // row r holds query ib + 8(r/4) + r%4: visible iff it is a real row
-      // (< L_q) and, causal, (unsigned)(p - j) < window with p = query + L_k - L_q
+      // (< L_q) and inside the window (pair_window) at p = query + L_k - L_q
       const int ib = qb * BM + 32 * mh + 4 * half;
-      const int mb = ib + (lk - lq) - j;
+      const int mb = ib + (lk - lq) - j + pw.off;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int off = 8 * (r >> 2) + (r & 3);
-        if ((ib + off >= lq) | (causal & ((uint32_t)(mb + off) >= wlim))) s[r] = -INFINITY;
+        if ((ib + off >= lq) | (pw.windowed & ((uint32_t)(mb + off) >= pw.lim))) s[r] = -INFINITY;
       }
     }
 #pragma unroll
@@ -685,7 +730,7 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
     dva[dt] = f32x16{};
   }
   const float c = a.scale * kLog2e;
-  const uint32_t wlim = (uint32_t)a.window;
+  const PairWindow pw = pair_window(lk, a.window, causal);
   const T* __restrict__ Qg = static_cast<const T*>(a.q);
   const T* __restrict__ Dg = static_cast<const T*>(a.dout);
 
@@ -737,11 +782,11 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
     }
     if (edge) {
       const int ib = qb * BM + 4 * half;
-      const int mb = ib + (lk - lq) - j;
+      const int mb = ib + (lk - lq) - j + pw.off;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int off = 8 * (r >> 2) + (r & 3);
-        if ((ib + off >= lq) | (causal & ((uint32_t)(mb + off) >= wlim))) s[r] = -INFINITY;
+        if ((ib + off >= lq) | (pw.windowed & ((uint32_t)(mb + off) >= pw.lim))) s[r] = -INFINITY;
       }
     }
 #pragma unroll
@@ -832,7 +877,7 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
   }
   const float c = a.scale * kLog2e;
   const bool causal = a.causal != 0;
-  const uint32_t wlim = (uint32_t)a.window;
+  const PairWindow pw = pair_window(lk, a.window, causal);
   const T* __restrict__ Qg = static_cast<const T*>(a.q);
   const T* __restrict__ Dg = static_cast<const T*>(a.dout);
 
@@ -880,7 +925,7 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
     const int qb = qr.lo + t % nq;
     const bool more = t + 1 < steps;
     if (more) issue(t + 1);
-    const bool edge = causal && !tile_is_full(sg, qb, BM, kb, BN);
+    const bool edge = pw.windowed && !tile_is_full(sg, qb, BM, kb, BN);
 #pragma unroll
     for (int mt = 0; mt < BM / 32; ++mt) {
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -891,11 +936,11 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
       }
       if (edge) {
         // row r holds query qb*BM + 32mt + 8(r/4) + 4half + r%4; visible iff
-        // (unsigned)(p - j) < window with p = query + L_k - L_q
-        const int mb = qb * BM + 32 * mt + 4 * half + (lk - lq) - j;
+        // inside the window (pair_window) at p = query + L_k - L_q
+        const int mb = qb * BM + 32 * mt + 4 * half + (lk - lq) - j + pw.off;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if ((uint32_t)(mb + 8 * (r >> 2) + (r & 3)) >= wlim) s[r] = -INFINITY;
+          if ((uint32_t)(mb + 8 * (r >> 2) + (r & 3)) >= pw.lim) s[r] = -INFINITY;
       }
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {

@@ -11,7 +11,8 @@
 //
 // Geometry of one sequence: L_q queries, L_k keys, delta = L_k - L_q >= 0;
 // query i sits at key position p = i + delta. Causal cell (i, j) is visible
-// iff j <= p and p - j < window; non-causal cells are all visible.
+// iff j <= p and p - j < window. Without the causal mask the window is
+// two-sided: visible iff |p - j| < window (window >= L_k: every cell).
 #pragma once
 
 #include <stdint.h>
@@ -71,13 +72,28 @@ SWA_HD TileRange query_tile_keys(const SeqGeom& s, int32_t qb, int32_t bm, int32
       }
     }
   } else {
-    jlo = 0;
-    jhi = s.lk - 1;
-    r.lo = 0;
+    // two-sided: keys within window - 1 of some row's position
+    const int64_t pmin = i0 + s.delta(), pmax = i1 + s.delta();
+    jlo = pmin - s.window + 1;
+    if (jlo < 0) jlo = 0;
+    jhi = pmax + s.window - 1;
+    if (jhi > s.lk - 1) jhi = s.lk - 1;
+    if (jlo > jhi) return r;
+    r.lo = (int32_t)(jlo / bn);
     r.hi = (int32_t)(jhi / bn);
-    if (i1 - i0 + 1 == bm && s.lk / bn - 1 >= 0) {
-      r.full_lo = 0;
-      r.full_hi = (int32_t)(s.lk / bn - 1);
+    // full tile kb: kb*bn >= pmax - window + 1, kb*bn + bn - 1 <= pmin + window - 1,
+    // kb*bn + bn <= lk, and the query tile has all bm rows
+    if (i1 - i0 + 1 == bm) {
+      int64_t flo = -floor_div(-(pmax - s.window + 1), bn);  // ceil
+      int64_t fhi = floor_div(pmin + s.window - bn, bn);
+      const int64_t fhi_bound = s.lk / bn - 1;
+      if (fhi > fhi_bound) fhi = fhi_bound;
+      if (flo < r.lo) flo = r.lo;
+      if (fhi > r.hi) fhi = r.hi;
+      if (flo <= fhi) {
+        r.full_lo = (int32_t)flo;
+        r.full_hi = (int32_t)fhi;
+      }
     }
   }
   return r;
@@ -99,8 +115,11 @@ SWA_HD TileRange key_tile_queries(const SeqGeom& s, int32_t kb, int32_t bn, int3
     ihi = j1 - s.delta() + s.window - 1;
     if (ihi > s.lq - 1) ihi = s.lq - 1;
   } else {
-    ilo = 0;
-    ihi = s.lq - 1;
+    // two-sided: p within window - 1 of some key of the tile
+    ilo = j0 - s.window + 1 - s.delta();
+    if (ilo < 0) ilo = 0;
+    ihi = j1 + s.window - 1 - s.delta();
+    if (ihi > s.lq - 1) ihi = s.lq - 1;
   }
   if (ilo > ihi) return r;
   r.lo = (int32_t)(ilo / bm);
@@ -122,8 +141,8 @@ SWA_HD int32_t xcd_remap(int32_t id, int32_t n, int32_t nxcd = 8) {
 // Per-cell visibility, used inside edge tiles.
 SWA_HD bool cell_visible(const SeqGeom& s, int64_t i, int64_t j) {
   if (i >= s.lq || j >= s.lk) return false;
-  if (!s.causal) return true;
   const int64_t p = i + s.delta();
+  if (!s.causal) return p - j < s.window && j - p < s.window;
   return j <= p && p - j < s.window;
 }
 
@@ -136,7 +155,8 @@ SWA_HD bool tile_full_i32(int32_t lq, int32_t lk, int32_t window, bool causal, i
                           int32_t bm, int32_t kb, int32_t bn) {
   const int32_t i0 = qb * bm, j0 = kb * bn, delta = lk - lq;
   if (i0 + bm > lq || j0 + bn > lk) return false;
-  if (!causal) return true;
+  // differences of positions lie in (-2^31, 2^31): no overflow
+  if (!causal) return (i0 + bm - 1 + delta) - j0 < window && (j0 + bn - 1) - (i0 + delta) < window;
   return j0 + bn - 1 <= i0 + delta && (i0 + bm - 1 + delta) - j0 < window;
 }
 
@@ -149,11 +169,13 @@ SWA_HD bool tile_full_i32(int32_t lq, int32_t lk, int32_t window, bool causal, i
 SWA_HD bool block_masked(int32_t lq, int32_t lk, int32_t window, bool causal, int32_t a, int32_t rows,
                          int32_t b, int32_t cols) {
   if (a >= lq || b >= lk) return true;
-  if (!causal) return false;
   const int64_t delta = (int64_t)lk - lq;
   const int64_t p_last = (int64_t)(a + rows - 1 < lq - 1 ? a + rows - 1 : lq - 1) + delta;
   const int64_t p_first = (int64_t)a + delta;
-  return (int64_t)b > p_last || p_first - ((int64_t)b + cols - 1) >= (int64_t)window;
+  const int64_t b_last = (int64_t)(b + cols - 1 < lk - 1 ? b + cols - 1 : lk - 1);
+  const bool too_old = p_first - b_last >= (int64_t)window;  // every key older than every row's window
+  if (!causal) return too_old || (int64_t)b - p_last >= (int64_t)window;
+  return (int64_t)b > p_last || too_old;
 }
 
 // Is tile (query tile qb, key tile kb) free of masked cells?

@@ -14,7 +14,6 @@ int main() {
       for (int w : wins)
         for (int causal = 0; causal <= 1; ++causal) {
           const int lk = lq + dl;
-          if (!causal && w < lk) continue;
           const swa::SeqGeom g{lq, lk, w, causal != 0};
           for (int bm : {16, 32, 64})
             for (int bn : {16, 32, 64, 128})
@@ -38,7 +37,6 @@ int main() {
       for (int w : wins)
         for (int causal = 0; causal <= 1; ++causal) {
           const int lk = lq + dl;
-          if (!causal && w < lk) continue;
           const swa::SeqGeom g{lq, lk, w, causal != 0};
           for (int rows : {32})
             for (int cols : {32, 64})

@@ -46,7 +46,9 @@ def good(**kw):
     (dict(head_dim=96), 4),
     (dict(head_dim=512), 4),
     (dict(dtype=7), 4),
-    (dict(causal=False, window=50), 4),
+    (dict(causal=False, window=50), 0),     # two-sided window
+    (dict(heads_q=1, heads_kv=1, total_q=2**30 + 8, total_k=2**30 + 8, max_seqlen_q=2**30 + 8,
+          max_seqlen_k=2**30 + 8, causal=False, window=50), 4),  # two-sided beyond 2^30 keys
     (dict(causal=False, window=100), 0),
     (dict(window=swa.INT32_MAX), 0),
     (dict(dtype=swa.ATTN_F32, head_dim=64), 0),
@@ -101,7 +103,9 @@ def test_backward_refuses_before_launch():
     bad = list(args)
     bad[8] = None  # dq
     assert L.attn_bwd(ctypes.byref(p), *bad, 16, need, None) == 1
-    assert L.attn_bwd(ctypes.byref(good(causal=False, window=3)), *args, 16, need, None) == 4
+    # refused before any launch (the pointers are not device memory)
+    assert L.attn_bwd(ctypes.byref(good(head_dim=96)), *args, 16, need, None) == 4
+    assert L.attn_bwd(ctypes.byref(good(head_dim=256, dtype=swa.ATTN_F32)), *args, 16, need, None) == 4
     assert swa.workspace_bytes(good(window=0)) == 0
 
 

@@ -60,6 +60,10 @@ SMALL = [
     ([300, 1, 517, 64], None, 8, 4, 256, 129, True, "bf16"),  # head_dim 256: ragged, windowed
     ([100, 40], [700, 300], 4, 2, 256, 16, True, "fp16"),   # L_q < L_k at 256
     ([200, 333], None, 4, 2, 256, INT32_MAX, False, "bf16"),  # full attention at 256
+    ([300, 1, 517, 64], None, 8, 2, 128, 65, False, "bf16"),  # two-sided windows
+    ([100, 40], [700, 300], 4, 1, 64, 16, False, "f32"),
+    ([257, 130], None, 4, 2, 256, 100, False, "fp16"),
+    ([200, 333], None, 4, 2, 128, 200, False, "f32"),
 ]
 
 
@@ -88,6 +92,18 @@ def test_window_one_closed_form(dt, d):
             assert np.array_equal(o[q0:q0 + lq], kv)
         else:
             assert np.all(np.abs(o[q0:q0 + lq] - kv) <= 1e-6 * np.maximum(1.0, np.abs(kv)))
+
+
+def test_two_sided_window_one_closed_form():
+    w = small_case([300, 130], [300, 200], heads_q=4, heads_kv=2, head_dim=128, window=1, causal=False,
+                   dtype="bf16", do_scale=0.1, seed=35)
+    x, dev, got = _run_full(w, zero=("dq", "dk"))
+    o = H.host64(got["o"])
+    for b in range(w.batch):
+        q0, k0 = int(x["cu_q"][b]), int(x["cu_k"][b])
+        lq, lk = w.lengths_q[b], w.lengths_k[b]
+        kv = np.repeat(x["v"][k0 + lk - lq:k0 + lk], 2, axis=1).astype(np.float64)
+        assert np.array_equal(o[q0:q0 + lq], kv)
 
 
 def test_wide_window_bitwise_equals_causal():

@@ -29,8 +29,8 @@ def _grid(n=60, seed=2024):
         lq = [int(x) for x in rng.integers(1, 300, nseq)]
         shorter = rng.random() < 0.35          # queries shorter than keys
         lk = [q + int(rng.integers(1, 200)) for q in lq] if shorter else None
-        causal = rng.random() < 0.8
-        window = int(WINDOWS[rng.integers(len(WINDOWS))]) if causal else INT32_MAX
+        causal = rng.random() < 0.7
+        window = int(WINDOWS[rng.integers(len(WINDOWS))])   # without causal: two-sided
         cases.append((tuple(lq), None if lk is None else tuple(lk), hkv * g, hkv, d, window, causal, dt))
     return cases
 

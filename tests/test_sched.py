@@ -35,6 +35,9 @@ CASES = [
     (300, 300, 128, True), (300, 300, 129, True), (300, 300, INT32_MAX, True),
     (100, 700, 64, True), (5, 400, 3, True), (0, 50, 8, True), (77, 77, 77, True),
     (200, 260, INT32_MAX, False), (129, 129, 1000, True), (64, 64, 64, True),
+    # two-sided windows (no causal mask)
+    (300, 300, 1, False), (300, 300, 64, False), (300, 300, 129, False), (100, 700, 64, False),
+    (5, 400, 3, False), (200, 260, 100, False), (129, 129, 128, False),
 ]
 
 
