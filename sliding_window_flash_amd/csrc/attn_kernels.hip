@@ -234,7 +234,14 @@ fwd_kernel(AttnArgs a) {
 
   TileLoader<T, BN, D, NT> kvld;
   kvld.init((uint32_t)(kstride * sizeof(T)), w, lane);
-  if (kr.lo <= kr.hi) fill_kv(kvld, st0, K, V, kstride, kr.lo, it.lk);
+  // an odd number of tiles starts in stage 1, so that the loop below runs
+  // whole (stage 0, stage 1) pairs: with no exit between the two steps the
+  // accumulators keep their registers across the loop (no copies)
+  const int ntiles = kr.hi - kr.lo + 1;
+  if (ntiles > 0) {
+    if (ntiles & 1) fill_kv(kvld, st1, K, V, kstride, kr.lo, it.lk);
+    else fill_kv(kvld, st0, K, V, kstride, kr.lo, it.lk);
+  }
   __syncthreads();
 
   // One key tile; `stage` (compile time) selects the LDS stage it reads.
@@ -311,11 +318,11 @@ fwd_kernel(AttnArgs a) {
     lsum += rs;
     __syncthreads();
   };
-  for (int kb = kr.lo; kb <= kr.hi;) {
+  int kb = kr.lo;
+  if (ntiles & 1) step(ic<1>{}, kb++);
+  for (; kb <= kr.hi; kb += 2) {
     step(ic<0>{}, kb);
-    if (++kb > kr.hi) break;
-    step(ic<1>{}, kb);
-    ++kb;
+    step(ic<1>{}, kb + 1);
   }
 
   const float ltot = sum_halves(lsum);
@@ -410,7 +417,14 @@ bwd_dq_kernel(AttnArgs a) {
 
   TileLoader<T, BN, D, NT> kvld;
   kvld.init((uint32_t)(kstride * sizeof(T)), w, lane);
-  if (kr.lo <= kr.hi) fill_kv(kvld, st0, K, V, kstride, kr.lo, it.lk);
+  // an odd number of tiles starts in stage 1, so that the loop below runs
+  // whole (stage 0, stage 1) pairs: with no exit between the two steps the
+  // accumulators keep their registers across the loop (no copies)
+  const int ntiles = kr.hi - kr.lo + 1;
+  if (ntiles > 0) {
+    if (ntiles & 1) fill_kv(kvld, st1, K, V, kstride, kr.lo, it.lk);
+    else fill_kv(kvld, st0, K, V, kstride, kr.lo, it.lk);
+  }
   __syncthreads();
 
   auto step = [&](auto stage_c, int kb) {
@@ -458,11 +472,11 @@ bwd_dq_kernel(AttnArgs a) {
     }
     __syncthreads();
   };
-  for (int kb = kr.lo; kb <= kr.hi;) {
+  int kb = kr.lo;
+  if (ntiles & 1) step(ic<1>{}, kb++);
+  for (; kb <= kr.hi; kb += 2) {
     step(ic<0>{}, kb);
-    if (++kb > kr.hi) break;
-    step(ic<1>{}, kb);
-    ++kb;
+    step(ic<1>{}, kb + 1);
   }
   if (row_ok) {
     T* row = static_cast<T*>(a.dq) + (int64_t)(it.q0 + i) * qstride + it.h * D;
@@ -565,7 +579,8 @@ bwd_dkdv_kernel(AttnArgs a) {
       ++nh;
     }
   };
-  if (steps > 0) fill(st0);
+  // odd step counts start in stage 1: the loop below runs whole stage pairs
+  if (steps > 0) fill(steps & 1 ? st1 : st0);
   __syncthreads();
 
   int qb = qr.lo;  // query tile of the current step
@@ -626,11 +641,11 @@ bwd_dkdv_kernel(AttnArgs a) {
     if (++qb > qr.hi) qb = qr.lo;
     __syncthreads();
   };
-  for (int t = 0; t < steps;) {
+  int t = 0;
+  if (steps & 1) step(ic<1>{}, t++);
+  for (; t < steps; t += 2) {
     step(ic<0>{}, t);
-    if (++t >= steps) break;
-    step(ic<1>{}, t);
-    ++t;
+    step(ic<1>{}, t + 1);
   }
 
   // Sum the two query halves: half 1 hands its dK partial to half 0 and half 0
@@ -757,7 +772,8 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
       ++nh;
     }
   };
-  if (steps > 0) fill(st0);
+  // odd step counts start in stage 1: the loop below runs whole stage pairs
+  if (steps > 0) fill(steps & 1 ? st1 : st0);
   __syncthreads();
 
   int qb = qr.lo;
@@ -815,11 +831,11 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
     if (++qb > qr.hi) qb = qr.lo;
     __syncthreads();
   };
-  for (int t = 0; t < steps;) {
+  int t = 0;
+  if (steps & 1) step(ic<1>{}, t++);
+  for (; t < steps; t += 2) {
     step(ic<0>{}, t);
-    if (++t >= steps) break;
-    step(ic<1>{}, t);
-    ++t;
+    step(ic<1>{}, t + 1);
   }
   if (key_ok) {
     const int64_t roff = (int64_t)(k0 + j) * kstride + g * D + DH * dh;
