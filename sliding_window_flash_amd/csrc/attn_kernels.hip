@@ -250,13 +250,11 @@ fwd_kernel(AttnArgs a) {
     const char* ks = stage ? st1 : st0;
     const char* vs = ks + KTile::kBytes;
     if (kb < kr.hi) fill_kv(kvld, stage ? st0 : st1, K, V, kstride, kb + 1, it.lk);
-    // an edge tile whose cells are all masked for this wave's 32 rows adds
-    // nothing (P = 0): the wave skips it but still loads its share and syncs
+    // Edge tiles are masked cell by cell. A wave whose 32 rows see none of an
+    // edge tile's keys still computes it (P = 0): an early exit from the step
+    // makes the compiler copy the O accumulator at every step, which costs more
+    // than the few all-masked wave tiles.
     const bool edge = !(kr.full_lo <= kb && kb <= kr.full_hi);
-    if (edge && block_masked(it.lq, it.lk, a.window, a.causal != 0, it.qb * BM + 32 * w, 32, kb * BN, BN)) {
-      __syncthreads();
-      return;
-    }
     f32x16 s[BN / 32];
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt) {
@@ -484,6 +482,23 @@ bwd_dq_kernel(AttnArgs a) {
   }
 }
 
+// fp32 accumulator blocks through LDS in their register layout: element r of
+// block dt of lane l at float index l + 64 (16 dt + r)
+template <int NB>
+__device__ __forceinline__ void hand_over(float* red, const f32x16 (&acc)[NB], int lane) {
+#pragma unroll
+  for (int dt = 0; dt < NB; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[lane + (dt * 16 + r) * 64] = acc[dt][r];
+}
+template <int NB>
+__device__ __forceinline__ void take_over(const float* red, f32x16 (&acc)[NB], int lane) {
+#pragma unroll
+  for (int dt = 0; dt < NB; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] += red[lane + (dt * 16 + r) * 64];
+}
+
 // ---------------------------------------------------------- backward: dK, dV
 // One workgroup per (KV head, sequence, key tile of BN = 128 keys), 8 waves:
 // wave w owns keys 32*(w%4) .. +31 and, in every BM = 64-row query step, the
@@ -653,26 +668,16 @@ bwd_dkdv_kernel(AttnArgs a) {
   // (one 32-key block per wave, reusing the K/V tiles and the stages).
   float* red_k = reinterpret_cast<float*>((kt < 2 ? klds : vlds) + (kt & 1) * kRedBlock);
   float* red_v = reinterpret_cast<float*>((kt < 2 ? st0 : st1) + (kt & 1) * kRedBlock);
+  // mh is wave-uniform: one branch around each whole loop (a branch per
+  // element would make the compiler copy the accumulators at every one)
   if (steps > 0) {
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int o = lane + (dt * 16 + r) * 64;
-        if (mh == 1) red_k[o] = dka[dt][r];
-        else red_v[o] = dva[dt][r];
-      }
+    if (mh == 1) hand_over(red_k, dka, lane);
+    else hand_over(red_v, dva, lane);
   }
   __syncthreads();
   if (steps > 0) {
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int o = lane + (dt * 16 + r) * 64;
-        if (mh == 0) dka[dt][r] += red_k[o];
-        else dva[dt][r] += red_v[o];
-      }
+    if (mh == 0) take_over(red_k, dka, lane);
+    else take_over(red_v, dva, lane);
   }
   if (key_ok) {
     const int64_t roff = (int64_t)(k0 + j) * kstride + g * D;
