@@ -97,15 +97,19 @@ struct TileStage {
   }
 };
 
+// Key tile kb of one sequence (K or V rows) into an LDS tile.
+template <typename T, int BN, int D, int NT>
+__device__ __forceinline__ void fill_tile(const TileLoader<T, BN, D, NT>& ld, char* dst, const T* X, int64_t kstride,
+                                          int kb, int lk) {
+  const int kvalid = min(BN, lk - kb * BN);
+  ld.issue(dst, X + (int64_t)kb * BN * kstride, (uint32_t)(kstride * sizeof(T)), kvalid);
+}
 // K and V key tile kb of one sequence into an LDS stage (K tile, then V tile).
 template <typename T, int BN, int D, int NT>
 __device__ __forceinline__ void fill_kv(const TileLoader<T, BN, D, NT>& ld, char* st, const T* K, const T* V,
                                         int64_t kstride, int kb, int lk) {
-  const int kvalid = min(BN, lk - kb * BN);
-  const int64_t o = (int64_t)kb * BN * kstride;
-  const uint32_t sb = (uint32_t)(kstride * sizeof(T));
-  ld.issue(st, K + o, sb, kvalid);
-  ld.issue(st + LdsTile<T, BN, D>::kBytes, V + o, sb, kvalid);
+  fill_tile(ld, st, K, kstride, kb, lk);
+  fill_tile(ld, st + LdsTile<T, BN, D>::kBytes, V, kstride, kb, lk);
 }
 
 struct QueryItem {
@@ -189,6 +193,7 @@ template <typename T, int D, int BM, int BN>
 __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
 fwd_kernel(AttnArgs a) {
   constexpr int NT = BM * 2;
+  constexpr bool kPipe = sizeof(T) == 2 && D <= 128;  // software-pipelined loop (see below)
   using KTile = LdsTile<T, BN, D>;
   // two stages (K tile then V tile each), separate arrays so that reading one
   // need not wait for the asynchronous fill of the other
@@ -237,6 +242,111 @@ fwd_kernel(AttnArgs a) {
   // an odd number of tiles starts in stage 1, so that the loop below runs
   // whole (stage 0, stage 1) pairs: with no exit between the two steps the
   // accumulators keep their registers across the loop (no copies)
+  const int ntiles = kr.hi - kr.lo + 1;
+  if constexpr (kPipe) {
+    // Software pipeline over key tiles: step j puts tile j+1's scores on the
+    // MFMA unit while the VALU turns tile j's scores into probabilities, then
+    // adds tile j's P V. K and V tiles rotate through their own two stages:
+    // K_{j+2} and V_{j+1} load during step j. Tile j sits in stage (j + p) & 1
+    // with p = (ntiles - 1) & 1, so the loop runs whole stage pairs and the
+    // last tile, which has no successor, is in stage 0.
+    const int p = (ntiles - 1) & 1;
+    if (ntiles > 0) {
+      fill_kv(kvld, p ? st1 : st0, K, V, kstride, kr.lo, it.lk);
+      if (ntiles > 1) fill_tile(kvld, p ? st0 : st1, K, kstride, kr.lo + 1, it.lk);
+    }
+    __syncthreads();
+    auto qk = [&](f32x16 (&s)[BN / 32], const char* ks) __attribute__((always_inline)) {
+#pragma unroll
+      for (int kt = 0; kt < BN / 32; ++kt) {
+        s[kt] = f32x16{};
+#pragma unroll
+        for (int ss = 0; ss < D / 16; ++ss) mma(s[kt], rrd.read(ks, 32 * kt, ss), qf[ss]);
+      }
+    };
+    // one step: tile kb's scores in `cur` (K and V in stage `stage`); with a
+    // successor, its scores go to `nxt` from the other stage's K tile
+    auto pstep = [&](auto stage_c, auto next_c, int kb, f32x16 (&cur)[BN / 32], f32x16 (&nxt)[BN / 32])
+        __attribute__((always_inline)) {
+      constexpr int stage = decltype(stage_c)::value;
+      constexpr bool has_next = decltype(next_c)::value;
+      char* here = stage ? st1 : st0;
+      char* other = stage ? st0 : st1;
+      if constexpr (has_next) {
+        if (kb + 2 <= kr.hi) fill_tile(kvld, here, K, kstride, kb + 2, it.lk);
+        fill_tile(kvld, other + KTile::kBytes, V, kstride, kb + 1, it.lk);
+      }
+      if (!(kr.full_lo <= kb && kb <= kr.full_hi)) {  // edge tile: mask cell by cell
+        const uint32_t mb = mpos - (uint32_t)(kb * BN + 4 * half);
+#pragma unroll
+        for (int kt = 0; kt < BN / 32; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (mb - (uint32_t)(32 * kt + 8 * (r >> 2) + (r & 3)) >= mlim) cur[kt][r] = -INFINITY;
+        if (rw.pad_keys && kb * BN + BN > it.lk) {  // two-sided: the keys past L_k
+          const int jb = kb * BN + 4 * half;
+#pragma unroll
+          for (int kt = 0; kt < BN / 32; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (jb + 32 * kt + 8 * (r >> 2) + (r & 3) >= it.lk) cur[kt][r] = -INFINITY;
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < BN / 32; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kt][r]);
+      mx = max_halves(mx);
+      const float mxs = mx == -INFINITY ? -INFINITY : mx * c;
+      const bool grow = mxs > m + kRescaleSlack;
+      if (__any(grow)) {
+        const float mnew = grow ? mxs : m;
+        const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mnew);
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+        m = mnew;
+      }
+      if constexpr (has_next) qk(nxt, other);
+      const float mu = m == -INFINITY ? 0.f : m;
+      Frag<T> pf[BN / 16];
+      float rs = 0.f;
+#pragma unroll
+      for (int u = 0; u < BN / 16; ++u) {
+        f32x16& sv = cur[u >> 1];
+#pragma unroll
+        for (int r = 8 * (u & 1); r < 8 * (u & 1) + 8; ++r) sv[r] = fast_exp2(fmaf(sv[r], c, -mu));
+        pf[u] = acc_frag<T>(sv, u & 1);
+        rs = frag_sum(pf[u], rs);  // over the rounded P that the MFMA multiplies
+      }
+      lsum += rs;
+#pragma unroll
+      for (int u = 0; u < BN / 16; ++u)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) mma(acc[dt], crd.read(here + KTile::kBytes, 16 * u, dt), pf[u]);
+      if constexpr (has_next) __syncthreads();
+    };
+    if (ntiles > 0) {
+      f32x16 sa[BN / 32], sb[BN / 32];
+      int kb = kr.lo;
+      // the first step refills the first tile's K stage: every wave must have
+      // read it first (later steps meet a barrier between the two)
+      if (p) {
+        qk(sb, st1);
+        __syncthreads();
+        pstep(ic<1>{}, std::true_type{}, kb++, sb, sa);
+      } else {
+        qk(sa, st0);
+        __syncthreads();
+      }
+      for (; kb < kr.hi; kb += 2) {
+        pstep(ic<0>{}, std::true_type{}, kb, sa, sb);
+        pstep(ic<1>{}, std::true_type{}, kb + 1, sb, sa);
+      }
+      pstep(ic<0>{}, std::false_type{}, kb, sa, sb);
+    }
+  } else {
   const int ntiles = kr.hi - kr.lo + 1;
   if (ntiles > 0) {
     if (ntiles & 1) fill_kv(kvld, st1, K, V, kstride, kr.lo, it.lk);
@@ -321,6 +431,8 @@ fwd_kernel(AttnArgs a) {
   for (; kb <= kr.hi; kb += 2) {
     step(ic<0>{}, kb);
     step(ic<1>{}, kb + 1);
+  }
+
   }
 
   const float ltot = sum_halves(lsum);
