@@ -34,8 +34,19 @@ G = Hq / Hkv), query row i and key j:
                (The lab's "What did fixing it take?" section: the backward
                must give every query and key its gradient, including key
                blocks no query visits, whose gradient is zero.)
-  empty rows   a query with no visible key (unreachable when L_q <= L_k) gets
-               O = 0, LSE = -inf, dQ = 0.
+  empty rows   a query with no visible key gets O = 0, LSE = -inf, dQ = 0
+               (unreachable without a mask when L_q <= L_k).
+  mask         optional, combined with the window. The lab's "What's not
+               proved" list says a window combined with an arbitrary mask still
+               falls back to the full score matrix in training; its record
+               entry on backward memory measures against the boolean mask that
+               mlx-lm passes. Reading used: the arbitrary mask is such a
+               boolean matrix, one per sequence and shared by every head, and
+               a cell is visible iff the window shows it AND the mask allows
+               it. Here ``mask`` is boolean [T_q, W] with W >= every L_k: row
+               t is packed query token t, column j is key j of that token's
+               sequence (0-based within the sequence); columns past L_k are
+               ignored.
 
 The full L_q x L_k masked matrix is built for each (sequence, head), a panel of
 at most ``panel_rows`` query rows at a time, so memory stays bounded while
@@ -85,14 +96,25 @@ def check_host_ram(nbytes: int, ceiling: Optional[int] = None) -> None:
 
 
 def visible_cells(lq: int, lk: int, window: int, causal: bool,
-                  rows: Optional[np.ndarray] = None) -> np.ndarray:
-    """Boolean [len(rows), lk] mask of visible (query, key) cells."""
+                  rows: Optional[np.ndarray] = None, allowed: Optional[np.ndarray] = None) -> np.ndarray:
+    """Boolean [len(rows), lk] mask of visible (query, key) cells. ``allowed``,
+    if given, is the caller's mask for these rows ([len(rows), >= lk])."""
     i = np.arange(lq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
     j = np.arange(lk, dtype=np.int64)
     pos = (i + (lk - lq))[:, None]
     if not causal:
-        return np.abs(pos - j[None, :]) < window
-    return (j[None, :] <= pos) & (pos - j[None, :] < window)
+        vis = np.abs(pos - j[None, :]) < window
+    else:
+        vis = (j[None, :] <= pos) & (pos - j[None, :] < window)
+    if allowed is not None:
+        vis = vis & np.asarray(allowed, dtype=bool)[:, :lk]
+    return vis
+
+
+def _mask_rows(mask, q0, rows):
+    """The caller's mask rows for query rows ``rows`` of the sequence starting
+    at packed token q0 (None without a mask)."""
+    return None if mask is None else mask[q0 + np.asarray(rows, dtype=np.int64)]
 
 
 def _panel(qh, kg, vg, doh, mask, scale, with_backward):
@@ -134,7 +156,7 @@ def _check_shapes(q, k, v, do, cu_q, cu_k):
 def sdpa_reference(q, k, v, do, cu_q, cu_k, scale: float, window: int, causal: bool, *,
                    with_backward: bool = True, panel_rows: int = 512,
                    ram_ceiling: Optional[int] = None, heads: Optional[Iterable[int]] = None,
-                   query_rows: Optional[tuple] = None) -> dict:
+                   query_rows: Optional[tuple] = None, mask: Optional[np.ndarray] = None) -> dict:
     """Full forward (and backward) over a packed batch.
 
     q, do: [T_q, Hq, d]; k, v: [T_k, Hkv, d]; cu_q, cu_k: [B+1] offsets.
@@ -144,7 +166,7 @@ def sdpa_reference(q, k, v, do, cu_q, cu_k, scale: float, window: int, causal: b
     ``heads`` and ``query_rows`` = (r0, r1) restrict the work to those query
     heads and to rows r0 <= i < r1 of every sequence (a timing sample; rows
     and heads left out stay at their initial values, and dK/dV then hold only
-    the contributions of the rows computed).
+    the contributions of the rows computed). ``mask``: see the module header.
     """
     tq, tk, hq, hkv, d = _check_shapes(q, k, v, do if with_backward else None, cu_q, cu_k)
     grp = hq // hkv
@@ -173,10 +195,11 @@ def sdpa_reference(q, k, v, do, cu_q, cu_k, scale: float, window: int, causal: b
             vg = _as64(v[k0:k1, g, :])
             for r0 in range(row_lo, row_hi, rows_per):
                 r1 = min(row_hi, r0 + rows_per)
-                mask = visible_cells(lq, lk, window, causal, np.arange(r0, r1))
+                rr = np.arange(r0, r1)
+                vis = visible_cells(lq, lk, window, causal, rr, _mask_rows(mask, q0, rr))
                 qh = _as64(q[q0 + r0:q0 + r1, h, :])
                 doh = _as64(do[q0 + r0:q0 + r1, h, :]) if with_backward else None
-                res = _panel(qh, kg, vg, doh, mask, scale, with_backward)
+                res = _panel(qh, kg, vg, doh, vis, scale, with_backward)
                 o[q0 + r0:q0 + r1, h, :] = res["o"]
                 lse[h, q0 + r0:q0 + r1] = res["lse"]
                 if with_backward:
@@ -194,7 +217,7 @@ def _locate(cu, t):
 
 
 def sdpa_query_rows(q, k, v, do, cu_q, cu_k, scale, window, causal,
-                    tokens: Iterable[int], heads: Iterable[int]) -> dict:
+                    tokens: Iterable[int], heads: Iterable[int], mask: Optional[np.ndarray] = None) -> dict:
     """O, LSE, D and dQ for selected (packed query token, query head) rows.
 
     Each row is the same plain definition as :func:`sdpa_reference`, built as a
@@ -209,8 +232,9 @@ def sdpa_query_rows(q, k, v, do, cu_q, cu_k, scale, window, causal,
         lq = int(cu_q[b + 1] - cu_q[b])
         g = h // grp
         kg, vg = _as64(k[k0:k1, g, :]), _as64(v[k0:k1, g, :])
-        mask = visible_cells(lq, k1 - k0, window, causal, np.array([i]))
-        r = _panel(_as64(q[t:t + 1, h, :]), kg, vg, _as64(do[t:t + 1, h, :]), mask, scale, True)
+        vis = visible_cells(lq, k1 - k0, window, causal, np.array([i]),
+                            _mask_rows(mask, int(cu_q[b]), [i]))
+        r = _panel(_as64(q[t:t + 1, h, :]), kg, vg, _as64(do[t:t + 1, h, :]), vis, scale, True)
         res["o"].append(r["o"][0])
         res["lse"].append(r["lse"][0])
         res["delta"].append(r["delta"][0])
@@ -220,7 +244,7 @@ def sdpa_query_rows(q, k, v, do, cu_q, cu_k, scale, window, causal,
 
 def sdpa_key_rows(q, k, v, do, cu_q, cu_k, scale, window, causal,
                   tokens: Iterable[int], kv_heads: Iterable[int], *,
-                  panel_rows: int = 512) -> dict:
+                  panel_rows: int = 512, mask: Optional[np.ndarray] = None) -> dict:
     """dK and dV for selected (packed key token, KV head) rows.
 
     Every query row that sees the key is rebuilt in full (its whole masked
@@ -237,7 +261,8 @@ def sdpa_key_rows(q, k, v, do, cu_q, cu_k, scale, window, causal,
         kg, vg = _as64(k[k0:k1, g, :]), _as64(v[k0:k1, g, :])
         # the column of the mask for key j, built 1024 rows at a time
         col = np.concatenate([
-            visible_cells(lq, lk, window, causal, np.arange(r, min(lq, r + 1024)))[:, j]
+            visible_cells(lq, lk, window, causal, np.arange(r, min(lq, r + 1024)),
+                          _mask_rows(mask, q0, np.arange(r, min(lq, r + 1024))))[:, j]
             for r in range(0, lq, 1024)]) if lq else np.zeros(0, bool)
         rows = np.nonzero(col)[0]
         dk_j = np.zeros(k.shape[2], F64)
@@ -245,10 +270,10 @@ def sdpa_key_rows(q, k, v, do, cu_q, cu_k, scale, window, causal,
         for h in range(g * grp, (g + 1) * grp):
             for r0 in range(0, rows.size, panel_rows):
                 rr = rows[r0:r0 + panel_rows]
-                mask = visible_cells(lq, lk, window, causal, rr)
+                vis = visible_cells(lq, lk, window, causal, rr, _mask_rows(mask, q0, rr))
                 qh = _as64(q[q0 + rr, h, :])
                 doh = _as64(do[q0 + rr, h, :])
-                r = _panel(qh, kg, vg, doh, mask, scale, True)
+                r = _panel(qh, kg, vg, doh, vis, scale, True)
                 dk_j += scale * (r["ds"][:, j] @ qh)
                 dv_j += r["p"][:, j] @ doh
         res["dk"].append(dk_j)

@@ -12,14 +12,15 @@ import numpy as np
 from . import dense
 
 
-def loss(q, k, v, do, cu_q, cu_k, scale, window, causal, forward=None) -> float:
+def loss(q, k, v, do, cu_q, cu_k, scale, window, causal, forward=None, mask=None) -> float:
     forward = dense.sdpa_reference if forward is None else forward
-    out = forward(q, k, v, None, cu_q, cu_k, scale, window, causal, with_backward=False)
+    kw = {} if mask is None else dict(mask=mask)
+    out = forward(q, k, v, None, cu_q, cu_k, scale, window, causal, with_backward=False, **kw)
     return float(np.sum(out["o"] * np.asarray(do, dtype=np.float64)))
 
 
 def grads(q, k, v, do, cu_q, cu_k, scale, window, causal, step: float = 1e-5,
-          forward=None) -> dict:
+          forward=None, mask=None) -> dict:
     """dQ, dK, dV of L by central differences; ``forward`` defaults to the
     dense oracle's forward."""
     args = dict(q=np.array(q, dtype=np.float64), k=np.array(k, dtype=np.float64),
@@ -32,10 +33,10 @@ def grads(q, k, v, do, cu_q, cu_k, scale, window, causal, step: float = 1e-5,
             keep = x[idx]
             x[idx] = keep + step
             up = loss(args["q"], args["k"], args["v"], do, cu_q, cu_k, scale, window, causal,
-                      forward)
+                      forward, mask)
             x[idx] = keep - step
             dn = loss(args["q"], args["k"], args["v"], do, cu_q, cu_k, scale, window, causal,
-                      forward)
+                      forward, mask)
             x[idx] = keep
             g[idx] = (up - dn) / (2 * step)
         out["d" + name] = g

@@ -21,7 +21,10 @@ def _dot(a, b):
     return math.fsum(x * y for x, y in zip(a, b))
 
 
-def sdpa_loop(q, k, v, do, cu_q, cu_k, scale, window, causal) -> dict:
+def sdpa_loop(q, k, v, do, cu_q, cu_k, scale, window, causal, mask=None) -> dict:
+    """``mask`` (optional): boolean [T_q, >= every L_k]; key j of the query at
+    packed token t is visible only where mask[t][j] is true, on top of the
+    window (the same reading as ``oracle.dense``)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -44,6 +47,8 @@ def sdpa_loop(q, k, v, do, cu_q, cu_k, scale, window, causal) -> dict:
                 me = i + shift
                 keys = []
                 for j in range(kb - ka):
+                    if mask is not None and not mask[qa + i][j]:
+                        continue
                     if causal:
                         if j <= me and me - j < window:
                             keys.append(j)

@@ -172,3 +172,100 @@ def small_case(lengths_q: Sequence[int], lengths_k: Optional[Sequence[int]] = No
     return Workload(f"case_s{seed}", tuple(int(x) for x in lengths_q),
                     tuple(int(x) for x in lengths_k), heads_q, heads_kv, head_dim, window,
                     causal, dtype, float(scale), do_scale, seed)
+
+
+# ---------------------------------------------------------------- masks
+# An arbitrary boolean mask combined with the window: one matrix per packed
+# batch, shared by every head. Row t is packed query token t; column j is key j
+# of that token's sequence (0-based within the sequence). The C ABI takes it
+# bit-packed: row t is ``row_words`` uint32 words, bit j % 32 of word j // 32
+# holds column j; ``row_words`` is a multiple of 4 (16-byte rows).
+# Mask draws use their own generator, ``default_rng(seed)``, independent of
+# the tensor draw.
+
+def mask_row_words(max_len_k: int) -> int:
+    """Words per packed row: ceil(max_len_k / 32) rounded up to a multiple of 4."""
+    words = (max(int(max_len_k), 1) + 31) // 32
+    return (words + 3) // 4 * 4
+
+
+def random_mask(w: Workload, density: float, seed: int, empty_rows: int = 0) -> np.ndarray:
+    """Boolean [T_q, max L_k]: each cell allowed with probability ``density``;
+    ``empty_rows`` rows, picked at random, allow no key at all."""
+    rng = np.random.default_rng(seed)
+    m = rng.random((w.total_q, max(w.lengths_k, default=1))) < density
+    if empty_rows:
+        m[rng.choice(w.total_q, size=min(empty_rows, w.total_q), replace=False)] = False
+    return m
+
+
+def pack_mask(mask: np.ndarray, row_words: Optional[int] = None) -> np.ndarray:
+    """uint32 [T_q, row_words] from a boolean [T_q, W] mask (bit j % 32 of word
+    j // 32 is column j)."""
+    mask = np.asarray(mask, dtype=bool)
+    words = mask_row_words(mask.shape[1]) if row_words is None else int(row_words)
+    padded = np.zeros((mask.shape[0], words * 32), dtype=bool)
+    padded[:, :mask.shape[1]] = mask
+    bits = padded.reshape(mask.shape[0], words, 32).astype(np.uint64)
+    weights = (np.uint64(1) << np.arange(32, dtype=np.uint64))
+    return (bits * weights).sum(axis=2).astype(np.uint32)
+
+
+def unpack_rows(bits: np.ndarray, rows, width: int) -> np.ndarray:
+    """Boolean [len(rows), width] from packed rows ``rows`` of ``bits``."""
+    sel = np.asarray(bits)[np.asarray(rows, dtype=np.int64)]
+    j = np.arange(width)
+    return ((sel[:, j // 32] >> (j % 32).astype(np.uint32)) & 1).astype(bool)
+
+
+class PackedMaskRows:
+    """Boolean row view of a packed mask: ``m[rows]`` unpacks only those rows,
+    so a mask over tens of thousands of tokens never exists as booleans."""
+
+    def __init__(self, bits: np.ndarray, width: int):
+        self.bits, self.width = bits, int(width)
+
+    def __getitem__(self, rows):
+        return unpack_rows(self.bits, np.atleast_1d(rows), self.width)
+
+
+def document_mask_bits(w: Workload, doc_lengths: Sequence[Sequence[int]], row_words: Optional[int] = None) -> np.ndarray:
+    """Packed block-diagonal mask: sequence b's keys are split into documents
+    of lengths ``doc_lengths[b]`` (summing to L_k(b)); the query at key position
+    p = i + L_k - L_q may see key j only inside p's document."""
+    words = mask_row_words(max(w.lengths_k, default=1)) if row_words is None else int(row_words)
+    bits = np.zeros((w.total_q, words), dtype=np.uint32)
+    full = np.uint32(0xFFFFFFFF)
+    t = 0
+    for b in range(w.batch):
+        lq, lk = w.lengths_q[b], w.lengths_k[b]
+        docs = [int(x) for x in doc_lengths[b]]
+        assert sum(docs) == lk, "documents must cover the sequence's keys"
+        starts = np.cumsum([0] + docs)
+        for d in range(len(docs)):
+            a, e = int(starts[d]), int(starts[d + 1])  # keys [a, e)
+            # queries whose position p lies in [a, e)
+            i0, i1 = max(0, a - (lk - lq)), max(0, e - (lk - lq))
+            if i1 <= i0:
+                continue
+            row = np.zeros(words, dtype=np.uint32)
+            for wd in range(a // 32, (e + 31) // 32):
+                lo, hi = max(a, 32 * wd) - 32 * wd, min(e, 32 * wd + 32) - 32 * wd
+                span = full if hi - lo == 32 else np.uint32(((1 << (hi - lo)) - 1) << lo)
+                row[wd] = span
+            bits[t + i0:t + i1] = row
+        t += lq
+    return bits
+
+
+def document_lengths(seed: int, total: int) -> list:
+    """Documents drawn like the corpus's transcripts (the lognormal above,
+    clipped to [LEN_MIN, LEN_MAX]) until ``total`` keys are covered; the last
+    one is cut to fit."""
+    rng = np.random.default_rng(seed)
+    out, left = [], int(total)
+    while left > 0:
+        n = int(np.clip(np.rint(rng.lognormal(LOGNORMAL_MU, LOGNORMAL_SIGMA)), LEN_MIN, LEN_MAX))
+        out.append(min(n, left))
+        left -= out[-1]
+    return out

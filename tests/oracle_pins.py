@@ -18,7 +18,13 @@ AssertionError if the module disagrees with:
   * two-sided windows (no causal mask): window 1 sees only the token itself;
     reversing the token order reverses every output (the window is
     symmetric); a row equals full attention over the keys within w - 1 of its
-    position; window >= L_k is full attention.
+    position; window >= L_k is full attention,
+  * a mask combined with the window: finite differences and the brute-force
+    loop with random masks (rows with no allowed key included); an all-true
+    mask changes nothing; a block-diagonal (document) mask equals running the
+    documents as separate packed sequences; the causal lower triangle as a
+    mask on a two-sided window equals the causal window; a row with no
+    visible key has O = 0, LSE = -inf and no gradient.
 """
 from __future__ import annotations
 
@@ -27,15 +33,16 @@ import math
 import numpy as np
 
 from oracle import fd, loop
-from sliding_window_flash_amd.workloads import INT32_MAX, make_inputs, small_case
+from sliding_window_flash_amd.workloads import INT32_MAX, document_mask_bits, make_inputs, random_mask, small_case, unpack_rows
 
 
 def _call(ref, w, x, **kw):
     args = dict(q=x["q"], k=x["k"], v=x["v"], do=x["do"], cu_q=x["cu_q"], cu_k=x["cu_k"],
-                scale=w.scale, window=w.window, causal=w.causal)
+                scale=w.scale, window=w.window, causal=w.causal, mask=None)
     args.update(kw)
+    extra = {} if args["mask"] is None else dict(mask=args["mask"])
     return ref.sdpa_reference(args["q"], args["k"], args["v"], args["do"], args["cu_q"],
-                              args["cu_k"], args["scale"], args["window"], args["causal"])
+                              args["cu_k"], args["scale"], args["window"], args["causal"], **extra)
 
 
 def _close(a, b, tol, what):
@@ -312,8 +319,106 @@ def pin_wide_two_sided_is_full(ref):
         assert np.array_equal(a[key], c[key]), f"two-sided window >= L_k vs full {key}"
 
 
+MASK_CASES = [
+    # (lengths_q, lengths_k, heads_q, heads_kv, head_dim, window, causal, density, empty rows)
+    ([5, 7], None, 2, 1, 3, 3, True, 0.6, 1),
+    ([3, 4], [5, 7], 2, 1, 2, INT32_MAX, True, 0.5, 1),
+    ([6, 5], None, 2, 1, 2, 2, False, 0.7, 0),
+    ([4, 6], [6, 8], 2, 1, 2, INT32_MAX, False, 0.5, 2),
+]
+
+
+def _mask_case(n, case):
+    lq, lk, hq, hkv, d, win, causal, dens, empty = case
+    w = small_case(lq, lk, heads_q=hq, heads_kv=hkv, head_dim=d, window=win, causal=causal, seed=400 + n)
+    return w, make_inputs(w), random_mask(w, dens, seed=450 + n, empty_rows=empty)
+
+
+def pin_mask_finite_differences(ref):
+    for n, case in enumerate(MASK_CASES):
+        w, x, m = _mask_case(n, case)
+        out = _call(ref, w, x, mask=m)
+        num = fd.grads(x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale, w.window,
+                       w.causal, forward=ref.sdpa_reference, mask=m)
+        for g in ("dq", "dk", "dv"):
+            _close(out[g], num[g], 1e-8, f"masked finite differences {g} case {n}")
+
+
+def pin_mask_loop(ref):
+    for n, case in enumerate(MASK_CASES):
+        w, x, m = _mask_case(n, case)
+        out = _call(ref, w, x, mask=m)
+        bf = loop.sdpa_loop(x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale,
+                            w.window, w.causal, mask=m)
+        for key in ("o", "lse", "delta", "dq", "dk", "dv"):
+            scale = max(1.0, float(np.max(np.abs(bf[key][np.isfinite(bf[key])]), initial=0)))
+            _close(out[key], bf[key], 1e-12 * scale, f"masked loop {key} case {n}")
+
+
+def pin_mask_all_allowed(ref):
+    w = small_case([6, 9], [7, 11], heads_q=4, heads_kv=2, head_dim=3, window=4, seed=17)
+    x = make_inputs(w)
+    a = _call(ref, w, x)
+    b = _call(ref, w, x, mask=np.ones((w.total_q, 11), bool))
+    for key in a:
+        assert np.array_equal(a[key], b[key]), f"all-true mask vs no mask {key}"
+
+
+def pin_mask_documents_are_sequences(ref):
+    """One packed sequence cut into documents by a block-diagonal mask equals
+    the documents run as separate sequences (same window)."""
+    docs = [4, 6, 3]
+    w = small_case([13], heads_q=2, heads_kv=1, head_dim=3, window=3, seed=18)
+    x = make_inputs(w)
+    m = unpack_rows(document_mask_bits(w, [docs]), range(13), 13)
+    a = _call(ref, w, x, mask=m)
+    cu = np.cumsum([0] + docs).astype(np.int32)
+    b = _call(ref, w, x, cu_q=cu, cu_k=cu)
+    for key in ("o", "dq", "dk", "dv"):
+        _close(a[key], b[key], 1e-13, f"document mask vs separate sequences {key}")
+    _close(a["lse"], b["lse"], 1e-13, "document mask vs separate sequences lse")
+
+
+def pin_mask_lower_triangle_is_causal(ref):
+    """A two-sided window with the causal lower triangle (j <= p) as the mask
+    is the causal window."""
+    w = small_case([6, 9], [8, 11], heads_q=2, heads_kv=1, head_dim=3, window=3, causal=False, seed=19)
+    x = make_inputs(w)
+    m = np.zeros((w.total_q, 11), bool)
+    for b in range(w.batch):
+        lq, lk = w.lengths_q[b], w.lengths_k[b]
+        for i in range(lq):
+            m[x["cu_q"][b] + i, :i + lk - lq + 1] = True
+    a = _call(ref, w, x, mask=m)
+    c = _call(ref, w, x, causal=True)
+    for key in a:
+        _close(a[key], c[key], 1e-13, f"two-sided + lower-triangle mask vs causal {key}")
+
+
+def pin_mask_empty_rows(ref):
+    w = small_case([5, 7], heads_q=2, heads_kv=1, head_dim=3, window=INT32_MAX, seed=20)
+    x = make_inputs(w)
+    m = np.ones((w.total_q, 7), bool)
+    dead = [1, 8]                  # query 1 of each sequence allows no key
+    m[dead] = False
+    out = _call(ref, w, x, mask=m)
+    _close(out["o"][dead], np.zeros_like(out["o"][dead]), 0.0, "empty row: O = 0")
+    assert np.all(out["lse"][:, dead] == -np.inf), "empty row: LSE = -inf"
+    _close(out["dq"][dead], np.zeros_like(out["dq"][dead]), 0.0, "empty row: dQ = 0")
+    # the other rows are the same as with those rows' queries removed from the loss
+    do0 = x["do"].copy()
+    do0[dead] = 0.0
+    full = _call(ref, w, x, do=do0)
+    live = [t for t in range(w.total_q) if t not in dead]
+    for key in ("dk", "dv"):
+        _close(out[key], full[key], 1e-13, f"empty rows add no {key}")
+    _close(out["o"][live], full["o"][live], 1e-13, "live rows unchanged")
+
+
 ALL_PINS = [pin_finite_differences, pin_loop, pin_window_one, pin_scale_zero,
             pin_hand_example, pin_softmax_rows, pin_shift_identities, pin_gqa_is_repeated_mha,
             pin_packed_is_concatenation, pin_window_is_local, pin_wide_window_is_causal,
             pin_two_sided_window_one, pin_two_sided_flip, pin_two_sided_is_local,
-            pin_wide_two_sided_is_full]
+            pin_wide_two_sided_is_full, pin_mask_finite_differences, pin_mask_loop,
+            pin_mask_all_allowed, pin_mask_documents_are_sequences,
+            pin_mask_lower_triangle_is_causal, pin_mask_empty_rows]

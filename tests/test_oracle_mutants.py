@@ -23,9 +23,14 @@ MUTANTS = {
     "interleaved head groups": ("g = h // grp\n            kg", "g = h % hkv\n            kg"),
     "log base 2 in LSE": ("lse = np.where(has_key, m + np.log(zs)", "lse = np.where(has_key, m + np.log2(zs)"),
     "dK from dO instead of Q": ("scale * (ds.T @ qh)", "scale * (ds.T @ doh)"),
-    "two-sided window one-sided": ("return np.abs(pos - j[None, :]) < window", "return (pos - j[None, :]) < window"),
-    "two-sided window one key wider": ("return np.abs(pos - j[None, :]) < window",
-                                       "return np.abs(pos - j[None, :]) <= window"),
+    "two-sided window one-sided": ("vis = np.abs(pos - j[None, :]) < window", "vis = (pos - j[None, :]) < window"),
+    "two-sided window one key wider": ("vis = np.abs(pos - j[None, :]) < window",
+                                       "vis = np.abs(pos - j[None, :]) <= window"),
+    "mask ignored": ("vis = vis & np.asarray(allowed, dtype=bool)[:, :lk]", "vis = vis"),
+    "mask rows not offset by the sequence start": ("mask[q0 + np.asarray(rows, dtype=np.int64)]",
+                                                   "mask[np.asarray(rows, dtype=np.int64)]"),
+    "mask complement applied": ("vis & np.asarray(allowed, dtype=bool)[:, :lk]",
+                                "vis & ~np.asarray(allowed, dtype=bool)[:, :lk]"),
 }
 
 

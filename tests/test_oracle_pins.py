@@ -1,5 +1,7 @@
 """The oracle against what the pages and the mathematics fix (no GPU)."""
 import numpy as np
+
+import sliding_window_flash_amd.workloads as W
 import pytest
 
 import oracle_pins as pins
@@ -29,6 +31,32 @@ def test_sampled_rows_match_full_reference():
     ktoks = np.concatenate([rng.integers(0, w.total_k, 20), [0, 179, 180, 275]])
     kh = rng.integers(0, w.heads_kv, ktoks.size)
     keys = dense.sdpa_key_rows(*args, ktoks, kh, panel_rows=11)
+    np.testing.assert_allclose(keys["dk"], full["dk"][ktoks, kh], atol=1e-13)
+    np.testing.assert_allclose(keys["dv"], full["dv"][ktoks, kh], atol=1e-13)
+
+
+def test_sampled_rows_match_full_reference_masked():
+    """The row samplers read the same mask rows as the full reference, also
+    through the packed-row view used at large sizes."""
+    w = small_case([150, 90, 70], [180, 90, 70], heads_q=4, heads_kv=2, head_dim=16,
+                   window=40, seed=22)
+    x = make_inputs(w)
+    m = W.random_mask(w, 0.7, seed=23, empty_rows=3)
+    view = W.PackedMaskRows(W.pack_mask(m), 180)
+    args = (x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale, w.window, w.causal)
+    full = dense.sdpa_reference(*args, panel_rows=37, mask=m)
+    rng = np.random.default_rng(1)
+    toks = rng.integers(0, w.total_q, 25)
+    heads = rng.integers(0, w.heads_q, 25)
+    rows = dense.sdpa_query_rows(*args, toks, heads, mask=view)
+    np.testing.assert_allclose(rows["o"], full["o"][toks, heads], atol=1e-13)
+    np.testing.assert_array_equal(np.isfinite(rows["lse"]), np.isfinite(full["lse"][heads, toks]))
+    fin = np.isfinite(rows["lse"])
+    np.testing.assert_allclose(rows["lse"][fin], full["lse"][heads, toks][fin], atol=1e-13)
+    np.testing.assert_allclose(rows["dq"], full["dq"][toks, heads], atol=1e-13)
+    ktoks = np.concatenate([rng.integers(0, w.total_k, 20), [0, 179, 180, 339]])
+    kh = rng.integers(0, w.heads_kv, ktoks.size)
+    keys = dense.sdpa_key_rows(*args, ktoks, kh, panel_rows=11, mask=view)
     np.testing.assert_allclose(keys["dk"], full["dk"][ktoks, kh], atol=1e-13)
     np.testing.assert_allclose(keys["dv"], full["dv"][ktoks, kh], atol=1e-13)
 

@@ -49,3 +49,33 @@ def test_inputs_are_seeded_and_bf16_representable():
     x = W.make_inputs(w.replace(dtype="fp16"))
     for k in ("q", "k", "v", "do"):
         assert np.array_equal(x[k].astype(np.float16).astype(np.float32), x[k]), k
+
+
+def test_mask_packing_bit_order():
+    """Bit j % 32 of word j // 32 holds column j; rows are padded to 4 words."""
+    m = np.zeros((2, 70), bool)
+    m[0, [0, 31, 32]] = True
+    m[1, 69] = True
+    b = W.pack_mask(m)
+    assert b.shape == (2, 4) and b.dtype == np.uint32
+    assert b[0].tolist() == [0x80000001, 0x1, 0, 0]
+    assert b[1].tolist() == [0, 0, 0x20, 0]
+    assert np.array_equal(W.unpack_rows(b, [0, 1], 70), m)
+    assert W.mask_row_words(1) == 4 and W.mask_row_words(128) == 4 and W.mask_row_words(129) == 8
+
+
+def test_document_mask_rows():
+    """Query i (key position p = i + L_k - L_q) sees exactly the keys of p's document."""
+    w = W.small_case([5, 7], [6, 9], window=3, seed=1)
+    docs = [[2, 4], [3, 3, 3]]
+    got = W.unpack_rows(W.document_mask_bits(w, docs), range(w.total_q), 9)
+    t = 0
+    for b in range(w.batch):
+        lq, lk = w.lengths_q[b], w.lengths_k[b]
+        owner = np.repeat(np.arange(len(docs[b])), docs[b])
+        for i in range(lq):
+            want = np.zeros(9, bool)
+            want[:lk] = owner == owner[i + lk - lq]
+            assert np.array_equal(got[t + i], want), (b, i)
+        t += lq
+    assert sum(W.document_lengths(7, 32768)) == 32768
