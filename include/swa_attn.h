@@ -144,6 +144,46 @@ attn_status_t attn_bwd_stages(const attn_params_t* p, int32_t stages, const void
                               const int32_t* cu_seqlens_k, void* dq, void* dk, void* dv,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* An arbitrary boolean mask combined with the window.
+ *
+ * "Off NVIDIA, you fix the platform yourself" (labs.layer2c.com), list of
+ * what is not proved: a window combined with an arbitrary mask still falls
+ * back to the full score matrix in training; its backward-memory record entry
+ * measures against the boolean mask mlx-lm passes. Here such a mask is one
+ * boolean matrix per packed batch, shared by every head: cell (i, j) of
+ * sequence b is visible iff the window shows it (attn_params_t) AND the mask
+ * allows it. The kernels still visit only the window's tiles, so time and
+ * memory stay linear in the sequence length; the mask adds one bit per
+ * (query token, key) of input.
+ *
+ * Layout: row t (packed query token t = cu_seqlens_q[b] + i) is `row_words`
+ * consecutive uint32 words; bit (j % 32) of word (j / 32) allows key j of that
+ * token's sequence (0-based within the sequence, i.e. packed key
+ * cu_seqlens_k[b] + j). Bits for j >= L_k are ignored. A query whose visible
+ * set is empty gets O = 0, LSE = -inf and contributes no gradient.
+ * Ownership: device memory owned by the caller, only read. */
+typedef struct {
+  const uint32_t* bits; /* device, [total_q, row_words], 16-byte aligned */
+  int64_t row_words;    /* a multiple of 4, >= ceil(max_seqlen_k / 32), <= 2^24 */
+} attn_mask_t;
+
+/* attn_fwd with a mask. Same outputs and errors as attn_fwd; also
+ * ATTN_ERR_NULL if `mask` or (total_q > 0) `mask->bits` is NULL, ATTN_ERR_ALIGN
+ * if `bits` is not 16-byte aligned, ATTN_ERR_SHAPE if `row_words` is not a
+ * multiple of 4 or is below ceil(max_seqlen_k / 32), ATTN_ERR_UNSUPPORTED if it
+ * is above 2^24. */
+attn_status_t attn_fwd_masked(const attn_params_t* p, const attn_mask_t* mask, const void* q,
+                              const void* k, const void* v, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, void* o, float* lse, void* stream);
+
+/* attn_bwd with a mask (the one the forward used). Same outputs, workspace
+ * and errors as attn_bwd, plus the mask checks of attn_fwd_masked. */
+attn_status_t attn_bwd_masked(const attn_params_t* p, const attn_mask_t* mask, const void* q,
+                              const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, void* dq, void* dk, void* dv,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_str(attn_status_t s);
 

@@ -259,12 +259,19 @@ def sdpa_key_rows(q, k, v, do, cu_q, cu_k, scale, window, causal,
         k0, k1 = int(cu_k[b]), int(cu_k[b + 1])
         lq, lk = q1 - q0, k1 - k0
         kg, vg = _as64(k[k0:k1, g, :]), _as64(v[k0:k1, g, :])
-        # the column of the mask for key j, built 1024 rows at a time
+        # The column of the visibility matrix for key j, built 1024 rows at a
+        # time over the rows whose position p = i + (L_k - L_q) the window lets
+        # reach j (j <= p < j + w causal, |p - j| < w two-sided); every other
+        # row's cell is masked by the window itself.
+        shift = lk - lq
+        lo = j - shift if causal else j - shift - window + 1
+        hi = j - shift + window - 1
+        lo, hi = max(0, lo), min(lq - 1, hi)
         col = np.concatenate([
-            visible_cells(lq, lk, window, causal, np.arange(r, min(lq, r + 1024)),
-                          _mask_rows(mask, q0, np.arange(r, min(lq, r + 1024))))[:, j]
-            for r in range(0, lq, 1024)]) if lq else np.zeros(0, bool)
-        rows = np.nonzero(col)[0]
+            visible_cells(lq, lk, window, causal, np.arange(r, min(hi + 1, r + 1024)),
+                          _mask_rows(mask, q0, np.arange(r, min(hi + 1, r + 1024))))[:, j]
+            for r in range(lo, hi + 1, 1024)]) if hi >= lo else np.zeros(0, bool)
+        rows = lo + np.nonzero(col)[0]
         dk_j = np.zeros(k.shape[2], F64)
         dv_j = np.zeros(k.shape[2], F64)
         for h in range(g * grp, (g + 1) * grp):

@@ -27,7 +27,7 @@ BWD_DELTA, BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 4, 7
 
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_stages", "attn_bwd_workspace_bytes", "attn_status_str",
             "attn_check_params", "attn_tile_sizes", "attn_query_tile_range",
-            "attn_key_tile_range")
+            "attn_key_tile_range", "attn_fwd_masked", "attn_bwd_masked")
 
 
 class AttnError(RuntimeError):
@@ -44,6 +44,11 @@ class AttnParams(ctypes.Structure):
         ("window", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
     ]
+
+
+class AttnMask(ctypes.Structure):
+    """attn_mask_t: bit-packed rows of a boolean mask combined with the window."""
+    _fields_ = [("bits", ctypes.c_void_p), ("row_words", ctypes.c_int64)]
 
 
 _LIB = None
@@ -68,6 +73,12 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_stages.restype = ctypes.c_int
         L.attn_bwd_workspace_bytes.argtypes = [P]
         L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        M = ctypes.POINTER(AttnMask)
+        L.attn_fwd_masked.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.attn_fwd_masked.restype = ctypes.c_int
+        L.attn_bwd_masked.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      ctypes.c_size_t, vp]
+        L.attn_bwd_masked.restype = ctypes.c_int
         L.attn_status_str.argtypes = [ctypes.c_int]
         L.attn_status_str.restype = ctypes.c_char_p
         L.attn_check_params.argtypes = [P]
@@ -174,9 +185,19 @@ def _require(t, name):
     return t
 
 
+def _mask_arg(mask):
+    """attn_mask_t for a device tensor of packed rows ([T_q, row_words], 32-bit
+    words; bit j % 32 of word j // 32 allows key j of the row's sequence)."""
+    _require(mask, "mask")
+    if mask.dim() != 2 or mask.element_size() != 4:
+        raise ValueError("mask must be [total_q, row_words] of 32-bit words")
+    return AttnMask(mask.data_ptr(), mask.shape[1])
+
+
 def fwd(q, k, v, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=INT32_MAX, causal=True,
-        scale=None, out=None, lse=None, stream=None):
-    """O [T_q, Hq, d] (q.dtype) and LSE [Hq, T_q] (fp32) through attn_fwd."""
+        scale=None, out=None, lse=None, stream=None, mask=None):
+    """O [T_q, Hq, d] (q.dtype) and LSE [Hq, T_q] (fp32) through attn_fwd, or
+    attn_fwd_masked when ``mask`` (packed rows, see :func:`_mask_arg`) is given."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (cu_q, "cu_q"), (cu_k, "cu_k")):
         _require(t, n)
@@ -186,18 +207,23 @@ def fwd(q, k, v, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=INT32_MAX, ca
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
-    st = lib().attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_q), _ptr(cu_k),
-                        _ptr(out), _ptr(lse), _stream_ptr(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(cu_q), _ptr(cu_k), _ptr(out), _ptr(lse), _stream_ptr(stream))
+    if mask is None:
+        st, what = lib().attn_fwd(ctypes.byref(p), *args), "attn_fwd"
+    else:
+        m = _mask_arg(mask)
+        st, what = lib().attn_fwd_masked(ctypes.byref(p), ctypes.byref(m), *args), "attn_fwd_masked"
     if st:
-        raise AttnError(st, "attn_fwd")
+        raise AttnError(st, what)
     return out, lse
 
 
 def bwd(q, k, v, o, lse, do, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=INT32_MAX,
         causal=True, scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None,
-        stages=BWD_ALL):
+        stages=BWD_ALL, mask=None):
     """dQ, dK, dV through attn_bwd_stages (the VJP of sum(O * dO)); ``stages``
-    selects a subset of the backward's launches (all three by default)."""
+    selects a subset of the backward's launches (all three by default). With
+    ``mask`` (the forward's), through attn_bwd_masked (all stages)."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (do, "do"),
                  (cu_q, "cu_q"), (cu_k, "cu_k")):
@@ -210,10 +236,16 @@ def bwd(q, k, v, o, lse, do, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=I
     nbytes = workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    st = lib().attn_bwd_stages(ctypes.byref(p), int(stages), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                               _ptr(lse), _ptr(do), _ptr(cu_q), _ptr(cu_k), _ptr(dq), _ptr(dk),
-                               _ptr(dv), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(cu_q), _ptr(cu_k), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream_ptr(stream))
+    if mask is None:
+        st, what = lib().attn_bwd_stages(ctypes.byref(p), int(stages), *args), "attn_bwd_stages"
+    else:
+        if stages != BWD_ALL:
+            raise ValueError("the masked backward runs all stages")
+        m = _mask_arg(mask)
+        st, what = lib().attn_bwd_masked(ctypes.byref(p), ctypes.byref(m), *args), "attn_bwd_masked"
     if st:
-        raise AttnError(st, "attn_bwd_stages")
+        raise AttnError(st, what)
     return dq, dk, dv

@@ -72,11 +72,21 @@ attn_status_t attn_check_params(const attn_params_t* p) {
   return ATTN_OK;
 }
 
-attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, const void* v,
-                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o,
-                       float* lse, void* stream) {
+static attn_status_t check_mask(const attn_params_t* p, const attn_mask_t* m) {
+  if (m == nullptr) return ATTN_ERR_NULL;
+  if (m->row_words < 1 || m->row_words % 4 != 0 || m->row_words < ((int64_t)p->max_seqlen_k + 31) / 32)
+    return ATTN_ERR_SHAPE;
+  // a 64-row mask tile is addressed with 32-bit byte offsets
+  if (m->row_words > (1 << 24)) return ATTN_ERR_UNSUPPORTED;
+  return check_tensor(m->bits, (int64_t)p->total_q * m->row_words, true);
+}
+
+static attn_status_t fwd_impl(const attn_params_t* p, const attn_mask_t* mask, const void* q,
+                              const void* k, const void* v, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, void* o, float* lse, void* stream) {
   attn_status_t s = attn_check_params(p);
   if (s != ATTN_OK) return s;
+  if (mask != nullptr && (s = check_mask(p, mask)) != ATTN_OK) return s;
   if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return ATTN_ERR_NULL;
   if (!aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k)) return ATTN_ERR_ALIGN;
   const int64_t nq = q_elems(p), nk = k_elems(p);
@@ -93,9 +103,28 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   a.cu_k = cu_seqlens_k;
   a.out_o = o;
   a.out_lse = lse;
+  if (mask != nullptr) {
+    a.mask = mask->bits;
+    a.mask_words = mask->row_words;
+  }
   if (swa::launch_fwd(p->dtype, p->head_dim, a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
+}
+
+attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, const void* v,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o,
+                       float* lse, void* stream) {
+  return fwd_impl(p, nullptr, q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, stream);
+}
+
+attn_status_t attn_fwd_masked(const attn_params_t* p, const attn_mask_t* mask, const void* q,
+                              const void* k, const void* v, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, void* o, float* lse, void* stream) {
+  attn_status_t s = attn_check_params(p);
+  if (s != ATTN_OK) return s;
+  if (mask == nullptr) return ATTN_ERR_NULL;
+  return fwd_impl(p, mask, q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, stream);
 }
 
 // Workspace: D [heads_q, total_q] fp32, then LSE*log2(e) [heads_q, total_q]
@@ -110,13 +139,14 @@ size_t attn_bwd_workspace_bytes(const attn_params_t* p) {
   return 2 * ws_array_bytes(p);
 }
 
-attn_status_t attn_bwd_stages(const attn_params_t* p, int32_t stages, const void* q,
-                              const void* k, const void* v, const void* o, const float* lse,
-                              const void* dout, const int32_t* cu_seqlens_q,
+static attn_status_t bwd_impl(const attn_params_t* p, const attn_mask_t* mask, int32_t stages,
+                              const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, const int32_t* cu_seqlens_q,
                               const int32_t* cu_seqlens_k, void* dq, void* dk, void* dv,
                               void* workspace, size_t workspace_bytes, void* stream) {
   attn_status_t s = attn_check_params(p);
   if (s != ATTN_OK) return s;
+  if (mask != nullptr && (s = check_mask(p, mask)) != ATTN_OK) return s;
   if (stages <= 0 || (stages & ~ATTN_BWD_ALL) != 0) return ATTN_ERR_SHAPE;
   const bool st_delta = stages & ATTN_BWD_DELTA, st_dq = stages & ATTN_BWD_DQ,
              st_dkdv = stages & ATTN_BWD_DKDV;
@@ -152,9 +182,22 @@ attn_status_t attn_bwd_stages(const attn_params_t* p, int32_t stages, const void
   a.dv = dv;
   a.delta = static_cast<float*>(workspace);
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_array_bytes(p));
+  if (mask != nullptr) {
+    a.mask = mask->bits;
+    a.mask_words = mask->row_words;
+  }
   if (swa::launch_bwd(p->dtype, p->head_dim, stages, a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
+}
+
+attn_status_t attn_bwd_stages(const attn_params_t* p, int32_t stages, const void* q,
+                              const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, void* dq, void* dk, void* dv,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(p, nullptr, stages, q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, dq, dk, dv,
+                  workspace, workspace_bytes, stream);
 }
 
 attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v,
@@ -162,8 +205,20 @@ attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, con
                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dq,
                        void* dk, void* dv, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  return attn_bwd_stages(p, ATTN_BWD_ALL, q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, dq,
-                         dk, dv, workspace, workspace_bytes, stream);
+  return bwd_impl(p, nullptr, ATTN_BWD_ALL, q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, dq,
+                  dk, dv, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_bwd_masked(const attn_params_t* p, const attn_mask_t* mask, const void* q,
+                              const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, void* dq, void* dk, void* dv,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status_t s = attn_check_params(p);
+  if (s != ATTN_OK) return s;
+  if (mask == nullptr) return ATTN_ERR_NULL;
+  return bwd_impl(p, mask, ATTN_BWD_ALL, q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, dq, dk,
+                  dv, workspace, workspace_bytes, stream);
 }
 
 const char* attn_status_str(attn_status_t s) {

@@ -148,6 +148,35 @@ __device__ __forceinline__ QueryItem decode_query_item(const AttnArgs& a, int bm
 // is the same softmax: O and LSE use the same reference at the end.
 constexpr float kRescaleSlack = 8.0f;
 
+// ------------------------------------------------ mask combined with the window
+// Mask row t (packed query token) is a.mask_words words; bit j % 32 of word
+// j / 32 allows key j of the token's sequence.
+
+// The words of query row t that cover key tile kb of NW * 32 keys; zeros for a
+// row past L_q (masked, never stored).
+template <int NW>
+__device__ __forceinline__ void row_mask_words(const AttnArgs& a, int64_t t, bool ok, int kb,
+                                               uint32_t (&mw)[NW]) {
+  static_assert(NW == 2, "64-key tiles");
+  if (ok) {
+    const uint2 v = *reinterpret_cast<const uint2*>(a.mask + t * a.mask_words + (int64_t)NW * kb);
+    mw[0] = v.x;
+    mw[1] = v.y;
+  } else {
+    mw[0] = mw[1] = 0u;
+  }
+}
+
+// Query-major score tiles (one query per lane; element r of 32-key block kt
+// is key 32 kt + 8 (r / 4) + 4 half + r % 4 of the tile): -inf where the
+// query's bit for that key is clear.
+__device__ __forceinline__ void apply_row_mask(f32x16& s, uint32_t word, int half) {
+  const uint32_t w = word >> (4 * half);
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) s[r] = -INFINITY;
+}
+
 template <int N> using ic = std::integral_constant<int, N>;
 
 // Per-query visibility as one unsigned range test with a wave-uniform limit:
@@ -189,9 +218,10 @@ __device__ __forceinline__ PairWindow pair_window(int lk, int window, bool causa
 // (the 128 KB of K/V stages leave room for one workgroup per CU anyway).
 constexpr int waves_per_simd(int d) { return d > 128 ? 1 : 2; }
 
-template <typename T, int D, int BM, int BN>
+template <typename T, int D, int BM, int BN, bool M>
 __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
 fwd_kernel(AttnArgs a) {
+  static_assert(BN == 64, "mask words cover 64-key tiles");
   constexpr int NT = BM * 2;
   constexpr bool kPipe = sizeof(T) == 2 && D <= 128;  // software-pipelined loop (see below)
   using KTile = LdsTile<T, BN, D>;
@@ -216,6 +246,7 @@ fwd_kernel(AttnArgs a) {
 
   const int i = it.qb * BM + w * 32 + l32;  // this lane's query row
   const bool row_ok = i < it.lq;
+  const int64_t mrow = it.q0 + (row_ok ? i : 0);  // its mask row (with M)
   Frag<T> qf[D / 16];
   {
     const T* qrow = Q + (int64_t)(it.q0 + (row_ok ? i : 0)) * qstride + it.h * D + 8 * half;
@@ -266,8 +297,9 @@ fwd_kernel(AttnArgs a) {
     };
     // one step: tile kb's scores in `cur` (K and V in stage `stage`); with a
     // successor, its scores go to `nxt` from the other stage's K tile
-    auto pstep = [&](auto stage_c, auto next_c, int kb, f32x16 (&cur)[BN / 32], f32x16 (&nxt)[BN / 32])
-        __attribute__((always_inline)) {
+    // With M, the mask words of tile kb are in `mcur`; the next tile's load into `mnxt`.
+    auto pstep = [&](auto stage_c, auto next_c, int kb, f32x16 (&cur)[BN / 32], f32x16 (&nxt)[BN / 32],
+                     uint32_t (&mcur)[BN / 32], uint32_t (&mnxt)[BN / 32]) __attribute__((always_inline)) {
       constexpr int stage = decltype(stage_c)::value;
       constexpr bool has_next = decltype(next_c)::value;
       char* here = stage ? st1 : st0;
@@ -275,6 +307,7 @@ fwd_kernel(AttnArgs a) {
       if constexpr (has_next) {
         if (kb + 2 <= kr.hi) fill_tile(kvld, here, K, kstride, kb + 2, it.lk);
         fill_tile(kvld, other + KTile::kBytes, V, kstride, kb + 1, it.lk);
+        if constexpr (M) row_mask_words(a, mrow, row_ok, kb + 1, mnxt);
       }
       if (!(kr.full_lo <= kb && kb <= kr.full_hi)) {  // edge tile: mask cell by cell
         const uint32_t mb = mpos - (uint32_t)(kb * BN + 4 * half);
@@ -291,6 +324,10 @@ fwd_kernel(AttnArgs a) {
             for (int r = 0; r < 16; ++r)
               if (jb + 32 * kt + 8 * (r >> 2) + (r & 3) >= it.lk) cur[kt][r] = -INFINITY;
         }
+      }
+      if constexpr (M) {
+#pragma unroll
+        for (int kt = 0; kt < BN / 32; ++kt) apply_row_mask(cur[kt], mcur[kt], half);
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -329,22 +366,25 @@ fwd_kernel(AttnArgs a) {
     };
     if (ntiles > 0) {
       f32x16 sa[BN / 32], sb[BN / 32];
+      uint32_t ma[BN / 32] = {}, mb[BN / 32] = {};
       int kb = kr.lo;
       // the first step refills the first tile's K stage: every wave must have
       // read it first (later steps meet a barrier between the two)
       if (p) {
+        if constexpr (M) row_mask_words(a, mrow, row_ok, kb, mb);
         qk(sb, st1);
         __syncthreads();
-        pstep(ic<1>{}, std::true_type{}, kb++, sb, sa);
+        pstep(ic<1>{}, std::true_type{}, kb++, sb, sa, mb, ma);
       } else {
+        if constexpr (M) row_mask_words(a, mrow, row_ok, kb, ma);
         qk(sa, st0);
         __syncthreads();
       }
       for (; kb < kr.hi; kb += 2) {
-        pstep(ic<0>{}, std::true_type{}, kb, sa, sb);
-        pstep(ic<1>{}, std::true_type{}, kb + 1, sb, sa);
+        pstep(ic<0>{}, std::true_type{}, kb, sa, sb, ma, mb);
+        pstep(ic<1>{}, std::true_type{}, kb + 1, sb, sa, mb, ma);
       }
-      pstep(ic<0>{}, std::false_type{}, kb, sa, sb);
+      pstep(ic<0>{}, std::false_type{}, kb, sa, sb, ma, mb);
     }
   } else {
   const int ntiles = kr.hi - kr.lo + 1;
@@ -365,6 +405,8 @@ fwd_kernel(AttnArgs a) {
     // makes the compiler copy the O accumulator at every step, which costs more
     // than the few all-masked wave tiles.
     const bool edge = !(kr.full_lo <= kb && kb <= kr.full_hi);
+    uint32_t mw[BN / 32] = {};
+    if constexpr (M) row_mask_words(a, mrow, row_ok, kb, mw);
     f32x16 s[BN / 32];
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt) {
@@ -387,6 +429,10 @@ fwd_kernel(AttnArgs a) {
           for (int r = 0; r < 16; ++r)
             if (jb + 32 * kt + 8 * (r >> 2) + (r & 3) >= it.lk) s[kt][r] = -INFINITY;
       }
+    }
+    if constexpr (M) {
+#pragma unroll
+      for (int kt = 0; kt < BN / 32; ++kt) apply_row_mask(s[kt], mw[kt], half);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -474,9 +520,10 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------- backward: dQ
-template <typename T, int D, int BM, int BN>
+template <typename T, int D, int BM, int BN, bool M>
 __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
 bwd_dq_kernel(AttnArgs a) {
+  static_assert(BN == 64, "mask words cover 64-key tiles");
   constexpr int NT = BM * 2;
   using KTile = LdsTile<T, BN, D>;
   __shared__ __attribute__((aligned(1024))) char st0[2 * KTile::kBytes];
@@ -497,6 +544,7 @@ bwd_dq_kernel(AttnArgs a) {
 
   const int i = it.qb * BM + w * 32 + l32;
   const bool row_ok = i < it.lq;
+  const int64_t mrow = it.q0 + (row_ok ? i : 0);  // its mask row (with M)
   Frag<T> qf[D / 16], df[D / 16];
   float lse2 = INFINITY, dlt = 0.f;
   {
@@ -548,6 +596,8 @@ bwd_dq_kernel(AttnArgs a) {
       __syncthreads();
       return;
     }
+    uint32_t mw[BN / 32] = {};
+    if constexpr (M) row_mask_words(a, mrow, row_ok, kb, mw);
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt) {
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -568,6 +618,7 @@ bwd_dq_kernel(AttnArgs a) {
             if (jb + 8 * (r >> 2) + (r & 3) >= it.lk) s[r] = -INFINITY;
         }
       }
+      if constexpr (M) apply_row_mask(s, mw[kt], half);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pv = fast_exp2(fmaf(s[r], c, -lse2));
@@ -620,14 +671,17 @@ __device__ __forceinline__ void take_over(const float* red, f32x16 (&acc)[NB], i
 // are summed through LDS at the end.
 // Key-major decode: KV head outermost, then sequence, then key tile ascending
 // (for the causal mask early key tiles are seen by the most queries).
-template <typename T, int D, int BN, int BM>
+template <typename T, int D, int BN, int BM, bool M>
 __global__ void __launch_bounds__(BN * 4) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(AttnArgs a) {
   constexpr int NT = BN * 4;  // 8 waves for BN = 128
   static_assert(BN == 128 && BM == 64, "wave layout assumes 4 key blocks x 2 query halves");
   using QTile = LdsTile<T, BM, D>;
   using KTile = LdsTile<T, BN, D>;
-  constexpr int kStage = 2 * QTile::kBytes + 2 * BM * 4;  // Q, dO, LSE*log2e, D
+  // with M, the step's mask tile follows: BM rows x 16 bytes (the 4 words of
+  // this key tile's 128 keys)
+  constexpr int kMaskOff = 2 * QTile::kBytes + 2 * BM * 4;
+  constexpr int kStage = kMaskOff + (M ? BM * 16 : 0);  // Q, dO, LSE*log2e, D[, mask]
   constexpr int kRedBlock = 32 * D * 4;                   // fp32 partial of one 32-key block
   static_assert(KTile::kBytes >= 2 * kRedBlock && kStage >= 2 * kRedBlock, "reduction reuse");
   __shared__ __attribute__((aligned(1024))) char st0[kStage];
@@ -701,6 +755,13 @@ bwd_dkdv_kernel(AttnArgs a) {
       buffer_to_lds4(buffer_rsrc(a.delta + idx, (uint32_t)qvalid * 4u), st + 2 * QTile::kBytes + BM * 4,
                        (uint32_t)lane * 4u);
     }
+    if constexpr (M) {
+      if (w == 1) {  // lane r: row r's words 4 kb .. 4 kb + 3; rows past L_q arrive as zeros
+        const uint32_t rb = (uint32_t)a.mask_words * 4u;
+        buffer_to_lds16(buffer_rsrc(a.mask + (int64_t)(q0 + nqb * BM) * a.mask_words + 4 * kb, (uint32_t)qvalid * rb),
+                        st + kMaskOff, (uint32_t)lane * rb);
+      }
+    }
     if (++nqb > qr.hi) {
       nqb = qr.lo;
       ++nh;
@@ -740,6 +801,15 @@ bwd_dkdv_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) {
         const int off = 8 * (r >> 2) + (r & 3);
         if ((ib + off >= lq) | (pw.windowed & ((uint32_t)(mb + off) >= pw.lim))) s[r] = -INFINITY;
+      }
+    }
+    if constexpr (M) {  // this lane's key is bit l32 of word kt of each row
+      const char* mt = qs + kMaskOff;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * mh + 4 * half + 8 * (r >> 2) + (r & 3);
+        const uint32_t word = *reinterpret_cast<const uint32_t*>(mt + 16 * row + 4 * kt);
+        if (!((word >> l32) & 1u)) s[r] = -INFINITY;
       }
     }
 #pragma unroll
@@ -806,7 +876,7 @@ bwd_dkdv_kernel(AttnArgs a) {
 // alike), then adds its dims' share of P^T dO and dS^T Q. K and V stay in LDS;
 // query tiles stream through two stages. LDS: 2 x 32 KB for K, V and 2 x 33 KB
 // for the stages; the accumulators take 128 registers.
-template <typename T, int D, int BN, int BM>
+template <typename T, int D, int BN, int BM, bool M>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_dkdv_wide_kernel(AttnArgs a) {
   constexpr int NT = 256;
@@ -815,7 +885,10 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
   using QTile = LdsTile<T, BM, D>;
   using KTile = LdsTile<T, BN, D>;
   constexpr int kStats = 64 * 4;                          // one 64-lane 4-byte load's worth
-  constexpr int kStage = 2 * QTile::kBytes + 2 * kStats;  // Q, dO, LSE*log2e, D
+  // with M, the step's mask tile follows: BM = 32 rows x 8 bytes (the 2 words
+  // of this key tile's 64 keys)
+  constexpr int kMaskOff = 2 * QTile::kBytes + 2 * kStats;
+  constexpr int kStage = kMaskOff + (M ? BM * 8 : 0);  // Q, dO, LSE*log2e, D[, mask]
   __shared__ __attribute__((aligned(1024))) char st0[kStage];
   __shared__ __attribute__((aligned(1024))) char st1[kStage];
   __shared__ __attribute__((aligned(1024))) char klds[KTile::kBytes];
@@ -884,6 +957,13 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
       buffer_to_lds4(buffer_rsrc(a.delta + idx, (uint32_t)qvalid * 4u), st + 2 * QTile::kBytes + kStats,
                      (uint32_t)lane * 4u);
     }
+    if constexpr (M) {
+      if (w == 1) {  // lane l: word 2 kb + l % 2 of row l / 2; rows past L_q arrive as zeros
+        const uint32_t rb = (uint32_t)a.mask_words * 4u;
+        buffer_to_lds4(buffer_rsrc(a.mask + (int64_t)(q0 + nqb * BM) * a.mask_words + 2 * kb, (uint32_t)qvalid * rb),
+                       st + kMaskOff, (uint32_t)(lane >> 1) * rb + (uint32_t)(lane & 1) * 4u);
+      }
+    }
     if (++nqb > qr.hi) {
       nqb = qr.lo;
       ++nh;
@@ -920,6 +1000,15 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) {
         const int off = 8 * (r >> 2) + (r & 3);
         if ((ib + off >= lq) | (pw.windowed & ((uint32_t)(mb + off) >= pw.lim))) s[r] = -INFINITY;
+      }
+    }
+    if constexpr (M) {  // this lane's key is bit l32 of word kt of each row
+      const char* mt = qs + kMaskOff;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 4 * half + 8 * (r >> 2) + (r & 3);
+        const uint32_t word = *reinterpret_cast<const uint32_t*>(mt + 8 * row + 4 * kt);
+        if (!((word >> l32) & 1u)) s[r] = -INFINITY;
       }
     }
 #pragma unroll
@@ -966,11 +1055,15 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
 // 4 waves of 32 keys, K and V in registers, 64-query steps.
 // Key-major decode: KV head outermost, then sequence, then key tile ascending
 // (for the causal mask early key tiles are seen by the most queries).
-template <typename T, int D, int BN, int BM>
+template <typename T, int D, int BN, int BM, bool M>
 __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
   constexpr int NT = BN * 2;
   using QTile = LdsTile<T, BM, D>;
-  constexpr int kStage = 2 * QTile::kBytes + 2 * BM * 4;  // Q, dO, LSE*log2e, D
+  // with M, the step's mask tile follows: BM rows x 4 words (this key tile's
+  // 128 keys), one word per thread
+  static_assert(!M || BM * 4 == NT, "one mask word per thread");
+  constexpr int kMaskOff = 2 * QTile::kBytes + 2 * BM * 4;
+  constexpr int kStage = kMaskOff + (M ? BM * 16 : 0);  // Q, dO, LSE*log2e, D[, mask]
   __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
@@ -1020,6 +1113,7 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
   const int steps = grp * nq;
   TileStage<T, BM, D, NT> sq, sd;
   float l2v = INFINITY, dlv = 0.f;  // LSE*log2e and D of row tid (tid < BM)
+  uint32_t mword = 0u;               // with M: word tid % 4 of row tid / 4
   auto issue = [&](int t) {
     const int h = g * grp + t / nq;
     const int qb = qr.lo + t % nq;
@@ -1034,6 +1128,10 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
       l2v = a.lse2[idx];
       dlv = a.delta[idx];
     }
+    if constexpr (M) {
+      const int row = tid >> 2;
+      mword = row < qvalid ? a.mask[(int64_t)(q0 + qb * BM + row) * a.mask_words + 4 * kb + (tid & 3)] : 0u;
+    }
   };
   auto commit = [&](char* st) {
     sq.store(st, tid);
@@ -1042,6 +1140,7 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
       reinterpret_cast<float*>(st + 2 * QTile::kBytes)[tid] = l2v;
       reinterpret_cast<float*>(st + 2 * QTile::kBytes + BM * 4)[tid] = dlv;
     }
+    if constexpr (M) reinterpret_cast<uint32_t*>(st + kMaskOff)[tid] = mword;
   };
   if (steps > 0) {
     issue(0);
@@ -1074,6 +1173,14 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if ((uint32_t)(mb + 8 * (r >> 2) + (r & 3)) >= pw.lim) s[r] = -INFINITY;
+      }
+      if constexpr (M) {  // this lane's key is bit l32 of word w of each row
+        const uint32_t* mt4 = reinterpret_cast<const uint32_t*>(qs + kMaskOff);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * mt + 4 * half + 8 * (r >> 2) + (r & 3);
+          if (!((mt4[4 * row + w] >> l32) & 1u)) s[r] = -INFINITY;
+        }
       }
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
@@ -1120,19 +1227,24 @@ template <int D> struct Tiles {
   static constexpr int kBwdBN = D > 128 ? 64 : 128, kBwdBM = D > 128 ? 32 : 64;
 };
 
-template <typename T, int D>
-static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
+// M: a mask combined with the window (a.mask != nullptr)
+template <typename T, int D, bool M>
+static hipError_t launch_fwd_m(const AttnArgs& a, hipStream_t st) {
   using TL = Tiles<D>;
   const int64_t nqb = (a.max_seqlen_q + TL::kFwdBM - 1) / TL::kFwdBM;
   const int64_t grid = nqb * a.heads_q * a.batch;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_kernel<T, D, TL::kFwdBM, TL::kFwdBN>), dim3((unsigned)grid), dim3(TL::kFwdBM * 2), 0,
+  hipLaunchKernelGGL((fwd_kernel<T, D, TL::kFwdBM, TL::kFwdBN, M>), dim3((unsigned)grid), dim3(TL::kFwdBM * 2), 0,
                      st, a);
   return hipGetLastError();
 }
-
 template <typename T, int D>
-static hipError_t launch_bwd_t(int stages, const AttnArgs& a, hipStream_t st) {
+static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
+  return a.mask != nullptr ? launch_fwd_m<T, D, true>(a, st) : launch_fwd_m<T, D, false>(a, st);
+}
+
+template <typename T, int D, bool M>
+static hipError_t launch_bwd_m(int stages, const AttnArgs& a, hipStream_t st) {
   using TL = Tiles<D>;
   const int64_t rows = (int64_t)a.total_q * a.heads_q;
   hipError_t e = hipSuccess;
@@ -1145,7 +1257,7 @@ static hipError_t launch_bwd_t(int stages, const AttnArgs& a, hipStream_t st) {
     const int64_t nqb = (a.max_seqlen_q + TL::kFwdBM - 1) / TL::kFwdBM;
     const int64_t g1 = nqb * a.heads_q * a.batch;
     if (g1 > 0 && rows > 0) {
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D, TL::kFwdBM, TL::kFwdBN>), dim3((unsigned)g1), dim3(TL::kFwdBM * 2),
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, TL::kFwdBM, TL::kFwdBN, M>), dim3((unsigned)g1), dim3(TL::kFwdBM * 2),
                          0, st, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1154,17 +1266,21 @@ static hipError_t launch_bwd_t(int stages, const AttnArgs& a, hipStream_t st) {
   const int64_t g2 = nkb * a.heads_kv * a.batch;
   if ((stages & 4) && g2 > 0) {
     if constexpr (D > 128)
-      hipLaunchKernelGGL((bwd_dkdv_wide_kernel<T, D, TL::kBwdBN, TL::kBwdBM>), dim3((unsigned)g2), dim3(256), 0,
+      hipLaunchKernelGGL((bwd_dkdv_wide_kernel<T, D, TL::kBwdBN, TL::kBwdBM, M>), dim3((unsigned)g2), dim3(256), 0,
                          st, a);
     else if constexpr (sizeof(T) == 2)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, TL::kBwdBN, TL::kBwdBM>), dim3((unsigned)g2),
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, TL::kBwdBN, TL::kBwdBM, M>), dim3((unsigned)g2),
                          dim3(TL::kBwdBN * 4), 0, st, a);
     else
-      hipLaunchKernelGGL((bwd_dkdv4_kernel<T, D, TL::kBwdBN, TL::kBwdBM>), dim3((unsigned)g2),
+      hipLaunchKernelGGL((bwd_dkdv4_kernel<T, D, TL::kBwdBN, TL::kBwdBM, M>), dim3((unsigned)g2),
                          dim3(TL::kBwdBN * 2), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
+}
+template <typename T, int D>
+static hipError_t launch_bwd_t(int stages, const AttnArgs& a, hipStream_t st) {
+  return a.mask != nullptr ? launch_bwd_m<T, D, true>(stages, a, st) : launch_bwd_m<T, D, false>(stages, a, st);
 }
 
 // head_dim 256 exists for the 16-bit types only (the C ABI refuses fp32 there)

@@ -415,6 +415,11 @@ struct AttnArgs {
   void* dv;
   float* delta;  // D = rowsum(dO * O), [heads_q, total_q]
   float* lse2;   // LSE * log2(e) (+inf where LSE = -inf), [heads_q, total_q]
+  // optional mask combined with the window: row t (packed query token) is
+  // mask_words uint32 words, bit j % 32 of word j / 32 allows key j of the
+  // token's sequence; nullptr = no mask
+  const uint32_t* mask;
+  int64_t mask_words;
   int32_t batch, heads_q, heads_kv, total_q, total_k, max_seqlen_q, max_seqlen_k;
   int32_t window, causal;
   float scale;

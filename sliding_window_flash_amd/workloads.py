@@ -213,9 +213,9 @@ def pack_mask(mask: np.ndarray, row_words: Optional[int] = None) -> np.ndarray:
 
 def unpack_rows(bits: np.ndarray, rows, width: int) -> np.ndarray:
     """Boolean [len(rows), width] from packed rows ``rows`` of ``bits``."""
-    sel = np.asarray(bits)[np.asarray(rows, dtype=np.int64)]
-    j = np.arange(width)
-    return ((sel[:, j // 32] >> (j % 32).astype(np.uint32)) & 1).astype(bool)
+    sel = np.ascontiguousarray(np.asarray(bits, dtype=np.uint32)[np.asarray(rows, dtype=np.int64)])
+    as_bytes = sel.astype("<u4").view(np.uint8)   # word w's byte b holds columns 32 w + 8 b ..
+    return np.unpackbits(as_bytes, axis=1, bitorder="little")[:, :width].astype(bool)
 
 
 class PackedMaskRows:

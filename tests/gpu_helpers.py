@@ -42,9 +42,10 @@ def to_device(w: Workload, x: dict) -> dict:
     return out
 
 
-def run_hip(w: Workload, dev: dict, *, window=None, poison=True, with_backward=True) -> dict:
+def run_hip(w: Workload, dev: dict, *, window=None, poison=True, with_backward=True, mask=None) -> dict:
     """Forward then backward through the C ABI. Outputs and workspace are
-    filled with NaN first, so any element the kernels fail to write shows."""
+    filled with NaN first, so any element the kernels fail to write shows.
+    ``mask``: packed mask rows on the device (the masked entry points)."""
     import torch
     window = w.window if window is None else window
     kw = dict(max_seqlen_q=w.max_seqlen_q, max_seqlen_k=w.max_seqlen_k, window=window,
@@ -55,7 +56,7 @@ def run_hip(w: Workload, dev: dict, *, window=None, poison=True, with_backward=T
     if poison:
         o.fill_(float("nan"))
         lse.fill_(float("nan"))
-    o, lse = swa.fwd(q, k, v, dev["cu_q"], dev["cu_k"], out=o, lse=lse, **kw)
+    o, lse = swa.fwd(q, k, v, dev["cu_q"], dev["cu_k"], out=o, lse=lse, mask=mask, **kw)
     res = dict(o=o, lse=lse)
     if with_backward:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -65,7 +66,8 @@ def run_hip(w: Workload, dev: dict, *, window=None, poison=True, with_backward=T
             for t in (dq, dk, dv):
                 t.fill_(float("nan"))
             ws.fill_(0xFF)
-        swa.bwd(q, k, v, o, lse, do, dev["cu_q"], dev["cu_k"], dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+        swa.bwd(q, k, v, o, lse, do, dev["cu_q"], dev["cu_k"], dq=dq, dk=dk, dv=dv, workspace=ws, mask=mask,
+                **kw)
         res.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return res
@@ -98,14 +100,16 @@ def compare(name: str, got, ref, dtype: str, zero_ref: bool = False) -> dict:
     return stats
 
 
-def full_reference(w: Workload, x: dict, window=None) -> dict:
+def full_reference(w: Workload, x: dict, window=None, mask=None) -> dict:
     window = w.window if window is None else window
+    kw = {} if mask is None else dict(mask=mask)
     return dense.sdpa_reference(x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale,
-                                window, w.causal)
+                                window, w.causal, **kw)
 
 
-def compare_full(w: Workload, x: dict, got: dict, window=None, zero=()) -> dict:
-    ref = full_reference(w, x, window)
+def compare_full(w: Workload, x: dict, got: dict, window=None, zero=(), mask=None) -> dict:
+    """``mask``: the boolean mask rows (oracle side) when the run used one."""
+    ref = full_reference(w, x, window, mask)
     out = {}
     for key in ("o", "lse", "dq", "dk", "dv"):
         if key in got:
@@ -134,18 +138,18 @@ def sample_rows(w: Workload, n_random: int, seed: int, tile: int = 128, few: boo
 
 
 def compare_sampled(w: Workload, x: dict, got: dict, n_q: int = 6, n_k: int = 3, seed: int = 0,
-                    window=None) -> dict:
+                    window=None, mask=None) -> dict:
     """Sampled query rows (O, LSE, dQ) and key rows (dK, dV) against the oracle
-    computed one row at a time."""
+    computed one row at a time. ``mask``: boolean rows or a packed-row view."""
     window = w.window if window is None else window
     rng = np.random.default_rng(seed)
     args = (x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale, window, w.causal)
     qt = sample_rows(w, n_q, seed)
     qh = rng.integers(0, w.heads_q, qt.size)
-    rq = dense.sdpa_query_rows(*args, qt, qh)
+    rq = dense.sdpa_query_rows(*args, qt, qh, mask=mask)
     kt = sample_rows(w.replace(lengths_q=w.lengths_k), n_k, seed + 1, few=True)
     kh = rng.integers(0, w.heads_kv, kt.size)
-    rk = dense.sdpa_key_rows(*args, kt, kh)
+    rk = dense.sdpa_key_rows(*args, kt, kh, mask=mask)
 
     def pick(t, i0, i1):
         return host64(t[index_tensor(i0), index_tensor(i1)])

@@ -118,3 +118,31 @@ def test_tile_sizes():
         swa.tile_sizes(256, swa.ATTN_F32)
     with pytest.raises(swa.AttnError):
         swa.tile_sizes(96, swa.ATTN_BF16)
+
+
+def _mask(bits=16, row_words=4):
+    return swa.AttnMask(bits, row_words)
+
+
+def test_masked_entry_points_refuse_before_launch():
+    """Every configuration here is refused by the checks; no kernel is launched
+    (the pointers are not device memory)."""
+    L = swa.lib()
+    p = good()   # max_seqlen_k = 100: at least 4 words per row
+    fw = lambda m, **kw: L.attn_fwd_masked(ctypes.byref(kw.get("p", p)), m, 16, 16, 16, 16, 16, 16, 16, None)
+    assert fw(None) == 1
+    assert fw(ctypes.byref(_mask(bits=None))) == 1
+    assert fw(ctypes.byref(_mask(bits=24))) == 7          # not 16-byte aligned
+    assert fw(ctypes.byref(_mask(row_words=6))) == 2      # not a multiple of 4
+    assert fw(ctypes.byref(_mask(row_words=0))) == 2
+    big = good(total_q=200, total_k=200, max_seqlen_k=200, max_seqlen_q=200)
+    assert fw(ctypes.byref(_mask(row_words=4)), p=big) == 2   # 200 keys need 7 words
+    assert fw(ctypes.byref(_mask(row_words=(1 << 24) + 4))) == 4
+    assert fw(ctypes.byref(_mask()), p=good(window=0)) == 3  # parameter checks come first
+    need = swa.workspace_bytes(p)
+    args = [16] * 11
+    bw = lambda m: L.attn_bwd_masked(ctypes.byref(p), m, *args, 16, need, None)
+    assert bw(None) == 1
+    assert bw(ctypes.byref(_mask(row_words=2))) == 2
+    assert bw(ctypes.byref(_mask(bits=8))) == 7
+    assert L.attn_bwd_masked(ctypes.byref(p), ctypes.byref(_mask()), *args, 16, need - 1, None) == 5

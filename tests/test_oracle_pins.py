@@ -35,11 +35,12 @@ def test_sampled_rows_match_full_reference():
     np.testing.assert_allclose(keys["dv"], full["dv"][ktoks, kh], atol=1e-13)
 
 
-def test_sampled_rows_match_full_reference_masked():
+@pytest.mark.parametrize("causal", [True, False])
+def test_sampled_rows_match_full_reference_masked(causal):
     """The row samplers read the same mask rows as the full reference, also
     through the packed-row view used at large sizes."""
     w = small_case([150, 90, 70], [180, 90, 70], heads_q=4, heads_kv=2, head_dim=16,
-                   window=40, seed=22)
+                   window=40, causal=causal, seed=22)
     x = make_inputs(w)
     m = W.random_mask(w, 0.7, seed=23, empty_rows=3)
     view = W.PackedMaskRows(W.pack_mask(m), 180)
