@@ -47,6 +47,14 @@ def in_window_pairs(w) -> int:
     return total * w.heads_q
 
 
+def document_pairs(w, docs) -> int:
+    """Visible cells of a causal window over one sequence packed from
+    documents (a query sees the keys of its own document only), summed over
+    query heads: the query at offset p of its document sees min(p + 1, w)."""
+    assert w.batch == 1 and w.causal and w.lengths_q == w.lengths_k
+    return w.heads_q * sum(sum(min(p + 1, w.window) for p in range(n)) for n in docs)
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
     for f in SRC_FILES:
@@ -103,7 +111,7 @@ def write_traffic(fetch_csv: str, write_csv: str, copy_mib: int, commands: list)
         for name, _, kib in rows:
             m = re.search(r"swa\d+(bwd_dkdv4_kernel|bwd_dkdv_kernel|bwd_delta_kernel|bwd_dq_kernel|fwd_kernel)",
                           name)
-            if m:
+            if m and "Lb1E" not in name:  # the masked instantiations are another workload
                 acc[KERNEL_NAMES[m.group(1)]].append(kib * 1024 * factor)
         return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
@@ -156,6 +164,9 @@ def main() -> int:
     ap.add_argument("--no-gemma", action="store_true",
                     help="skip the head_dim-256 memory-probe shape (timing and peak-bytes sweep)")
     ap.add_argument("--gemma-steps", type=int, default=10)
+    ap.add_argument("--no-masked", action="store_true",
+                    help="skip the document-mask leg (the workload's tokens packed from documents)")
+    ap.add_argument("--masked-steps", type=int, default=10)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (a known-size kernel for "
                          "scaling hardware byte counters)")
@@ -359,6 +370,40 @@ def main() -> int:
                  "peak_ratio_per_doubling": [round(gsweep["16384"] / gsweep["8192"], 3),
                                              round(gsweep["32768"] / gsweep["16384"], 3)]}
 
+    # The workload with an arbitrary mask combined with the window: its tokens
+    # packed from corpus-like documents (block-diagonal mask, bit-packed rows).
+    # Counted FLOPs are 14d per cell that both the window and the mask show.
+    masked = None
+    if not args.no_masked and w.batch == 1 and w.causal and w.lengths_q == w.lengths_k:
+        docs = W.document_lengths(91, w.lengths_k[0])
+        mt = torch.from_numpy(W.document_mask_bits(w, [docs]).view(np.int32)).to(dev)
+
+        def mstep():
+            swa.fwd(q, k, v, cu_q, cu_k, out=o2, lse=l2, mask=mt, **kw)
+            swa.bwd(q, k, v, o2, l2, do, cu_q, cu_k, dq=dq3, dk=dk3, dv=dv3, workspace=ws3, mask=mt, **kw)
+
+        o2, l2 = torch.empty_like(q), torch.empty((w.heads_q, w.total_q), dtype=torch.float32, device=dev)
+        dq3, dk3, dv3 = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws3 = torch.empty(swa.workspace_bytes(p), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            mstep()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.masked_steps):
+            mstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        m_ms = e0.elapsed_time(e1) / args.masked_steps
+        m_pairs = document_pairs(w, docs)
+        m_tf = 14 * d * m_pairs / (m_ms * 1e-3) / 1e12
+        masked = {"workload": w.name + " packed from documents", "documents": docs,
+                  "mask_bytes": int(mt.numel() * 4), "ms_per_step": round(m_ms, 4),
+                  "steps": args.masked_steps, "visible_pairs": m_pairs, "tflops": round(m_tf, 2),
+                  "pct_bf16_peak": round(100 * m_tf / BF16_DENSE_PEAK_TFLOPS, 2),
+                  "time_vs_unmasked": round(m_ms / ms_per_step, 3)}
+        del mt, o2, l2, dq3, dk3, dv3, ws3
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, x, args.cpu_rows)
@@ -387,6 +432,7 @@ def main() -> int:
         "roofline": roofline,
         "memory": mem,
         "memory_probe_shape": gemma,
+        "masked_documents": masked,
         "cpu_baseline": cpu,
         "source_hash": source_hash(),
         "device": torch.cuda.get_device_name(0),
