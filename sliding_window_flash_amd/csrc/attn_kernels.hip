@@ -176,6 +176,26 @@ __device__ __forceinline__ void apply_row_mask(f32x16& s, uint32_t word, int hal
   for (int r = 0; r < 16; ++r)
     if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) s[r] = -INFINITY;
 }
+// Key-major score tiles (one key per lane, bit `bit` of each row's word;
+// element r is query row 8 (r / 4) + 4 half + r % 4 of the block): -inf where
+// the row's bit for the lane's key is clear. Skipped when every word the wave
+// holds is all ones.
+__device__ __forceinline__ void apply_col_mask(f32x16& s, const uint32_t (&words)[16], int bit) {
+  uint32_t all = words[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) all &= words[r];
+  if (__all(all == 0xFFFFFFFFu)) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (!((words[r] >> bit) & 1u)) s[r] = -INFINITY;
+}
+// Both blocks of a 64-key tile; skipped when every lane's words are all ones
+// (a tile inside one document, say), which the wave decides as a whole.
+__device__ __forceinline__ void apply_row_mask2(f32x16 (&s)[2], const uint32_t (&mw)[2], int half) {
+  if (__all((mw[0] & mw[1]) == 0xFFFFFFFFu)) return;
+  apply_row_mask(s[0], mw[0], half);
+  apply_row_mask(s[1], mw[1], half);
+}
 
 template <int N> using ic = std::integral_constant<int, N>;
 
@@ -325,10 +345,7 @@ fwd_kernel(AttnArgs a) {
               if (jb + 32 * kt + 8 * (r >> 2) + (r & 3) >= it.lk) cur[kt][r] = -INFINITY;
         }
       }
-      if constexpr (M) {
-#pragma unroll
-        for (int kt = 0; kt < BN / 32; ++kt) apply_row_mask(cur[kt], mcur[kt], half);
-      }
+      if constexpr (M) apply_row_mask2(cur, mcur, half);
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < BN / 32; ++kt)
@@ -430,10 +447,7 @@ fwd_kernel(AttnArgs a) {
             if (jb + 32 * kt + 8 * (r >> 2) + (r & 3) >= it.lk) s[kt][r] = -INFINITY;
       }
     }
-    if constexpr (M) {
-#pragma unroll
-      for (int kt = 0; kt < BN / 32; ++kt) apply_row_mask(s[kt], mw[kt], half);
-    }
+    if constexpr (M) apply_row_mask2(s, mw, half);
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt)
@@ -601,6 +615,7 @@ bwd_dq_kernel(AttnArgs a) {
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt) {
       f32x16 s = f32x16{}, dp = f32x16{};
+      // the mask test is skipped when the whole wave's words for this block are all ones
 #pragma unroll
       for (int ss = 0; ss < D / 16; ++ss) {
         mma(s, rrd.read(ks, 32 * kt, ss), qf[ss]);
@@ -618,7 +633,9 @@ bwd_dq_kernel(AttnArgs a) {
             if (jb + 8 * (r >> 2) + (r & 3) >= it.lk) s[r] = -INFINITY;
         }
       }
-      if constexpr (M) apply_row_mask(s, mw[kt], half);
+      if constexpr (M) {
+        if (!__all(mw[kt] == 0xFFFFFFFFu)) apply_row_mask(s, mw[kt], half);
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pv = fast_exp2(fmaf(s[r], c, -lse2));
@@ -805,12 +822,11 @@ bwd_dkdv_kernel(AttnArgs a) {
     }
     if constexpr (M) {  // this lane's key is bit l32 of word kt of each row
       const char* mt = qs + kMaskOff;
+      uint32_t words[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * mh + 4 * half + 8 * (r >> 2) + (r & 3);
-        const uint32_t word = *reinterpret_cast<const uint32_t*>(mt + 16 * row + 4 * kt);
-        if (!((word >> l32) & 1u)) s[r] = -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        words[r] = *reinterpret_cast<const uint32_t*>(mt + 16 * (32 * mh + 4 * half + 8 * (r >> 2) + (r & 3)) + 4 * kt);
+      apply_col_mask(s, words, l32);
     }
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -1004,12 +1020,11 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
     }
     if constexpr (M) {  // this lane's key is bit l32 of word kt of each row
       const char* mt = qs + kMaskOff;
+      uint32_t words[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 4 * half + 8 * (r >> 2) + (r & 3);
-        const uint32_t word = *reinterpret_cast<const uint32_t*>(mt + 8 * row + 4 * kt);
-        if (!((word >> l32) & 1u)) s[r] = -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        words[r] = *reinterpret_cast<const uint32_t*>(mt + 8 * (4 * half + 8 * (r >> 2) + (r & 3)) + 4 * kt);
+      apply_col_mask(s, words, l32);
     }
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -1176,11 +1191,10 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
       }
       if constexpr (M) {  // this lane's key is bit l32 of word w of each row
         const uint32_t* mt4 = reinterpret_cast<const uint32_t*>(qs + kMaskOff);
+        uint32_t words[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 32 * mt + 4 * half + 8 * (r >> 2) + (r & 3);
-          if (!((mt4[4 * row + w] >> l32) & 1u)) s[r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r) words[r] = mt4[4 * (32 * mt + 4 * half + 8 * (r >> 2) + (r & 3)) + w];
+        apply_col_mask(s, words, l32);
       }
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
