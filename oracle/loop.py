@@ -79,3 +79,29 @@ def sdpa_loop(q, k, v, do, cu_q, cu_k, scale, window, causal, mask=None) -> dict
     dk_arr = np.array([[[math.fsum(x) for x in row] for row in head] for head in dk]).reshape(tk, hkv, d)
     dv_arr = np.array([[[math.fsum(x) for x in row] for row in head] for head in dv]).reshape(tk, hkv, d)
     return dict(o=o, lse=lse, delta=delta, dq=dq, dk=dk_arr, dv=dv_arr)
+
+
+def ce_loop(h, w, targets, dnll) -> dict:
+    """Linear cross-entropy, one token at a time in plain Python floats: the
+    logits h_i . w_v by explicit sums, the log-sum-exp over the vocabulary
+    with the largest logit factored out, and dH_i = g_i (sum_v p_iv w_v -
+    w_{y_i}) (the same definitions as ``oracle.ce``; the mlx-train-perf
+    README's logit-free cross-entropy passage). Tiny shapes only."""
+    h = np.asarray(h, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    n, dim = h.shape
+    vocab = w.shape[0]
+    nll, lse, tgt = [], [], []
+    dh = np.zeros((n, dim))
+    for i in range(n):
+        z = [_dot(h[i], w[v]) for v in range(vocab)]
+        top = max(z)
+        ls = top + math.log(math.fsum(math.exp(x - top) for x in z))
+        y = int(targets[i])
+        lse.append(ls)
+        tgt.append(z[y])
+        nll.append(ls - z[y])
+        p = [math.exp(x - ls) for x in z]
+        for c in range(dim):
+            dh[i, c] = float(dnll[i]) * (math.fsum(p[v] * w[v, c] for v in range(vocab)) - w[y, c])
+    return dict(nll=np.array(nll), lse=np.array(lse), tgt=np.array(tgt), dh=dh)

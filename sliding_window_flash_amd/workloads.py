@@ -269,3 +269,37 @@ def document_lengths(seed: int, total: int) -> list:
         out.append(min(n, left))
         left -= out[-1]
     return out
+
+
+# ------------------------------------------- linear cross-entropy (second workload)
+# The mlx-train-perf README measures its loss layer at n = 8,192 tokens,
+# vocabulary 151,936, hidden size 4,096, bf16. The hidden states and head are
+# synthetic: H ~ N(0, 1), W ~ N(0, 1) / sqrt(D) (so that the logits are of
+# order one), targets uniform over the vocabulary, upstream gradients N(0, 1)
+# (tests) or the mean loss's 1/n (bench). Draw order from default_rng(seed):
+# H, W, targets, dnll; 16-bit dtypes round H and W to nearest even.
+
+@dataclasses.dataclass(frozen=True)
+class CEWorkload:
+    name: str
+    n: int            # tokens
+    vocab: int        # V
+    hidden: int       # D
+    dtype: str        # "bf16", "fp16" or "f32"
+    seed: int
+
+
+CE_BENCH = CEWorkload("ce_bf16_n8192_v151936_d4096", 8192, 151936, 4096, "bf16", 7)
+
+
+def make_ce_inputs(w: CEWorkload, mean_dnll: bool = False) -> dict:
+    rng = np.random.default_rng(w.seed)
+    h = rng.standard_normal((w.n, w.hidden), dtype=np.float32)
+    head = rng.standard_normal((w.vocab, w.hidden), dtype=np.float32) * np.float32(1 / math.sqrt(w.hidden))
+    targets = rng.integers(0, w.vocab, w.n, dtype=np.int64).astype(np.int32)
+    dnll = rng.standard_normal(w.n, dtype=np.float32)
+    if mean_dnll:
+        dnll[:] = np.float32(1.0 / w.n)
+    if w.dtype in ("bf16", "fp16"):
+        h, head = _round_16(h, w.dtype), _round_16(head, w.dtype)
+    return dict(h=h, w=head, targets=targets, dnll=dnll)
