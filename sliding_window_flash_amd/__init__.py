@@ -27,7 +27,8 @@ BWD_DELTA, BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 4, 7
 
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_stages", "attn_bwd_workspace_bytes", "attn_status_str",
             "attn_check_params", "attn_tile_sizes", "attn_query_tile_range",
-            "attn_key_tile_range", "attn_fwd_masked", "attn_bwd_masked")
+            "attn_key_tile_range", "attn_fwd_masked", "attn_bwd_masked",
+            "ce_check_params", "ce_fwd_workspace_bytes", "ce_fwd", "ce_bwd_workspace_bytes", "ce_bwd")
 
 
 class AttnError(RuntimeError):
@@ -44,6 +45,12 @@ class AttnParams(ctypes.Structure):
         ("window", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
     ]
+
+
+class CEParams(ctypes.Structure):
+    """ce_params_t (include/swa_ce.h)."""
+    _fields_ = [("n", ctypes.c_int32), ("vocab", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
 
 
 class AttnMask(ctypes.Structure):
@@ -79,6 +86,17 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_masked.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       ctypes.c_size_t, vp]
         L.attn_bwd_masked.restype = ctypes.c_int
+        C = ctypes.POINTER(CEParams)
+        L.ce_check_params.argtypes = [C]
+        L.ce_check_params.restype = ctypes.c_int
+        L.ce_fwd_workspace_bytes.argtypes = [C]
+        L.ce_fwd_workspace_bytes.restype = ctypes.c_size_t
+        L.ce_bwd_workspace_bytes.argtypes = [C]
+        L.ce_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.ce_fwd.argtypes = [C, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.ce_fwd.restype = ctypes.c_int
+        L.ce_bwd.argtypes = [C, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.ce_bwd.restype = ctypes.c_int
         L.attn_status_str.argtypes = [ctypes.c_int]
         L.attn_status_str.restype = ctypes.c_char_p
         L.attn_check_params.argtypes = [P]
@@ -249,3 +267,54 @@ def bwd(q, k, v, o, lse, do, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=I
     if st:
         raise AttnError(st, what)
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------- linear cross-entropy
+def ce_params(n: int, vocab: int, hidden: int, dtype: int) -> CEParams:
+    return CEParams(n, vocab, hidden, dtype)
+
+
+def ce_params_for(h, w) -> CEParams:
+    torch = _torch()
+    dt = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16, torch.float32: ATTN_F32}.get(h.dtype)
+    if dt is None or w.dtype != h.dtype:
+        raise AttnError(4, f"dtypes {h.dtype}, {w.dtype}")
+    return CEParams(h.shape[0], w.shape[0], h.shape[1], dt)
+
+
+def ce_fwd(h, w, targets, *, nll=None, lse=None, tgt=None, workspace=None, stream=None):
+    """Per-token loss, LSE and target logit (fp32 [n] each) of the linear
+    cross-entropy with logits h @ w.T, through ce_fwd (no logits tensor)."""
+    torch = _torch()
+    for t, nme in ((h, "h"), (w, "w"), (targets, "targets")):
+        _require(t, nme)
+    p = ce_params_for(h, w)
+    n = h.shape[0]
+    nll = torch.empty(n, dtype=torch.float32, device=h.device) if nll is None else nll
+    lse = torch.empty(n, dtype=torch.float32, device=h.device) if lse is None else lse
+    tgt = torch.empty(n, dtype=torch.float32, device=h.device) if tgt is None else tgt
+    if workspace is None:
+        workspace = torch.empty(max(lib().ce_fwd_workspace_bytes(ctypes.byref(p)), 1), dtype=torch.uint8,
+                                device=h.device)
+    st = lib().ce_fwd(ctypes.byref(p), _ptr(h), _ptr(w), _ptr(targets), _ptr(nll), _ptr(lse), _ptr(tgt),
+                      _ptr(workspace), workspace.numel(), _stream_ptr(stream))
+    if st:
+        raise AttnError(st, "ce_fwd")
+    return nll, lse, tgt
+
+
+def ce_bwd(h, w, targets, lse, dnll, *, dh=None, workspace=None, stream=None):
+    """dH [n, hidden] (h.dtype) of sum(dnll * nll), through ce_bwd."""
+    torch = _torch()
+    for t, nme in ((h, "h"), (w, "w"), (targets, "targets"), (lse, "lse"), (dnll, "dnll")):
+        _require(t, nme)
+    p = ce_params_for(h, w)
+    dh = torch.empty_like(h) if dh is None else dh
+    if workspace is None:
+        workspace = torch.empty(max(lib().ce_bwd_workspace_bytes(ctypes.byref(p)), 1), dtype=torch.uint8,
+                                device=h.device)
+    st = lib().ce_bwd(ctypes.byref(p), _ptr(h), _ptr(w), _ptr(targets), _ptr(lse), _ptr(dnll), _ptr(dh),
+                      _ptr(workspace), workspace.numel(), _stream_ptr(stream))
+    if st:
+        raise AttnError(st, "ce_bwd")
+    return dh

@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libswa_attn.so")
-SOURCES = ["api.hip", "attn_kernels.hip"]
+SOURCES = ["api.hip", "attn_kernels.hip", "ce_kernels.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -4,6 +4,8 @@
 #include <stdint.h>
 
 #include "../../include/swa_attn.h"
+#include "../../include/swa_ce.h"
+#include "ce_launch.hpp"
 #include "launch.hpp"
 #include "sched.hpp"
 
@@ -287,6 +289,95 @@ attn_status_t attn_key_tile_range(const attn_params_t* p, const int32_t* cu_seql
   const swa::TileRange r = swa::key_tile_queries(g, kb, bn, bm);
   *qb_lo = r.lo;
   *qb_hi = r.hi;
+  return ATTN_OK;
+}
+
+// ------------------------------------------------------ linear cross-entropy
+
+attn_status_t ce_check_params(const ce_params_t* p) {
+  if (p == nullptr) return ATTN_ERR_NULL;
+  if (p->n < 0 || p->vocab < 1 || p->hidden < 256 || p->hidden % 256 != 0) return ATTN_ERR_SHAPE;
+  if ((int64_t)p->n * p->hidden > INT32_MAX || (int64_t)p->vocab * p->hidden > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (p->dtype != ATTN_BF16 && p->dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+size_t ce_fwd_workspace_bytes(const ce_params_t* p) {
+  if (ce_check_params(p) != ATTN_OK) return 0;
+  const size_t tiles = (size_t)(p->vocab + 255) / 256;
+  return round_up(tiles * (size_t)(p->n > 0 ? p->n : 1) * 8, 256);
+}
+
+static size_t ce_dz_bytes(const ce_params_t* p) {
+  const size_t ldz = (size_t)(swa::ce_vocab_chunk(p->vocab) + 63) / 64 * 64;
+  return round_up((size_t)(p->n > 0 ? p->n : 1) * ldz * 2, 256);
+}
+
+size_t ce_bwd_workspace_bytes(const ce_params_t* p) {
+  if (ce_check_params(p) != ATTN_OK) return 0;
+  size_t b = ce_dz_bytes(p);
+  if (p->vocab > swa::ce_vocab_chunk(p->vocab)) b += round_up((size_t)p->n * p->hidden * 4, 256);
+  return b;
+}
+
+static swa::CEArgs ce_args(const ce_params_t* p) {
+  swa::CEArgs a{};
+  a.n = p->n;
+  a.vocab = p->vocab;
+  a.hidden = p->hidden;
+  return a;
+}
+
+attn_status_t ce_fwd(const ce_params_t* p, const void* h, const void* w, const int32_t* targets,
+                     float* nll, float* lse, float* target_logit, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  attn_status_t s = ce_check_params(p);
+  if (s != ATTN_OK) return s;
+  const int64_t nh = (int64_t)p->n * p->hidden, vh = (int64_t)p->vocab * p->hidden;
+  if ((s = check_tensor(h, nh, true)) != ATTN_OK) return s;
+  if ((s = check_tensor(w, vh, true)) != ATTN_OK) return s;
+  if ((s = check_tensor(targets, p->n, false)) != ATTN_OK) return s;
+  if ((s = check_tensor(nll, p->n, false)) != ATTN_OK) return s;
+  if ((s = check_tensor(lse, p->n, false)) != ATTN_OK) return s;
+  if ((s = check_tensor(target_logit, p->n, false)) != ATTN_OK) return s;
+  if (workspace == nullptr || workspace_bytes < ce_fwd_workspace_bytes(p)) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  swa::CEArgs a = ce_args(p);
+  a.h = h;
+  a.w = w;
+  a.targets = targets;
+  a.nll = nll;
+  a.out_lse = lse;
+  a.tgt = target_logit;
+  a.part = static_cast<float*>(workspace);
+  if (swa::launch_ce_fwd(p->dtype, a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+attn_status_t ce_bwd(const ce_params_t* p, const void* h, const void* w, const int32_t* targets,
+                     const float* lse, const float* dnll, void* dh, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  attn_status_t s = ce_check_params(p);
+  if (s != ATTN_OK) return s;
+  const int64_t nh = (int64_t)p->n * p->hidden, vh = (int64_t)p->vocab * p->hidden;
+  if ((s = check_tensor(h, nh, true)) != ATTN_OK) return s;
+  if ((s = check_tensor(w, vh, true)) != ATTN_OK) return s;
+  if ((s = check_tensor(targets, p->n, false)) != ATTN_OK) return s;
+  if ((s = check_tensor(lse, p->n, false)) != ATTN_OK) return s;
+  if ((s = check_tensor(dnll, p->n, false)) != ATTN_OK) return s;
+  if ((s = check_tensor(dh, nh, true)) != ATTN_OK) return s;
+  if (workspace == nullptr || workspace_bytes < ce_bwd_workspace_bytes(p)) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  swa::CEArgs a = ce_args(p);
+  a.h = h;
+  a.w = w;
+  a.targets = targets;
+  a.lse = lse;
+  a.dnll = dnll;
+  a.dh = dh;
+  a.dz = workspace;
+  a.dh32 = reinterpret_cast<float*>(static_cast<char*>(workspace) + ce_dz_bytes(p));
+  if (swa::launch_ce_bwd(p->dtype, a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
 }
 

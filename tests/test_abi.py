@@ -12,9 +12,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "swa_attn.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+    names = set()
+    for hdr in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if hdr.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", hdr)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b((?:attn|ce)_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported():
@@ -146,3 +150,41 @@ def test_masked_entry_points_refuse_before_launch():
     assert bw(ctypes.byref(_mask(row_words=2))) == 2
     assert bw(ctypes.byref(_mask(bits=8))) == 7
     assert L.attn_bwd_masked(ctypes.byref(p), ctypes.byref(_mask()), *args, 16, need - 1, None) == 5
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 0),
+    (dict(n=0), 0),
+    (dict(n=-1), 2),
+    (dict(vocab=0), 2),
+    (dict(hidden=300), 2),
+    (dict(hidden=0), 2),
+    (dict(dtype=swa.ATTN_F32), 4),
+    (dict(dtype=9), 4),
+    (dict(n=1 << 20, hidden=4096), 2),   # n * hidden >= 2^31
+])
+def test_ce_parameter_checks(kw, code):
+    base = dict(n=100, vocab=1000, hidden=512, dtype=swa.ATTN_BF16)
+    base.update(kw)
+    assert swa.lib().ce_check_params(ctypes.byref(swa.ce_params(**base))) == code
+
+
+def test_ce_refuses_before_launch():
+    """Every call here is refused by the checks (the pointers are not device memory)."""
+    L = swa.lib()
+    p = swa.ce_params(100, 1000, 512, swa.ATTN_BF16)
+    fw = L.ce_fwd_workspace_bytes(ctypes.byref(p))
+    bw = L.ce_bwd_workspace_bytes(ctypes.byref(p))
+    assert fw >= 4 * 100 * 8 and fw % 256 == 0 and bw >= 100 * 1024 * 2
+    assert L.ce_fwd(None, 16, 16, 16, 16, 16, 16, 16, fw, None) == 1
+    assert L.ce_fwd(ctypes.byref(p), None, 16, 16, 16, 16, 16, 16, fw, None) == 1
+    assert L.ce_fwd(ctypes.byref(p), 24, 16, 16, 16, 16, 16, 16, fw, None) == 7
+    assert L.ce_fwd(ctypes.byref(p), 16, 16, 16, 16, 16, 16, 16, fw - 1, None) == 5
+    assert L.ce_fwd(ctypes.byref(p), 16, 16, 16, 16, 16, 16, None, fw, None) == 5
+    assert L.ce_bwd(ctypes.byref(p), 16, 16, 16, 16, 16, 16, 16, bw - 1, None) == 5
+    assert L.ce_bwd(ctypes.byref(p), 16, 16, 16, 16, None, 16, 16, bw, None) == 1
+    assert L.ce_bwd(ctypes.byref(swa.ce_params(100, 1000, 512, swa.ATTN_F32)), 16, 16, 16, 16, 16, 16, 16, bw,
+                    None) == 4
+    # several vocabulary chunks need the fp32 dH accumulator as well
+    big = swa.ce_params(64, 40000, 256, swa.ATTN_BF16)
+    assert L.ce_bwd_workspace_bytes(ctypes.byref(big)) >= 64 * 16384 * 2 + 64 * 256 * 4
