@@ -15,6 +15,7 @@ Prints one JSON line. With --gpus N > 1 it exits: this path runs on one GPU.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -167,6 +168,9 @@ def main() -> int:
     ap.add_argument("--no-masked", action="store_true",
                     help="skip the document-mask leg (the workload's tokens packed from documents)")
     ap.add_argument("--masked-steps", type=int, default=10)
+    ap.add_argument("--no-ce", action="store_true",
+                    help="skip the linear cross-entropy leg (the second workload)")
+    ap.add_argument("--ce-steps", type=int, default=5)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (a known-size kernel for "
                          "scaling hardware byte counters)")
@@ -404,6 +408,55 @@ def main() -> int:
                   "time_vs_unmasked": round(m_ms / ms_per_step, 3)}
         del mt, o2, l2, dq3, dk3, dv3, ws3
 
+    # The second workload: the linear cross-entropy without the logits tensor
+    # at the mlx-train-perf README's loss-layer shape. Forward 2 n V D FLOPs
+    # (the logits), backward 4 n V D (the logits again and dH = dz W).
+    ce_leg = None
+    if not args.no_ce:
+        cw = W.CE_BENCH
+        g = torch.Generator(device=dev).manual_seed(cw.seed)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base_mem = torch.cuda.memory_allocated()
+        ch = torch.randn((cw.n, cw.hidden), generator=g, device=dev).to(torch.bfloat16)
+        cwh = (torch.randn((cw.vocab, cw.hidden), generator=g, device=dev) / math.sqrt(cw.hidden)).to(torch.bfloat16)
+        ct = torch.randint(0, cw.vocab, (cw.n,), generator=g, device=dev, dtype=torch.int32)
+        cg = torch.full((cw.n,), 1.0 / cw.n, device=dev)
+        torch.cuda.synchronize()
+        inputs_mem = torch.cuda.memory_allocated() - base_mem
+        torch.cuda.reset_peak_memory_stats()
+        nll_, lse_, tgt_ = swa.ce_fwd(ch, cwh, ct)
+        dh_ = swa.ce_bwd(ch, cwh, ct, lse_, cg)
+        torch.cuda.synchronize()
+        ce_peak = torch.cuda.max_memory_allocated() - base_mem - inputs_mem
+        fws = torch.empty(swa.lib().ce_fwd_workspace_bytes(ctypes.byref(swa.ce_params_for(ch, cwh))),
+                          dtype=torch.uint8, device=dev)
+        bws = torch.empty(swa.lib().ce_bwd_workspace_bytes(ctypes.byref(swa.ce_params_for(ch, cwh))),
+                          dtype=torch.uint8, device=dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        fms, bms = [], []
+        for it in range(args.ce_steps + 1):
+            ev[0].record(stream)
+            swa.ce_fwd(ch, cwh, ct, nll=nll_, lse=lse_, tgt=tgt_, workspace=fws)
+            ev[1].record(stream)
+            swa.ce_bwd(ch, cwh, ct, lse_, cg, dh=dh_, workspace=bws)
+            ev[2].record(stream)
+            torch.cuda.synchronize()
+            if it:  # the first pass is a warmup
+                fms.append(ev[0].elapsed_time(ev[1]))
+                bms.append(ev[1].elapsed_time(ev[2]))
+        f_ms, b_ms = float(np.mean(fms)), float(np.mean(bms))
+        nvd = cw.n * cw.vocab * cw.hidden
+        ce_leg = {"workload": cw.name, "tokens": cw.n, "vocab": cw.vocab, "hidden": cw.hidden, "dtype": cw.dtype,
+                  "steps": args.ce_steps, "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+                  "fwd_tflops": round(2 * nvd / (f_ms * 1e-3) / 1e12, 2),
+                  "bwd_tflops": round(4 * nvd / (b_ms * 1e-3) / 1e12, 2),
+                  "fwd_pct_bf16_peak": round(100 * 2 * nvd / (f_ms * 1e-3) / 1e12 / BF16_DENSE_PEAK_TFLOPS, 2),
+                  "bwd_pct_bf16_peak": round(100 * 4 * nvd / (b_ms * 1e-3) / 1e12 / BF16_DENSE_PEAK_TFLOPS, 2),
+                  "peak_above_inputs_gb": round(ce_peak / 1e9, 4),
+                  "logits_tensor_not_built_gb": round(cw.n * cw.vocab * 2 / 1e9, 3)}
+        del ch, cwh, ct, cg, nll_, lse_, tgt_, dh_, fws, bws
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, x, args.cpu_rows)
@@ -433,6 +486,7 @@ def main() -> int:
         "memory": mem,
         "memory_probe_shape": gemma,
         "masked_documents": masked,
+        "linear_cross_entropy": ce_leg,
         "cpu_baseline": cpu,
         "source_hash": source_hash(),
         "device": torch.cuda.get_device_name(0),
