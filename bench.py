@@ -101,9 +101,11 @@ def write_traffic(fetch_csv: str, write_csv: str, copy_mib: int, commands: list)
 
     fetch, write = read(fetch_csv, "FETCH_SIZE"), read(write_csv, "WRITE_SIZE")
     known = copy_mib << 20
-    # the calibration copy: the non-attention dispatch that reads the most (a
-    # fill writes as much but reads nothing), and the same kernel's write
-    cf = max((r for r in fetch if "swa" not in r[0]), key=lambda r: r[2])
+    # the calibration copy: the runtime's copy kernel (torch's device copy_)
+    # that reads the most, else the non-attention dispatch that reads the most
+    # (a fill writes as much but reads nothing); then the same kernel's write
+    copies = [r for r in fetch if "copyBuffer" in r[0]]
+    cf = max(copies or [r for r in fetch if "swa" not in r[0]], key=lambda r: r[2])
     cw = max((r for r in write if r[0] == cf[0] and r[1] == cf[1]), key=lambda r: r[2])
     f_fetch, f_write = known / (cf[2] * 1024), known / (cw[2] * 1024)
 

@@ -348,22 +348,40 @@ __global__ void __launch_bounds__(kThreads) ce_dh_kernel(CEArgs a, int first, in
 }
 
 // Per token: fold the per-tile (max, sum) partials into LSE (natural log) and
-// the loss. A target outside [0, V) was never found: its logit stays NaN.
-__global__ void __launch_bounds__(256) ce_reduce_kernel(CEArgs a) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= a.n) return;
+// the loss. A block takes 16 tokens; its 16 thread groups split the vocabulary
+// tiles (reads of 16 consecutive tokens stay contiguous) and combine through
+// LDS. A target outside [0, V) was never found: its logit stays NaN.
+constexpr int kRedTok = 16, kRedGrp = 16;
+__global__ void __launch_bounds__(kRedTok * kRedGrp) ce_reduce_kernel(CEArgs a) {
+  __shared__ float2 acc[kRedGrp][kRedTok];
+  const int tl = threadIdx.x % kRedTok, grp = threadIdx.x / kRedTok;
+  const int t = blockIdx.x * kRedTok + tl;
   const int num_v = (a.vocab + kTile - 1) / kTile;
-  const float2* part = reinterpret_cast<const float2*>(a.part) + t;
-  float m = -INFINITY;
-  for (int v = 0; v < num_v; ++v) m = fmaxf(m, part[(int64_t)v * a.n].x);
-  float s = 0.f;
-  for (int v = 0; v < num_v; ++v) {
-    const float2 p = part[(int64_t)v * a.n];
-    if (p.x != -INFINITY) s += p.y * fast_exp2(p.x - m);
+  float m = -INFINITY, s = 0.f;
+  if (t < a.n) {
+    const float2* part = reinterpret_cast<const float2*>(a.part) + t;
+    for (int v = grp; v < num_v; v += kRedGrp) {
+      const float2 p = part[(int64_t)v * a.n];
+      if (p.x == -INFINITY) continue;
+      const float mn = fmaxf(m, p.x);
+      s = (m == -INFINITY ? 0.f : s * fast_exp2(m - mn)) + p.y * fast_exp2(p.x - mn);
+      m = mn;
+    }
   }
-  const float lse = (m + fast_log2(s)) * kLn2;
-  a.out_lse[t] = lse;
-  a.nll[t] = lse - a.tgt[t];
+  acc[grp][tl] = make_float2(m, s);
+  __syncthreads();
+  if (grp == 0 && t < a.n) {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < kRedGrp; ++g) mt = fmaxf(mt, acc[g][tl].x);
+    float st = 0.f;
+#pragma unroll
+    for (int g = 0; g < kRedGrp; ++g)
+      if (acc[g][tl].x != -INFINITY) st += acc[g][tl].y * fast_exp2(acc[g][tl].x - mt);
+    const float lse = (mt + fast_log2(st)) * kLn2;
+    a.out_lse[t] = lse;
+    a.nll[t] = lse - a.tgt[t];
+  }
 }
 
 // the target logits start as NaN (a target outside [0, V) is never found)
@@ -388,7 +406,8 @@ static hipError_t ce_fwd_t(const CEArgs& a0, hipStream_t st) {
   hipLaunchKernelGGL(ce_fill_nan_kernel, dim3((unsigned)((a.n + 255) / 256)), dim3(256), 0, st, a.tgt, a.n);
   const int64_t grid = (int64_t)((a.vocab + kTile - 1) / kTile) * ((a.n + kTile - 1) / kTile);
   hipLaunchKernelGGL((ce_logits_kernel<T, kFwd>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL(ce_reduce_kernel, dim3((unsigned)((a.n + 255) / 256)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(ce_reduce_kernel, dim3((unsigned)((a.n + kRedTok - 1) / kRedTok)), dim3(kRedTok * kRedGrp), 0,
+                     st, a);
   return hipGetLastError();
 }
 
