@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import gpu_helpers as H
+import sliding_window_flash_amd as swa
 from sliding_window_flash_amd import workloads as W
 from sliding_window_flash_amd.workloads import INT32_MAX, make_inputs, small_case
 
@@ -128,6 +129,29 @@ def test_backward_is_deterministic():
     import torch
     for key in a:
         assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64), ("fp16", 256)])
+def test_stages_run_separately(dt, d):
+    """attn_bwd_stages one stage at a time (the D preprocess as its own launch,
+    dQ reading D from the workspace) and with dK/dV before dQ, against the
+    oracle; attn_bwd fuses D into dQ instead."""
+    import torch
+    w = small_case([300, 77], [340, 77], heads_q=4, heads_kv=2, head_dim=d, window=90, dtype=dt,
+                   do_scale=1.0 if dt == "f32" else 0.1, seed=36)
+    x = make_inputs(w)
+    dev = H.to_device(w, x)
+    kw = dict(max_seqlen_q=w.max_seqlen_q, max_seqlen_k=w.max_seqlen_k, window=w.window, causal=w.causal,
+              scale=w.scale)
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o, lse = swa.fwd(q, k, v, dev["cu_q"], dev["cu_k"], **kw)
+    dq, dk, dv = torch.full_like(q, float("nan")), torch.full_like(k, float("nan")), torch.full_like(v, float("nan"))
+    ws = torch.full((swa.workspace_bytes(swa.params_for(q, k, dev["cu_q"], dev["cu_k"], **kw)),), 255,
+                    dtype=torch.uint8, device=q.device)
+    for stage in (swa.BWD_DELTA, swa.BWD_DKDV, swa.BWD_DQ):
+        swa.bwd(q, k, v, o, lse, do, dev["cu_q"], dev["cu_k"], dq=dq, dk=dk, dv=dv, workspace=ws, stages=stage, **kw)
+    torch.cuda.synchronize()
+    H.compare_full(w, x, dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv))
 
 
 def test_gqa_2k_full_oracle():
