@@ -112,24 +112,6 @@ template <typename T, int ROWS, int D> struct LdsTile {
   }
 };
 
-// Cooperative global -> LDS copy of `rows` rows (row r from src + r*stride
-// elements), zero-filling rows >= valid. 16-byte vector loads and stores.
-template <typename T, int ROWS, int D, int NTHREADS>
-__device__ __forceinline__ void load_tile(char* lds, const T* __restrict__ src, int64_t stride,
-                                          int valid, int tid) {
-  using Tile = LdsTile<T, ROWS, D>;
-  constexpr int kTotal = ROWS * Tile::kChunks;
-#pragma unroll
-  for (int idx = tid; idx < kTotal; idx += NTHREADS) {
-    const int r = idx / Tile::kChunks;
-    const int c = idx % Tile::kChunks;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (r < valid)
-      val = *reinterpret_cast<const u32x4*>(src + (int64_t)r * stride + c * Tile::kElemsPerChunk);
-    *reinterpret_cast<u32x4*>(lds + Tile::chunk_off(r, c)) = val;
-  }
-}
-
 // Operand fragment read along a row: row `row`, contraction elements
 // [8*k8, 8*k8+8) of that row.
 template <typename T, int ROWS, int D>
