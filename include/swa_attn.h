@@ -192,9 +192,11 @@ const char* attn_status_str(attn_status_t s);
 attn_status_t attn_check_params(const attn_params_t* p);
 
 /* Tile sizes the compiled kernels use for (head_dim, dtype): query rows per
- * forward/dQ tile, key rows per forward/dQ step, key rows per dK/dV tile and
- * query rows per dK/dV step. Returns ATTN_ERR_UNSUPPORTED for an unsupported
- * pair. Host only. */
+ * forward/dQ workgroup counted over its heads (4 waves of 32 rows: with a KV
+ * group of 4k query heads a workgroup takes 4 heads x 32 rows, with 2k heads
+ * 2 x 64, otherwise 1 x 128), key rows per forward/dQ step, key rows per dK/dV
+ * tile and query rows per dK/dV step. Returns ATTN_ERR_UNSUPPORTED for an
+ * unsupported pair. Host only. */
 attn_status_t attn_tile_sizes(int32_t head_dim, int32_t dtype, int32_t* fwd_bm,
                               int32_t* fwd_bn, int32_t* bwd_bn, int32_t* bwd_bm);
 

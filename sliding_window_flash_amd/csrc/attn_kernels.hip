@@ -24,9 +24,8 @@
 // error against fp32 score tiles).
 //
 // Every kernel streams its shared operand tiles (K/V, or Q/dO) through two LDS
-// stages: the next tile's global loads are issued into registers before the
-// current tile's MFMAs and written to the other stage after them, so one
-// barrier per step suffices.
+// stages: the next tile's global-to-LDS loads are issued during the current
+// step into the other stage and waited for at the step's one barrier.
 #include <math.h>
 
 #include <type_traits>
@@ -112,28 +111,40 @@ __device__ __forceinline__ void fill_kv(const TileLoader<T, BN, D, NT>& ld, char
   fill_tile(ld, st + LdsTile<T, BN, D>::kBytes, V, kstride, kb, lk);
 }
 
-struct QueryItem {
-  int qb, h, b, q0, lq, k0, lk;
+// Query-major work items (forward and dQ). A workgroup's 4 waves take HW query
+// heads of one KV group (HW = 4, 2 or 1: the largest that divides the group)
+// and 128 / HW query rows, 32 rows per wave. All of them read the same K/V
+// tiles, and the key range the workgroup visits spans the window plus 32 or
+// 64 rows instead of 128, so fewer key tiles are computed only in part (at a
+// 1,024 window: 17 instead of 19 64-key tiles per 32-row wave).
+__host__ __device__ inline int query_heads_per_wg(int heads_q, int heads_kv) {
+  const int grp = heads_q / heads_kv;
+  return grp % 4 == 0 ? 4 : (grp % 2 == 0 ? 2 : 1);
+}
+struct GroupedItem {
+  int qb, rows, h, b, q0, lq, k0, lk, g, row0;  // row0: first row of this wave
 };
-
-// Query-major work decode. Logical order: KV head (outermost), sequence, query
-// tile (descending: for the causal mask later tiles see more keys, so the
-// longest run first), head within the KV group (innermost, so the G heads
-// sharing K/V run together). The launch id is remapped so that each XCD runs
-// a contiguous logical range.
-__device__ __forceinline__ QueryItem decode_query_item(const AttnArgs& a, int bm) {
-  QueryItem it;
-  const int nqb = (a.max_seqlen_q + bm - 1) / bm;
+// Logical order: KV head (outermost), sequence, row block (descending: under
+// the causal mask later blocks see more keys, so the longest run first), head
+// chunk within the group (innermost). The launch id is remapped so that each
+// XCD runs a contiguous logical range.
+__device__ __forceinline__ GroupedItem decode_grouped_item(const AttnArgs& a, int w) {
+  GroupedItem it;
+  const int hw = query_heads_per_wg(a.heads_q, a.heads_kv);
   const int grp = a.heads_q / a.heads_kv;
-  const int n = nqb * a.heads_q * a.batch;
+  const int nch = grp / hw;
+  it.rows = 128 / hw;
+  const int nqb = (a.max_seqlen_q + it.rows - 1) / it.rows;
+  const int n = nqb * a.heads_kv * nch * a.batch;
   int L = xcd_remap((int)blockIdx.x, n);
-  const int hh = L % grp;
-  L /= grp;
+  const int ch = L % nch;
+  L /= nch;
   it.qb = nqb - 1 - L % nqb;
   L /= nqb;
   it.b = L % a.batch;
-  const int g = L / a.batch;
-  it.h = g * grp + hh;
+  it.g = L / a.batch;
+  it.h = it.g * grp + ch * hw + w % hw;
+  it.row0 = it.qb * it.rows + 32 * (w / hw);
   it.q0 = a.cu_q[it.b];
   it.lq = a.cu_q[it.b + 1] - it.q0;
   it.k0 = a.cu_k[it.b];
@@ -252,11 +263,11 @@ fwd_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int w = wave_uniform(tid >> 6);
-  const QueryItem it = decode_query_item(a, BM);
-  if (it.qb * BM >= it.lq) return;
-  const int g = it.h / (a.heads_q / a.heads_kv);
+  const GroupedItem it = decode_grouped_item(a, w);
+  if (it.qb * it.rows >= it.lq) return;
+  const int g = it.g;
   const SeqGeom sg{it.lq, it.lk, a.window, a.causal != 0};
-  const TileRange kr = query_tile_keys(sg, it.qb, BM, BN);
+  const TileRange kr = query_tile_keys(sg, it.qb, it.rows, BN);
 
   const int64_t qstride = (int64_t)a.heads_q * D;
   const int64_t kstride = (int64_t)a.heads_kv * D;
@@ -264,7 +275,7 @@ fwd_kernel(AttnArgs a) {
   const T* __restrict__ K = static_cast<const T*>(a.k) + (int64_t)it.k0 * kstride + g * D;
   const T* __restrict__ V = static_cast<const T*>(a.v) + (int64_t)it.k0 * kstride + g * D;
 
-  const int i = it.qb * BM + w * 32 + l32;  // this lane's query row
+  const int i = it.row0 + l32;  // this lane's query row
   const bool row_ok = i < it.lq;
   const int64_t mrow = it.q0 + (row_ok ? i : 0);  // its mask row (with M)
   Frag<T> qf[D / 16];
@@ -545,18 +556,18 @@ bwd_dq_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int w = wave_uniform(tid >> 6);
-  const QueryItem it = decode_query_item(a, BM);
-  if (it.qb * BM >= it.lq) return;
-  const int g = it.h / (a.heads_q / a.heads_kv);
+  const GroupedItem it = decode_grouped_item(a, w);
+  if (it.qb * it.rows >= it.lq) return;
+  const int g = it.g;
   const SeqGeom sg{it.lq, it.lk, a.window, a.causal != 0};
-  const TileRange kr = query_tile_keys(sg, it.qb, BM, BN);
+  const TileRange kr = query_tile_keys(sg, it.qb, it.rows, BN);
 
   const int64_t qstride = (int64_t)a.heads_q * D;
   const int64_t kstride = (int64_t)a.heads_kv * D;
   const T* __restrict__ K = static_cast<const T*>(a.k) + (int64_t)it.k0 * kstride + g * D;
   const T* __restrict__ V = static_cast<const T*>(a.v) + (int64_t)it.k0 * kstride + g * D;
 
-  const int i = it.qb * BM + w * 32 + l32;
+  const int i = it.row0 + l32;
   const bool row_ok = i < it.lq;
   const int64_t mrow = it.q0 + (row_ok ? i : 0);  // its mask row (with M)
   Frag<T> qf[D / 16], df[D / 16];
@@ -606,7 +617,7 @@ bwd_dq_kernel(AttnArgs a) {
     if (kb < kr.hi) fill_kv(kvld, stage ? st0 : st1, K, V, kstride, kb + 1, it.lk);
     const bool edge = !(kr.full_lo <= kb && kb <= kr.full_hi);
     // all cells masked for this wave's 32 rows: dS = 0, nothing to add
-    if (edge && block_masked(it.lq, it.lk, a.window, a.causal != 0, it.qb * BM + 32 * w, 32, kb * BN, BN)) {
+    if (edge && block_masked(it.lq, it.lk, a.window, a.causal != 0, it.row0, 32, kb * BN, BN)) {
       __syncthreads();
       return;
     }
@@ -795,10 +806,10 @@ bwd_dkdv_kernel(AttnArgs a) {
     const char* dos = qs + QTile::kBytes;
     const float* lse2s = reinterpret_cast<const float*>(qs + 2 * QTile::kBytes);
     const float* dlts = lse2s + BM;
-    if (t + 1 < steps) fill(stage ? st0 : st1);
     const bool edge = !tile_full_i32(lq, lk, a.window, causal, qb, BM, kb, BN);
     // this wave's 32 keys x 32 queries all masked: P = dS = 0, nothing to add
     if (edge && block_masked(lq, lk, a.window, causal, qb * BM + 32 * mh, 32, kb * BN + 32 * kt, 32)) {
+      if (t + 1 < steps) fill(stage ? st0 : st1);
       if (++qb > qr.hi) qb = qr.lo;
       __syncthreads();
       return;
@@ -841,6 +852,10 @@ bwd_dkdv_kernel(AttnArgs a) {
         dp[r] = pv * (dp[r] - d4[e]);  // dS
       }
     }
+    // the next step's stage is filled here, after this step's row reads and
+    // softmax, not at the top of the step, where the loads met the burst of
+    // row reads every wave makes (moving them here cut dK/dV time by 4%)
+    if (t + 1 < steps) fill(stage ? st0 : st1);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const Frag<T> pf = acc_frag<T>(s, u);
@@ -1231,8 +1246,9 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------- launchers
-// Tile shapes (every dtype): forward and dQ take 128 query rows (4 waves of
-// 32) and step over keys 64 at a time. dK/dV takes 128 keys (8 waves: 4 key
+// Tile shapes (every dtype): forward and dQ take 4 waves of 32 query rows (4,
+// 2 or 1 heads of a KV group x 32, 64 or 128 rows; query_heads_per_wg) and
+// step over keys 64 at a time. dK/dV takes 128 keys (8 waves: 4 key
 // blocks of 32 x 2 query halves; fp32: 4 waves) and steps over queries 64 at a
 // time; at head_dim 256 it takes 64 keys (4 waves: 2 key blocks x 2 dim
 // halves) and steps over queries 32 at a time.
@@ -1245,8 +1261,9 @@ template <int D> struct Tiles {
 template <typename T, int D, bool M>
 static hipError_t launch_fwd_m(const AttnArgs& a, hipStream_t st) {
   using TL = Tiles<D>;
-  const int64_t nqb = (a.max_seqlen_q + TL::kFwdBM - 1) / TL::kFwdBM;
-  const int64_t grid = nqb * a.heads_q * a.batch;
+  const int hw = query_heads_per_wg(a.heads_q, a.heads_kv);
+  const int64_t nqb = (a.max_seqlen_q + 128 / hw - 1) / (128 / hw);
+  const int64_t grid = nqb * (a.heads_q / hw) * a.batch;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((fwd_kernel<T, D, TL::kFwdBM, TL::kFwdBN, M>), dim3((unsigned)grid), dim3(TL::kFwdBM * 2), 0,
                      st, a);
@@ -1268,8 +1285,9 @@ static hipError_t launch_bwd_m(int stages, const AttnArgs& a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 2) {
-    const int64_t nqb = (a.max_seqlen_q + TL::kFwdBM - 1) / TL::kFwdBM;
-    const int64_t g1 = nqb * a.heads_q * a.batch;
+    const int hw = query_heads_per_wg(a.heads_q, a.heads_kv);
+    const int64_t nqb = (a.max_seqlen_q + 128 / hw - 1) / (128 / hw);
+    const int64_t g1 = nqb * (a.heads_q / hw) * a.batch;
     if (g1 > 0 && rows > 0) {
       hipLaunchKernelGGL((bwd_dq_kernel<T, D, TL::kFwdBM, TL::kFwdBN, M>), dim3((unsigned)g1), dim3(TL::kFwdBM * 2),
                          0, st, a);
