@@ -616,11 +616,6 @@ bwd_dq_kernel(AttnArgs a) {
     const char* vs = ks + KTile::kBytes;
     if (kb < kr.hi) fill_kv(kvld, stage ? st0 : st1, K, V, kstride, kb + 1, it.lk);
     const bool edge = !(kr.full_lo <= kb && kb <= kr.full_hi);
-    // all cells masked for this wave's 32 rows: dS = 0, nothing to add
-    if (edge && block_masked(it.lq, it.lk, a.window, a.causal != 0, it.row0, 32, kb * BN, BN)) {
-      __syncthreads();
-      return;
-    }
     uint32_t mw[BN / 32] = {};
     if constexpr (M) row_mask_words(a, mrow, row_ok, kb, mw);
 #pragma unroll
