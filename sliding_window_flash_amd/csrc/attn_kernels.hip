@@ -615,6 +615,10 @@ bwd_dq_kernel(AttnArgs a) {
     const char* ks = stage ? st1 : st0;
     const char* vs = ks + KTile::kBytes;
     if (kb < kr.hi) fill_kv(kvld, stage ? st0 : st1, K, V, kstride, kb + 1, it.lk);
+    // Edge tiles are masked cell by cell; a wave's all-masked 32 x 64 block is
+    // computed like any other (P = dS = 0): an early exit from the step made
+    // the compiler copy the accumulators at every step and spill, which cost
+    // more (6% of dQ) than the few all-masked blocks.
     const bool edge = !(kr.full_lo <= kb && kb <= kr.full_hi);
     uint32_t mw[BN / 32] = {};
     if constexpr (M) row_mask_words(a, mrow, row_ok, kb, mw);
