@@ -521,26 +521,48 @@ fwd_kernel(AttnArgs a) {
 // The second output lets the other backward kernels copy LSE into LDS raw:
 // P = 2^(S * scale * log2e - LSE * log2e); a row without visible keys
 // (LSE = -inf) gets +inf, so its P is 0.
+// A block takes one query head and kDeltaPasses x (256 / LPR) consecutive
+// tokens; in each pass LPR lanes share a (token, head) row, 8 elements per
+// lane, and the rows of a pass are consecutive tokens of the head, so their D
+// and LSE*log2e land in consecutive words of the [Hq, T] outputs. All of a
+// thread's loads are issued before the first reduction.
+constexpr int kDeltaPasses = 4;
+template <int D> constexpr int delta_tokens_per_block() { return kDeltaPasses * (256 / (D / 8)); }
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_delta_kernel(AttnArgs a) {
   constexpr int LPR = D / 8;  // lanes per (token, head) row, 8 elements each
-  const int64_t rows = (int64_t)a.total_q * a.heads_q;
-  const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
-  const int sub = threadIdx.x % LPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const Frag<T> o = global_frag<T>(static_cast<const T*>(a.o) + row * D + sub * 8);
-    const Frag<T> d = global_frag<T>(static_cast<const T*>(a.dout) + row * D + sub * 8);
+  constexpr int RPP = 256 / LPR;
+  constexpr int TPB = delta_tokens_per_block<D>();
+  const int h = (int)(blockIdx.x % (unsigned)a.heads_q);
+  const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)a.heads_q) * TPB;
+  const int sub = threadIdx.x % LPR, rs = threadIdx.x / LPR;
+  Frag<T> o[kDeltaPasses], d[kDeltaPasses];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc += to_f32(o.v[j]) * to_f32(d.v[j]);
+  for (int p = 0; p < kDeltaPasses; ++p) {
+    const int64_t t = t0 + p * RPP + rs;
+    if (t < a.total_q) {
+      const int64_t off = (t * a.heads_q + h) * D + sub * 8;
+      o[p] = global_frag<T>(static_cast<const T*>(a.o) + off);
+      d[p] = global_frag<T>(static_cast<const T*>(a.dout) + off);
+    } else {
+      o[p] = zero_frag<T>();
+      d[p] = zero_frag<T>();
+    }
   }
 #pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (sub == 0 && row < rows) {
-    const int64_t t = row / a.heads_q, h = row % a.heads_q;
-    a.delta[h * a.total_q + t] = acc;
-    const float l = a.lse[h * a.total_q + t];
-    a.lse2[h * a.total_q + t] = l == -INFINITY ? INFINITY : l * kLog2e;
+  for (int p = 0; p < kDeltaPasses; ++p) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += to_f32(o[p].v[j]) * to_f32(d[p].v[j]);
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    const int64_t t = t0 + p * RPP + rs;
+    if (sub == 0 && t < a.total_q) {
+      const int64_t idx = (int64_t)h * a.total_q + t;
+      a.delta[idx] = acc;
+      const float l = a.lse[idx];
+      a.lse2[idx] = l == -INFINITY ? INFINITY : l * kLog2e;
+    }
   }
 }
 
@@ -1279,7 +1301,8 @@ static hipError_t launch_bwd_m(int stages, const AttnArgs& a, hipStream_t st) {
   const int64_t rows = (int64_t)a.total_q * a.heads_q;
   hipError_t e = hipSuccess;
   if ((stages & 1) && rows > 0) {
-    const int64_t g0 = (rows + (256 / (D / 8)) - 1) / (256 / (D / 8));
+    const int64_t tpb = delta_tokens_per_block<D>();
+    const int64_t g0 = (a.total_q + tpb - 1) / tpb * a.heads_q;
     hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)g0), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
