@@ -65,3 +65,28 @@ def test_sweep_case(case):
     got = H.run_hip(w, H.to_device(w, x))
     zero = ("dq", "dk") if win == 1 else ()
     H.compare_full(w, x, got, zero=zero)
+
+
+# Query-major workgroups take 4, 2 or 1 heads of a KV group (the largest that
+# divides the group size) and 32, 64 or 128 rows; with groups larger than that
+# a group is split into several head chunks. These cases exercise every chunk
+# layout: groups 8 and 12 (4 heads x 32 rows, 2 and 3 chunks), 6 (2 heads x 64
+# rows, 3 chunks) and 5 (1 head x 128 rows, 5 chunks).
+GROUP_CASES = [
+    ((200, 57), None, 16, 2, 128, 64, True, "bf16"),
+    ((130, 261), (260, 300), 24, 2, 64, 100, True, "f32"),
+    ((97, 190), None, 12, 2, 128, 31, False, "bf16"),
+    ((300,), (333,), 6, 1, 64, INT32_MAX, True, "fp16"),
+    ((150, 33, 70), None, 10, 2, 128, 129, True, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", GROUP_CASES, ids=lambda c: f"{c[7]}-d{c[4]}-g{c[2] // c[3]}-w{c[5]}-{'c' if c[6] else 'nc'}")
+def test_group_chunks(case):
+    lq, lk, hq, hkv, d, win, causal, dt = case
+    w = small_case(lq, lk, heads_q=hq, heads_kv=hkv, head_dim=d, window=win, causal=causal, dtype=dt,
+                   do_scale=0.1, seed=zlib.crc32(repr(case).encode()) % 10000)
+    H.say(f"group-chunk case {case}")
+    x = make_inputs(w)
+    got = H.run_hip(w, H.to_device(w, x))
+    H.compare_full(w, x, got)
