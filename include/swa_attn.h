@@ -76,7 +76,8 @@ typedef enum {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
-  ATTN_ERR_SHAPE = 2,       /* sizes inconsistent (batch < 1, heads_q % heads_kv, heads_q > 16384, totals ...) */
+  ATTN_ERR_SHAPE = 2,       /* sizes inconsistent (batch < 1, heads_q % heads_kv, heads_q > 16384, totals,
+                               more than 2^31 - 1 work items: ceil(max_seqlen / 32) x heads x batch ...) */
   ATTN_ERR_WINDOW = 3,      /* window < 1 */
   ATTN_ERR_UNSUPPORTED = 4, /* head_dim not 64/128 (256: 16-bit dtypes only), unknown dtype, scale <= 0,
                                a two-sided window with max_seqlen_k > 2^30 */

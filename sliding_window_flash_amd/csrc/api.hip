@@ -39,6 +39,12 @@ swa::AttnArgs base_args(const attn_params_t* p) {
   return a;
 }
 
+// a * b * c <= INT32_MAX for non-negative factors, without overflowing
+bool fits_i32(int64_t a, int64_t b, int64_t c) {
+  if (a == 0 || b == 0 || c == 0) return true;
+  return a <= INT32_MAX / b && a * b <= INT32_MAX / c;
+}
+
 int64_t q_elems(const attn_params_t* p) { return (int64_t)p->total_q * p->heads_q * p->head_dim; }
 int64_t k_elems(const attn_params_t* p) { return (int64_t)p->total_k * p->heads_kv * p->head_dim; }
 
@@ -70,6 +76,12 @@ attn_status_t attn_check_params(const attn_params_t* p) {
   if (p->heads_q > 16384) return ATTN_ERR_SHAPE;
   // packed element counts must stay addressable
   if ((int64_t)p->total_q * p->heads_q > INT32_MAX || (int64_t)p->total_k * p->heads_kv > INT32_MAX)
+    return ATTN_ERR_SHAPE;
+  // the kernels take their work item from a 32-bit launch id: query-major
+  // grids have at most ceil(max_seqlen_q / 32) x heads_q x batch items, key-major
+  // ones at most ceil(max_seqlen_k / 64) x heads_kv x batch
+  if (!fits_i32(((int64_t)p->max_seqlen_q + 31) / 32, p->heads_q, p->batch) ||
+      !fits_i32(((int64_t)p->max_seqlen_k + 63) / 64, p->heads_kv, p->batch))
     return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }

@@ -64,6 +64,11 @@ def good(**kw):
     (dict(scale=0.0), 4),
     (dict(scale=-0.1), 4),
     (dict(scale=float("inf")), 4),
+    # work items beyond a 32-bit launch id: many sequences, one of them long
+    (dict(batch=2**20, heads_q=64, heads_kv=8, total_q=2**24, total_k=2**24, max_seqlen_q=2**14,
+          max_seqlen_k=2**14), 2),
+    (dict(batch=2**10, heads_q=64, heads_kv=8, total_q=2**24, total_k=2**24, max_seqlen_q=2**14,
+          max_seqlen_k=2**14), 0),
     (dict(scale=float("nan")), 4),
     (dict(heads_q=16384, heads_kv=16384), 0),
     (dict(heads_q=16386, heads_kv=2), 2),
