@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark: sliding-window attention forward + backward on one MI355X.
 
-A step is one pass of the whole path: attn_fwd (O, LSE) and the three backward
-stages (D, dQ, dK/dV) over the 32,768-token workload (batch 1, 32 query / 8 KV
-heads, head_dim 128, causal window 1,024, bf16), inputs resident in HBM.
+A step is one pass of the whole path: attn_fwd (O, LSE) and the backward's two
+launches (dQ, which also forms D = rowsum(dO * O); dK/dV) over the 32,768-token
+workload (batch 1, 32 query / 8 KV heads, head_dim 128, causal window 1,024,
+bf16), inputs resident in HBM.
 
 value = in-window FLOPs / time: 14 * head_dim FLOPs per visible (query, key)
 pair summed over query heads (forward Q K^T and P V; backward Q K^T, dO V^T,
@@ -225,7 +226,9 @@ def main() -> int:
     ws = torch.empty(swa.workspace_bytes(p), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    names = ["fwd", "bwd_delta", "bwd_dq", "bwd_dkdv"]
+    # the backward is two launches: dQ (which also forms D = rowsum(dO * O) and
+    # LSE * log2 e for dK/dV) and dK/dV
+    names = ["fwd", "bwd_dq", "bwd_dkdv"]
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
@@ -240,7 +243,7 @@ def main() -> int:
         swa.fwd(q, k, v, cu_q, cu_k, out=o, lse=lse, **kw)
         if evs is not None:
             evs[1].record(stream)
-        for n, stage in enumerate((swa.BWD_DELTA, swa.BWD_DQ, swa.BWD_DKDV)):
+        for n, stage in enumerate((swa.BWD_DQ, swa.BWD_DKDV)):
             swa.bwd(q, k, v, o, lse, do, cu_q, cu_k, dq=dq, dk=dk, dv=dv, workspace=ws,
                     stages=stage, **kw)
             if evs is not None:
@@ -250,7 +253,7 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -265,14 +268,12 @@ def main() -> int:
     flops_counted = 14 * d * pairs
     value = flops_counted / (ms_per_step * 1e-3) / 1e12
     # algorithmic work of each launch (per visible pair: fwd 2 contractions,
-    # dQ 3 (S, dP recomputed, dS K), dK/dV 4 (S, dP, P^T dO, dS^T Q); D reads O
-    # and dO and writes one fp32 per row)
-    esz = 2 if w.dtype == "bf16" else 4
+    # dQ 3 (S, dP recomputed, dS K; its D = rowsum(dO * O) per row adds no
+    # contraction), dK/dV 4 (S, dP, P^T dO, dS^T Q))
     algo = {
         "fwd": ("mfma", 4 * d * pairs),
         "bwd_dq": ("mfma", 6 * d * pairs),
         "bwd_dkdv": ("mfma", 8 * d * pairs),
-        "bwd_delta": ("hbm", 2 * w.total_q * w.heads_q * d * esz + 4 * w.total_q * w.heads_q),
     }
     kernels = {}
     for n in names:
@@ -482,7 +483,7 @@ def main() -> int:
                    "flops_counted": flops_counted},
         "pct_bf16_peak": round(100 * value / BF16_DENSE_PEAK_TFLOPS, 2),
         "fwd_ms": round(kern_ms["fwd"], 4),
-        "bwd_ms": round(kern_ms["bwd_delta"] + kern_ms["bwd_dq"] + kern_ms["bwd_dkdv"], 4),
+        "bwd_ms": round(kern_ms["bwd_dq"] + kern_ms["bwd_dkdv"], 4),
         "kernels": kernels,
         "roofline": roofline,
         "memory": mem,

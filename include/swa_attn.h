@@ -122,16 +122,18 @@ attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, con
                        void* dk, void* dv, void* workspace, size_t workspace_bytes,
                        void* stream);
 
-/* The backward's three stages, for callers that schedule them themselves:
+/* The backward's stages, for callers that schedule them themselves:
  *   ATTN_BWD_DELTA: D = rowsum(dO * O) and LSE * log2(e) into the workspace;
- *   ATTN_BWD_DQ:    dQ (reads Q, K, V, dO and the workspace);
+ *   ATTN_BWD_DQ:    dQ (reads Q, K, V, O, LSE and dO); it forms D and
+ *                   LSE * log2(e) for its rows itself and writes them into the
+ *                   workspace as DELTA does, so a call that selects both runs
+ *                   only DQ;
  *   ATTN_BWD_DKDV:  dK and dV (reads Q, K, V, dO and the workspace).
- * DQ and DKDV need a completed DELTA of the same call parameters and
- * workspace; they are independent of each other, so they may run on two
- * streams once DELTA is done. attn_bwd is attn_bwd_stages with all three, in
- * this order, on one stream. Same arguments and checks as attn_bwd; pointers a
- * selected stage does not read or write may be NULL (O and LSE are read only
- * by DELTA, dQ written only by DQ, dK and dV only by DKDV). */
+ * DKDV needs a completed DELTA or DQ of the same call parameters and
+ * workspace. attn_bwd is attn_bwd_stages with all of them: DQ, then DKDV, on
+ * one stream. Same arguments and checks as attn_bwd; pointers a selected
+ * stage does not read or write may be NULL (O and LSE are read only by DELTA
+ * and DQ, dQ written only by DQ, dK and dV only by DKDV). */
 typedef enum {
   ATTN_BWD_DELTA = 1,
   ATTN_BWD_DQ = 2,

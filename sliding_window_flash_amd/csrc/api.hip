@@ -172,8 +172,9 @@ static attn_status_t bwd_impl(const attn_params_t* p, const attn_mask_t* mask, i
     if ((s = check_tensor(k, nk, true)) != ATTN_OK) return s;
     if ((s = check_tensor(v, nk, true)) != ATTN_OK) return s;
   }
-  if (st_delta && (s = check_tensor(lse, nrow, false)) != ATTN_OK) return s;
-  if (st_delta && (s = check_tensor(o, nq, true)) != ATTN_OK) return s;
+  // O and LSE are read by the D preprocess and by dQ, which forms D itself
+  if ((st_delta || st_dq) && (s = check_tensor(lse, nrow, false)) != ATTN_OK) return s;
+  if ((st_delta || st_dq) && (s = check_tensor(o, nq, true)) != ATTN_OK) return s;
   if ((s = check_tensor(dout, nq, true)) != ATTN_OK) return s;
   if (st_dq && (s = check_tensor(dq, nq, true)) != ATTN_OK) return s;
   if (st_dkdv) {

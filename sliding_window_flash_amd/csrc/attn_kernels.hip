@@ -603,9 +603,26 @@ bwd_dq_kernel(AttnArgs a) {
       qf[s] = row_ok ? global_frag<T>(qrow + 16 * s) : zero_frag<T>();
       df[s] = row_ok ? global_frag<T>(drow + 16 * s) : zero_frag<T>();
     }
+    // D = rowsum(dO * O) for this row: this lane holds half of each 16-dim
+    // chunk of dO (df) and reads the same half of O; the two lane halves' sums
+    // are added across the wave
+    const T* orow = static_cast<const T*>(a.o) + roff;
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const Frag<T> of = row_ok ? global_frag<T>(orow + 16 * s) : zero_frag<T>();
+#pragma unroll
+      for (int j = 0; j < 8; ++j) part = fmaf(to_f32(of.v[j]), to_f32(df[s].v[j]), part);
+    }
+    dlt = sum_halves(part);
     if (row_ok) {
-      lse2 = a.lse2[(int64_t)it.h * a.total_q + it.q0 + i];
-      dlt = a.delta[(int64_t)it.h * a.total_q + it.q0 + i];
+      const int64_t idx = (int64_t)it.h * a.total_q + it.q0 + i;
+      const float l = a.lse[idx];
+      lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+      if (half == 0) {
+        a.delta[idx] = dlt;
+        a.lse2[idx] = lse2;
+      }
     }
   }
   RowReader<T, D> rrd;
@@ -1300,7 +1317,9 @@ static hipError_t launch_bwd_m(int stages, const AttnArgs& a, hipStream_t st) {
   using TL = Tiles<D>;
   const int64_t rows = (int64_t)a.total_q * a.heads_q;
   hipError_t e = hipSuccess;
-  if ((stages & 1) && rows > 0) {
+  // dQ forms D and LSE*log2e for its rows itself, so the D preprocess runs
+  // only when dQ is not part of the call
+  if ((stages & 1) && !(stages & 2) && rows > 0) {
     const int64_t tpb = delta_tokens_per_block<D>();
     const int64_t g0 = (a.total_q + tpb - 1) / tpb * a.heads_q;
     hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)g0), dim3(256), 0, st, a);

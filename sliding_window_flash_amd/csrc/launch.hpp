@@ -8,7 +8,8 @@
 namespace swa {
 
 hipError_t launch_fwd(int dtype, int head_dim, const AttnArgs& a, hipStream_t st);
-// stages: bit 1 = D preprocess, 2 = dQ, 4 = dK/dV (run in that order)
+// stages: bit 1 = D preprocess (skipped when bit 2 is set: dQ forms D itself),
+// 2 = dQ, 4 = dK/dV (run in that order)
 hipError_t launch_bwd(int dtype, int head_dim, int stages, const AttnArgs& a, hipStream_t st);
 bool tile_sizes(int dtype, int head_dim, int* fwd_bm, int* fwd_bn, int* bwd_bn, int* bwd_bm);
 

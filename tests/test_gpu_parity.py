@@ -131,11 +131,12 @@ def test_backward_is_deterministic():
         assert torch.equal(a[key], b[key]), key
 
 
+@pytest.mark.parametrize("order", ["delta-dkdv-dq", "dq-dkdv"])
 @pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64), ("fp16", 256)])
-def test_stages_run_separately(dt, d):
-    """attn_bwd_stages one stage at a time (the D preprocess as its own launch,
-    dQ reading D from the workspace) and with dK/dV before dQ, against the
-    oracle; attn_bwd fuses D into dQ instead."""
+def test_stages_run_separately(dt, d, order):
+    """attn_bwd_stages one stage at a time against the oracle, on a workspace
+    poisoned with NaN: the D preprocess as its own launch with dK/dV before dQ,
+    and dQ alone forming D for the dK/dV launch after it (what attn_bwd does)."""
     import torch
     w = small_case([300, 77], [340, 77], heads_q=4, heads_kv=2, head_dim=d, window=90, dtype=dt,
                    do_scale=1.0 if dt == "f32" else 0.1, seed=36)
@@ -148,7 +149,9 @@ def test_stages_run_separately(dt, d):
     dq, dk, dv = torch.full_like(q, float("nan")), torch.full_like(k, float("nan")), torch.full_like(v, float("nan"))
     ws = torch.full((swa.workspace_bytes(swa.params_for(q, k, dev["cu_q"], dev["cu_k"], **kw)),), 255,
                     dtype=torch.uint8, device=q.device)
-    for stage in (swa.BWD_DELTA, swa.BWD_DKDV, swa.BWD_DQ):
+    stages = {"delta-dkdv-dq": (swa.BWD_DELTA, swa.BWD_DKDV, swa.BWD_DQ),
+              "dq-dkdv": (swa.BWD_DQ, swa.BWD_DKDV)}[order]
+    for stage in stages:
         swa.bwd(q, k, v, o, lse, do, dev["cu_q"], dev["cu_k"], dq=dq, dk=dk, dv=dv, workspace=ws, stages=stage, **kw)
     torch.cuda.synchronize()
     H.compare_full(w, x, dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv))
