@@ -171,6 +171,9 @@ def main() -> int:
     ap.add_argument("--no-masked", action="store_true",
                     help="skip the document-mask leg (the workload's tokens packed from documents)")
     ap.add_argument("--masked-steps", type=int, default=10)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads' timing (2K windowed, 8K causal, ragged batch)")
+    ap.add_argument("--config-steps", type=int, default=10)
     ap.add_argument("--no-ce", action="store_true",
                     help="skip the linear cross-entropy leg (the second workload)")
     ap.add_argument("--ce-steps", type=int, default=5)
@@ -377,6 +380,55 @@ def main() -> int:
                  "peak_ratio_per_doubling": [round(gsweep["16384"] / gsweep["8192"], 3),
                                              round(gsweep["32768"] / gsweep["16384"], 3)]}
 
+    # The other bf16 workloads (parity configurations, not the headline): the
+    # 2K windowed case, the 8K full-causal case with forward and backward
+    # timed separately (the mlx-train-perf README times its flash op at this
+    # shape on an M1 Max: 0.186 s forward, 0.576 s backward; another machine
+    # and stack, quoted as context) and the ragged packed batch.
+    configs = None
+    if not args.no_configs:
+        configs = {}
+        for name in ("bf16_n2048_w1024_32q8kv_d128", "bf16_n8192_causal_32q8kv_d128",
+                     "bf16_varlen4_w1024_32q8kv_d128"):
+            cw = W.WORKLOADS[name]
+            (qq, kk, vv, dd, cq, ck), ckw = device_inputs(cw)
+            oo = torch.empty_like(qq)
+            ll = torch.empty((cw.heads_q, cw.total_q), dtype=torch.float32, device=dev)
+            dq4, dk4, dv4 = torch.empty_like(qq), torch.empty_like(kk), torch.empty_like(vv)
+            ws4 = torch.empty(swa.workspace_bytes(swa.params_for(qq, kk, cq, ck, **ckw)), dtype=torch.uint8,
+                              device=dev)
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.config_steps)]
+
+            def cstep(e=None):
+                if e is not None:
+                    e[0].record(stream)
+                swa.fwd(qq, kk, vv, cq, ck, out=oo, lse=ll, **ckw)
+                if e is not None:
+                    e[1].record(stream)
+                swa.bwd(qq, kk, vv, oo, ll, dd, cq, ck, dq=dq4, dk=dk4, dv=dv4, workspace=ws4, **ckw)
+                if e is not None:
+                    e[2].record(stream)
+
+            for _ in range(3):
+                cstep()
+            torch.cuda.synchronize()
+            for e in ev:
+                cstep(e)
+            torch.cuda.synchronize()
+            f_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+            b_ms = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+            cp = in_window_pairs(cw)
+            d_ = cw.head_dim
+            configs[name] = {
+                "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+                "fwd_tflops": round(4 * d_ * cp / (f_ms * 1e-3) / 1e12, 2),
+                "bwd_tflops": round(10 * d_ * cp / (b_ms * 1e-3) / 1e12, 2),
+                "tflops": round(14 * d_ * cp / ((f_ms + b_ms) * 1e-3) / 1e12, 2),
+                "in_window_pairs": cp, "steps": args.config_steps}
+            if name == "bf16_n8192_causal_32q8kv_d128":
+                configs[name]["pages_m1_max_s"] = {"fwd": 0.186, "bwd": 0.576}
+            del qq, kk, vv, dd, oo, ll, dq4, dk4, dv4, ws4
+
     # The workload with an arbitrary mask combined with the window: its tokens
     # packed from corpus-like documents (block-diagonal mask, bit-packed rows).
     # Counted FLOPs are 14d per cell that both the window and the mask show.
@@ -488,6 +540,7 @@ def main() -> int:
         "roofline": roofline,
         "memory": mem,
         "memory_probe_shape": gemma,
+        "other_configs": configs,
         "masked_documents": masked,
         "linear_cross_entropy": ce_leg,
         "cpu_baseline": cpu,
