@@ -243,14 +243,15 @@ __device__ __forceinline__ PairWindow pair_window(int lk, int window, bool causa
   return {true, window - 1, 2u * (uint32_t)window - 1u};
 }
 
-// Waves per SIMD of the query-major kernels: two up to head_dim 128 (256
-// registers each; one wave's softmax overlaps the other's MFMAs); one at
-// head_dim 256, whose accumulator and Q fragments need the 512-register budget
-// (the 128 KB of K/V stages leave room for one workgroup per CU anyway).
-constexpr int waves_per_simd(int d) { return d > 128 ? 1 : 2; }
+// Waves per SIMD of the query-major kernels: two for 16-bit types up to
+// head_dim 128 (256 registers each; one wave's softmax overlaps the other's
+// MFMAs); one at head_dim 256 and for fp32 at 128, whose accumulator and Q
+// fragments need the 512-register budget (their 128 KB of K/V stages leave
+// room for one workgroup per CU anyway).
+template <typename T> constexpr int waves_per_simd(int d) { return d > 128 || (sizeof(T) == 4 && d > 64) ? 1 : 2; }
 
 template <typename T, int D, int BM, int BN, bool M>
-__global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
+__global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(waves_per_simd<T>(D), waves_per_simd<T>(D))))
 fwd_kernel(AttnArgs a) {
   static_assert(BN == 64, "mask words cover 64-key tiles");
   constexpr int NT = BM * 2;
@@ -568,7 +569,7 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------- backward: dQ
 template <typename T, int D, int BM, int BN, bool M>
-__global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
+__global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(waves_per_simd<T>(D), waves_per_simd<T>(D))))
 bwd_dq_kernel(AttnArgs a) {
   static_assert(BN == 64, "mask words cover 64-key tiles");
   constexpr int NT = BM * 2;
