@@ -1,23 +1,26 @@
 // Forward and backward attention kernels for gfx950, and their launchers.
 //
-// Forward (per query tile of BM rows, one query head): S^T = K Q^T on MFMA,
-// mask edge cells, online softmax per query in the exp2 domain, O^T += V^T P^T
-// on MFMA; the epilogue writes O and the natural-log LSE. The mlx-train-perf
-// README's flash-attention passage describes this saved state (the output and
-// the log-sum-exp) and the tile recompute in the backward.
+// Forward (per block of query rows and heads of one KV group): S^T = K Q^T on
+// MFMA, mask edge cells, online softmax per query in the exp2 domain, O^T +=
+// V^T P^T on MFMA; the epilogue writes O and the natural-log LSE. The
+// mlx-train-perf README's flash-attention passage describes this saved state
+// (the output and the log-sum-exp) and the tile recompute in the backward.
 //
-// Backward, three launches on the caller's stream:
-//   delta: D = rowsum(dO * O) per (token, head), fp32 workspace.
-//   dq:    per query tile: recompute S^T, dP^T = V dO^T, P = exp(S - LSE),
-//          dS = P (dP - D), dQ^T += K^T dS^T. The accumulator is cleared
-//          before the first visited key tile, which under a window is not
-//          tile zero ("Off NVIDIA, you fix the platform yourself", section
-//          "What did fixing it take?").
-//   dkdv:  per key tile of BN keys and KV head: K and V stay in registers; for
-//          each query head of the group and each query tile that sees the key
-//          tile: S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS. A key
-//          tile no query sees writes exact zeros (same section: some key
-//          blocks are never visited).
+// Backward, two launches on the caller's stream:
+//   dq:    per block of query rows: D = rowsum(dO * O) and LSE * log2 e for
+//          its rows (written to the workspace for dkdv), then per key tile:
+//          recompute S^T, dP^T = V dO^T, P = exp(S - LSE), dS = P (dP - D),
+//          dQ^T += K^T dS^T. The accumulator is cleared before the first
+//          visited key tile, which under a window is not tile zero ("Off
+//          NVIDIA, you fix the platform yourself", section "What did fixing
+//          it take?").
+//   dkdv:  per key tile of BN keys and KV head: K and V stay in LDS (fp32: in
+//          registers); for each query head of the group and each query tile
+//          that sees the key tile: S = Q K^T, dP = dO V^T, dV^T += dO^T P,
+//          dK^T += Q^T dS. A key tile no query sees writes exact zeros (same
+//          section: some key blocks are never visited).
+// A separate D launch (delta) serves callers of the stage API who run dkdv
+// without dq.
 // Score tiles S, P, dP, dS stay fp32 in registers; P and dS are rounded to
 // bf16 only as MFMA operands (the lab record's "Attention gradient error, real
 // Gemma 4 activations" entry: bf16 scratch scores cost about fourfold in dQ
