@@ -90,7 +90,7 @@ typedef struct {
   int32_t batch;        /* B >= 1 packed sequences */
   int32_t heads_q;      /* query heads, a multiple of heads_kv */
   int32_t heads_kv;     /* key/value heads; G = heads_q / heads_kv queries share one */
-  int32_t head_dim;     /* 64 or 128 */
+  int32_t head_dim;     /* 64 or 128; 256 for bf16 and fp16 */
   int32_t total_q;      /* cu_seqlens_q[B] */
   int32_t total_k;      /* cu_seqlens_k[B] */
   int32_t max_seqlen_q; /* >= every L_q; sizes the launch grid (no device reads) */
