@@ -246,6 +246,45 @@ __device__ __forceinline__ PairWindow pair_window(int lk, int window, bool causa
   return {true, window - 1, 2u * (uint32_t)window - 1u};
 }
 
+// Edge-tile masks as bit runs. Within one tile the visible cells of a lane's
+// row (or, key-major, of a lane's key) form one interval of offsets, so the
+// mask is one run of ones, built once per tile; each cell then costs a
+// sign-extended bit field and a bit select instead of compares.
+__device__ __forceinline__ uint64_t bit_run(int lo, int hi) {  // bits [lo, hi), 0 <= lo, hi <= 64
+  if (hi <= lo) return 0ull;
+  return (hi >= 64 ? ~0ull : (1ull << hi) - 1ull) & ~((1ull << lo) - 1ull);
+}
+// Query-major: bit o set iff (unsigned)(mb - o) < mlim (row_window, with mb =
+// mpos - the key of offset 0) and, with nk >= 0, o < nk (keys past L_k).
+// Offsets past mb wrap to at least 2^32 - 64 > mlim, so they are never visible.
+__device__ __forceinline__ uint64_t row_keys_visible(uint32_t mb, uint32_t mlim, int nk) {
+  const int hi = (int)min(mb, 63u) + 1;
+  const int lo = mb >= mlim ? (int)min(mb - mlim + 1u, 64u) : 0;
+  return bit_run(lo, nk >= 0 ? min(hi, nk) : hi);
+}
+// Key-major: bit o set iff row ib + o is a real row (< L_q) and, when
+// windowed, (unsigned)(mb + o) < lim (pair_window, mb = ib + L_k - L_q - j +
+// off). L_q and L_k are at most 2^30, so mb and the bounds stay in int range.
+__device__ __forceinline__ uint32_t key_rows_visible(int ib, int mb, int lq, const PairWindow& pw) {
+  int hi = min(max(lq - ib, 0), 32), lo = 0;
+  if (pw.windowed) {
+    const int lim = (int)pw.lim;
+    lo = min(max(-mb, 0), 32);
+    hi = min(hi, mb >= lim ? 0 : (mb < lim - 32 ? 32 : lim - mb));
+  }
+  return (uint32_t)bit_run(lo, hi);
+}
+// s[r] (offset o = 8 (r / 4) + r % 4 in the lane's 32-cell block) becomes -inf
+// where bit o of vis is clear
+__device__ __forceinline__ void apply_visible(f32x16& s, uint32_t vis) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int o = 8 * (r >> 2) + (r & 3);
+    const int keep = (int)(vis << (31 - o)) >> 31;
+    s[r] = __int_as_float((__float_as_int(s[r]) & keep) | (~keep & (int)0xff800000u));
+  }
+}
+
 // Waves per SIMD of the query-major kernels: two for 16-bit types up to
 // head_dim 128 (256 registers each; one wave's softmax overlaps the other's
 // MFMAs); one at head_dim 256 and for fp32 at 128, whose accumulator and Q
@@ -345,20 +384,10 @@ fwd_kernel(AttnArgs a) {
         if constexpr (M) row_mask_words(a, mrow, row_ok, kb + 1, mnxt);
       }
       if (!(kr.full_lo <= kb && kb <= kr.full_hi)) {  // edge tile: mask cell by cell
-        const uint32_t mb = mpos - (uint32_t)(kb * BN + 4 * half);
+        const int jb = kb * BN + 4 * half;  // two-sided: the keys past L_k are masked as well
+        const uint64_t vis = row_keys_visible(mpos - (uint32_t)jb, mlim, rw.pad_keys ? max(it.lk - jb, 0) : -1);
 #pragma unroll
-        for (int kt = 0; kt < BN / 32; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (mb - (uint32_t)(32 * kt + 8 * (r >> 2) + (r & 3)) >= mlim) cur[kt][r] = -INFINITY;
-        if (rw.pad_keys && kb * BN + BN > it.lk) {  // two-sided: the keys past L_k
-          const int jb = kb * BN + 4 * half;
-#pragma unroll
-          for (int kt = 0; kt < BN / 32; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (jb + 32 * kt + 8 * (r >> 2) + (r & 3) >= it.lk) cur[kt][r] = -INFINITY;
-        }
+        for (int kt = 0; kt < BN / 32; ++kt) apply_visible(cur[kt], (uint32_t)(vis >> (32 * kt)));
       }
       if constexpr (M) apply_row_mask2(cur, mcur, half);
       float mx = -INFINITY;
@@ -446,21 +475,11 @@ fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int ss = 0; ss < D / 16; ++ss) mma(s[kt], rrd.read(ks, 32 * kt, ss), qf[ss]);
     }
-    if (edge) {
-      const uint32_t mb = mpos - (uint32_t)(kb * BN + 4 * half);
+    if (edge) {  // two-sided: the keys past L_k are masked as well
+      const int k0l = kb * BN + 4 * half;
+      const uint64_t vis = row_keys_visible(mpos - (uint32_t)k0l, mlim, rw.pad_keys ? max(it.lk - k0l, 0) : -1);
 #pragma unroll
-      for (int kt = 0; kt < BN / 32; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (mb - (uint32_t)(32 * kt + 8 * (r >> 2) + (r & 3)) >= mlim) s[kt][r] = -INFINITY;
-      if (rw.pad_keys && kb * BN + BN > it.lk) {  // two-sided: the keys past L_k
-        const int jb = kb * BN + 4 * half;
-#pragma unroll
-        for (int kt = 0; kt < BN / 32; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (jb + 32 * kt + 8 * (r >> 2) + (r & 3) >= it.lk) s[kt][r] = -INFINITY;
-      }
+      for (int kt = 0; kt < BN / 32; ++kt) apply_visible(s[kt], (uint32_t)(vis >> (32 * kt)));
     }
     if constexpr (M) apply_row_mask2(s, mw, half);
     float mx = -INFINITY;
@@ -675,16 +694,8 @@ bwd_dq_kernel(AttnArgs a) {
         mma(dp, rrd.read(vs, 32 * kt, ss), df[ss]);
       }
       if (edge) {
-        const uint32_t mb = mpos - (uint32_t)(kb * BN + 32 * kt + 4 * half);
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (mb - (uint32_t)(8 * (r >> 2) + (r & 3)) >= mlim) s[r] = -INFINITY;
-        if (rw.pad_keys && kb * BN + BN > it.lk) {  // two-sided: the keys past L_k
-          const int jb = kb * BN + 32 * kt + 4 * half;
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (jb + 8 * (r >> 2) + (r & 3) >= it.lk) s[r] = -INFINITY;
-        }
+        const int jb = kb * BN + 32 * kt + 4 * half;  // two-sided: the keys past L_k are masked as well
+        apply_visible(s, (uint32_t)row_keys_visible(mpos - (uint32_t)jb, mlim, rw.pad_keys ? max(it.lk - jb, 0) : -1));
       }
       if constexpr (M) {
         if (!__all(mw[kt] == 0xFFFFFFFFu)) apply_row_mask(s, mw[kt], half);
@@ -866,12 +877,7 @@ bwd_dkdv_kernel(AttnArgs a) {
       // row r holds query ib + 8(r/4) + r%4: visible iff it is a real row
       // (< L_q) and inside the window (pair_window) at p = query + L_k - L_q
       const int ib = qb * BM + 32 * mh + 4 * half;
-      const int mb = ib + (lk - lq) - j + pw.off;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = 8 * (r >> 2) + (r & 3);
-        if ((ib + off >= lq) | (pw.windowed & ((uint32_t)(mb + off) >= pw.lim))) s[r] = -INFINITY;
-      }
+      apply_visible(s, key_rows_visible(ib, ib + (lk - lq) - j + pw.off, lq, pw));
     }
     if constexpr (M) {  // this lane's key is bit l32 of word kt of each row
       const char* mt = qs + kMaskOff;
@@ -1068,12 +1074,7 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
     }
     if (edge) {
       const int ib = qb * BM + 4 * half;
-      const int mb = ib + (lk - lq) - j + pw.off;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = 8 * (r >> 2) + (r & 3);
-        if ((ib + off >= lq) | (pw.windowed & ((uint32_t)(mb + off) >= pw.lim))) s[r] = -INFINITY;
-      }
+      apply_visible(s, key_rows_visible(ib, ib + (lk - lq) - j + pw.off, lq, pw));
     }
     if constexpr (M) {  // this lane's key is bit l32 of word kt of each row
       const char* mt = qs + kMaskOff;
