@@ -948,34 +948,30 @@ bwd_dkdv_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------ backward: dK, dV at head_dim 256
-// One workgroup per (KV head, sequence, key tile of BN = 64 keys), 4 waves, one
-// per SIMD: wave w owns keys 32*(w%2) .. +31 and head dims 128*(w/2) .. +127
-// of dK and dV. Each wave forms S and dP for its 32 keys over all 256 dims in
-// every BM = 32-query step (the two dim halves of a key block compute them
-// alike), then adds its dims' share of P^T dO and dS^T Q. K and V stay in LDS;
-// query tiles stream through two stages. LDS: 2 x 32 KB for K, V and 2 x 33 KB
-// for the stages; the accumulators take 128 registers.
+// One workgroup per (KV head, sequence, key tile of BN = 128 keys), 4 waves, one
+// per SIMD: wave w owns keys 32*w .. +31 and all 256 head dims of their dK and
+// dV, with its keys' K and V rows in registers (64 + 64). The (head, query
+// tile) steps run twice: the first pass forms S and P and accumulates dV, the
+// second forms S, dP and dS and accumulates dK, so only one 128-register
+// accumulator is live at a time (dK and dV together, with S and dP, would not
+// fit the accumulator registers). LDS holds only the two stages of the
+// streamed query tiles (Q, dO, LSE*log2e, D), BM = 32 queries per step.
 template <typename T, int D, int BN, int BM, bool M>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_dkdv_wide_kernel(AttnArgs a) {
   constexpr int NT = 256;
-  static_assert(D == 256 && BN == 64 && BM == 32, "wave layout assumes 2 key blocks x 2 dim halves");
-  constexpr int DH = D / 2;                               // dims per wave
+  static_assert(D == 256 && BN == 128 && BM == 32, "wave layout assumes 4 key blocks of 32 keys, all dims per wave");
   using QTile = LdsTile<T, BM, D>;
-  using KTile = LdsTile<T, BN, D>;
-  constexpr int kStats = 64 * 4;                          // one 64-lane 4-byte load's worth
-  // with M, the step's mask tile follows: BM = 32 rows x 8 bytes (the 2 words
-  // of this key tile's 64 keys)
+  constexpr int kStats = 64 * 4;  // one 64-lane 4-byte load's worth
+  // with M, the step's mask tile follows: one 16-byte load per lane (rows past
+  // BM arrive as zeros), the 4 words of this key tile's 128 keys per row
   constexpr int kMaskOff = 2 * QTile::kBytes + 2 * kStats;
-  constexpr int kStage = kMaskOff + (M ? BM * 8 : 0);  // Q, dO, LSE*log2e, D[, mask]
+  constexpr int kStage = kMaskOff + (M ? 64 * 16 : 0);  // Q, dO, LSE*log2e, D[, mask]
   __shared__ __attribute__((aligned(1024))) char st0[kStage];
   __shared__ __attribute__((aligned(1024))) char st1[kStage];
-  __shared__ __attribute__((aligned(1024))) char klds[KTile::kBytes];
-  __shared__ __attribute__((aligned(1024))) char vlds[KTile::kBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int w = wave_uniform(tid >> 6);
-  const int kt = w & 1, dh = w >> 1;
   const int nkb = (a.max_seqlen_k + BN - 1) / BN;
   int L = xcd_remap((int)blockIdx.x, nkb * a.heads_kv * a.batch);
   const int kb = L % nkb;
@@ -992,36 +988,33 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
 
   const int64_t qstride = (int64_t)a.heads_q * D;
   const int64_t kstride = (int64_t)a.heads_kv * D;
-  const int j = kb * BN + 32 * kt + l32;  // this lane's key (rows past L_k arrive as zeros; not stored)
+  const int j = kb * BN + 32 * w + l32;  // this lane's key (rows past L_k are zeros; not stored)
   const bool key_ok = j < lk;
+  Frag<T> kf[D / 16], vf[D / 16];
   {
-    const int kvalid = min(BN, lk - kb * BN);
-    const int64_t koff = (int64_t)(k0 + kb * BN) * kstride + g * D;
-    const uint32_t sb = (uint32_t)(kstride * sizeof(T));
-    TileLoader<T, BN, D, NT> kvld;
-    kvld.init(sb, w, lane);
-    kvld.issue(klds, static_cast<const T*>(a.k) + koff, sb, kvalid);
-    kvld.issue(vlds, static_cast<const T*>(a.v) + koff, sb, kvalid);
+    const int64_t roff = (int64_t)(k0 + (key_ok ? j : 0)) * kstride + g * D + 8 * half;
+    const T* krow = static_cast<const T*>(a.k) + roff;
+    const T* vrow = static_cast<const T*>(a.v) + roff;
+#pragma unroll
+    for (int ss = 0; ss < D / 16; ++ss) {
+      kf[ss] = key_ok ? global_frag<T>(krow + 16 * ss) : zero_frag<T>();
+      vf[ss] = key_ok ? global_frag<T>(vrow + 16 * ss) : zero_frag<T>();
+    }
   }
   RowReader<T, D> rrd;
   rrd.init(l32, half);
   ColReader<T, D> crd;
   crd.init(lane);
-  f32x16 dka[DH / 32], dva[DH / 32];
-#pragma unroll
-  for (int dt = 0; dt < DH / 32; ++dt) {
-    dka[dt] = f32x16{};
-    dva[dt] = f32x16{};
-  }
   const float c = a.scale * kLog2e;
   const PairWindow pw = pair_window(lk, a.window, causal);
   const T* __restrict__ Qg = static_cast<const T*>(a.q);
   const T* __restrict__ Dg = static_cast<const T*>(a.dout);
 
-  // (head, query tile) steps as in the 128-key kernel; an empty range writes zeros
+  // (head, query tile) steps as in the 128-key kernel, walked once per pass;
+  // an empty range writes zeros
   const int nq = qr.hi >= qr.lo ? qr.hi - qr.lo + 1 : 0;
   const int steps = grp * nq;
-  int nh = g * grp, nqb = qr.lo;
+  int nh = g * grp, nqb = qr.lo;  // (head, query tile) of the next step to fill
   const uint32_t qsb = (uint32_t)(qstride * sizeof(T));
   TileLoader<T, BM, D, NT> qld;
   qld.init(qsb, w, lane);
@@ -1037,89 +1030,130 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
                      (uint32_t)lane * 4u);
     }
     if constexpr (M) {
-      if (w == 1) {  // lane l: word 2 kb + l % 2 of row l / 2; rows past L_q arrive as zeros
+      if (w == 1) {  // lane r: row r's words 4 kb .. 4 kb + 3; rows past L_q arrive as zeros
         const uint32_t rb = (uint32_t)a.mask_words * 4u;
-        buffer_to_lds4(buffer_rsrc(a.mask + (int64_t)(q0 + nqb * BM) * a.mask_words + 2 * kb, (uint32_t)qvalid * rb),
-                       st + kMaskOff, (uint32_t)(lane >> 1) * rb + (uint32_t)(lane & 1) * 4u);
+        buffer_to_lds16(buffer_rsrc(a.mask + (int64_t)(q0 + nqb * BM) * a.mask_words + 4 * kb, (uint32_t)qvalid * rb),
+                        st + kMaskOff, (uint32_t)lane * rb);
       }
     }
     if (++nqb > qr.hi) {
       nqb = qr.lo;
-      ++nh;
+      if (++nh == g * grp + grp) nh = g * grp;  // the second pass starts over
     }
   };
-  // odd step counts start in stage 1: the loop below runs whole stage pairs
-  if (steps > 0) fill(steps & 1 ? st1 : st0);
+  const int total = 2 * steps;
+  // odd step counts start in stage 1: the loops below run whole stage pairs
+  if (total > 0) fill(steps & 1 ? st1 : st0);
   __syncthreads();
 
-  int qb = qr.lo;
-  auto step = [&](auto stage_c, int t) {
-    constexpr int stage = decltype(stage_c)::value;
-    const char* qs = stage ? st1 : st0;
-    const char* dos = qs + QTile::kBytes;
-    const float* lse2s = reinterpret_cast<const float*>(qs + 2 * QTile::kBytes);
-    const float* dlts = reinterpret_cast<const float*>(qs + 2 * QTile::kBytes + kStats);
-    if (t + 1 < steps) fill(stage ? st0 : st1);
+  int qb = qr.lo;  // query tile of the current step
+  // S for this wave's 32 keys against the stage's 32 query rows, masked and
+  // turned into P (fp32); returns false when the whole block is masked
+  auto probs = [&](const char* qs, f32x16& s) -> bool {
     const bool edge = !tile_full_i32(lq, lk, a.window, causal, qb, BM, kb, BN);
-    if (edge && block_masked(lq, lk, a.window, causal, qb * BM, BM, kb * BN + 32 * kt, 32)) {
-      if (++qb > qr.hi) qb = qr.lo;
-      __syncthreads();
-      return;
-    }
-    f32x16 s = f32x16{}, dp = f32x16{};
+    if (edge && block_masked(lq, lk, a.window, causal, qb * BM, BM, kb * BN + 32 * w, 32)) return false;
+    s = f32x16{};
 #pragma unroll
-    for (int ss = 0; ss < D / 16; ++ss) {
-      mma(s, rrd.read(qs, 0, ss), rrd.read(klds, 32 * kt, ss));
-      mma(dp, rrd.read(dos, 0, ss), rrd.read(vlds, 32 * kt, ss));
-    }
+    for (int ss = 0; ss < D / 16; ++ss) mma(s, rrd.read(qs, 0, ss), kf[ss]);
     if (edge) {
       const int ib = qb * BM + 4 * half;
       apply_visible(s, key_rows_visible(ib, ib + (lk - lq) - j + pw.off, lq, pw));
     }
-    if constexpr (M) {  // this lane's key is bit l32 of word kt of each row
+    if constexpr (M) {  // this lane's key is bit l32 of word w of each row
       const char* mt = qs + kMaskOff;
       uint32_t words[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        words[r] = *reinterpret_cast<const uint32_t*>(mt + 8 * (4 * half + 8 * (r >> 2) + (r & 3)) + 4 * kt);
+        words[r] = *reinterpret_cast<const uint32_t*>(mt + 16 * (4 * half + 8 * (r >> 2) + (r & 3)) + 4 * w);
       apply_col_mask(s, words, l32);
     }
+    const float* lse2s = reinterpret_cast<const float*>(qs + 2 * QTile::kBytes);
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const int rr = 8 * r4 + 4 * half;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + rr);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlts + rr);
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + 8 * r4 + 4 * half);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * r4 + e;
-        const float pv = fast_exp2(fmaf(s[r], c, -l4[e]));
-        s[r] = pv;
-        dp[r] = pv * (dp[r] - d4[e]);  // dS
-      }
+      for (int e = 0; e < 4; ++e) s[4 * r4 + e] = fast_exp2(fmaf(s[4 * r4 + e], c, -l4[e]));
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const Frag<T> pf = acc_frag<T>(s, u);
-      const Frag<T> dsf = acc_frag<T>(dp, u);
-#pragma unroll
-      for (int dt = 0; dt < DH / 32; ++dt) {
-        mma(dva[dt], crd.read(dos, 16 * u, (DH / 32) * dh + dt), pf);
-        mma(dka[dt], crd.read(qs, 16 * u, (DH / 32) * dh + dt), dsf);
-      }
-    }
+    return true;
+  };
+  auto next = [&](int t) {
     if (++qb > qr.hi) qb = qr.lo;
+    (void)t;
     __syncthreads();
   };
-  int t = 0;
-  if (steps & 1) step(ic<1>{}, t++);
-  for (; t < steps; t += 2) {
-    step(ic<0>{}, t);
-    step(ic<1>{}, t + 1);
+
+  // pass 1: dV += P^T dO
+  {
+    f32x16 dva[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) dva[dt] = f32x16{};
+    auto step = [&](auto stage_c, int t) {
+      constexpr int stage = decltype(stage_c)::value;
+      const char* qs = stage ? st1 : st0;
+      const char* dos = qs + QTile::kBytes;
+      if (t + 1 < total) fill(stage ? st0 : st1);
+      f32x16 s;
+      if (probs(qs, s)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const Frag<T> pf = acc_frag<T>(s, u);
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) mma(dva[dt], crd.read(dos, 16 * u, dt), pf);
+        }
+      }
+      next(t);
+    };
+    int t = 0;
+    if (steps & 1) step(ic<1>{}, t++);
+    for (; t < steps; t += 2) {
+      step(ic<0>{}, t);
+      step(ic<1>{}, t + 1);
+    }
+    if (key_ok)
+      store_acc_rows<T, D>(static_cast<T*>(a.dv) + (int64_t)(k0 + j) * kstride + g * D, dva, 1.f, half);
   }
-  if (key_ok) {
-    const int64_t roff = (int64_t)(k0 + j) * kstride + g * D + DH * dh;
-    store_acc_rows<T, DH>(static_cast<T*>(a.dk) + roff, dka, a.scale, half);
-    store_acc_rows<T, DH>(static_cast<T*>(a.dv) + roff, dva, 1.f, half);
+  // pass 2: dK += dS^T Q, dS = P (dP - D); the stages continue where pass 1 left
+  // them (steps & 1 ? stage 0 : stage 1 holds step `steps`)
+  {
+    f32x16 dka[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) dka[dt] = f32x16{};
+    auto step = [&](auto stage_c, int t) {
+      constexpr int stage = decltype(stage_c)::value;
+      const char* qs = stage ? st1 : st0;
+      const char* dos = qs + QTile::kBytes;
+      const float* dlts = reinterpret_cast<const float*>(qs + 2 * QTile::kBytes + kStats);
+      if (t + 1 < total) fill(stage ? st0 : st1);
+      f32x16 s;
+      if (probs(qs, s)) {
+        f32x16 dp = f32x16{};
+#pragma unroll
+        for (int ss = 0; ss < D / 16; ++ss) mma(dp, rrd.read(dos, 0, ss), vf[ss]);
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlts + 8 * r4 + 4 * half);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = s[4 * r4 + e] * (dp[4 * r4 + e] - d4[e]);  // dS
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const Frag<T> dsf = acc_frag<T>(dp, u);
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) mma(dka[dt], crd.read(qs, 16 * u, dt), dsf);
+        }
+      }
+      next(t);
+    };
+    // pass 1 always ends on stage 1 (an odd count starts on stage 1), so step
+    // `steps` sits in stage 0; an odd count ends this pass with a lone stage 0
+    int t = steps;
+    for (; t + 1 < total; t += 2) {
+      step(ic<0>{}, t);
+      step(ic<1>{}, t + 1);
+    }
+    if (t < total) step(ic<0>{}, t);
+    if (key_ok)
+      store_acc_rows<T, D>(static_cast<T*>(a.dk) + (int64_t)(k0 + j) * kstride + g * D, dka, a.scale, half);
   }
 }
 
@@ -1293,11 +1327,11 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
 // 2 or 1 heads of a KV group x 32, 64 or 128 rows; query_heads_per_wg) and
 // step over keys 64 at a time. dK/dV takes 128 keys (8 waves: 4 key
 // blocks of 32 x 2 query halves; fp32: 4 waves) and steps over queries 64 at a
-// time; at head_dim 256 it takes 64 keys (4 waves: 2 key blocks x 2 dim
-// halves) and steps over queries 32 at a time.
+// time; at head_dim 256 it takes 128 keys (4 waves of 32 keys, two passes) and
+// steps over queries 32 at a time.
 template <int D> struct Tiles {
   static constexpr int kFwdBM = 128, kFwdBN = 64;
-  static constexpr int kBwdBN = D > 128 ? 64 : 128, kBwdBM = D > 128 ? 32 : 64;
+  static constexpr int kBwdBN = 128, kBwdBM = D > 128 ? 32 : 64;
 };
 
 // M: a mask combined with the window (a.mask != nullptr)

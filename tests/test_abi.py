@@ -122,7 +122,7 @@ def test_tile_sizes():
     bm, bn, kbn, kbm = swa.tile_sizes(128, swa.ATTN_BF16)
     assert bm % 32 == 0 and bn % 32 == 0 and kbn % 32 == 0 and kbm % 32 == 0
     assert swa.tile_sizes(128, swa.ATTN_F16) == (bm, bn, kbn, kbm)
-    assert swa.tile_sizes(256, swa.ATTN_BF16)[2:] == (64, 32)
+    assert swa.tile_sizes(256, swa.ATTN_BF16)[2:] == (128, 32)
     with pytest.raises(swa.AttnError):
         swa.tile_sizes(256, swa.ATTN_F32)
     with pytest.raises(swa.AttnError):
