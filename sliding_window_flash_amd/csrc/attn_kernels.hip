@@ -14,8 +14,9 @@
 //          visited key tile, which under a window is not tile zero ("Off
 //          NVIDIA, you fix the platform yourself", section "What did fixing
 //          it take?").
-//   dkdv:  per key tile of BN keys and KV head: K and V stay in LDS (fp32: in
-//          registers); for each query head of the group and each query tile
+//   dkdv:  per key tile of BN keys and KV head: K and V stay in LDS (fp32 and
+//          head_dim 256: in registers; head_dim 256 walks the query tiles
+//          twice, dV first, then dK); for each query head of the group and each query tile
 //          that sees the key tile: S = Q K^T, dP = dO V^T, dV^T += dO^T P,
 //          dK^T += Q^T dS. A key tile no query sees writes exact zeros (same
 //          section: some key blocks are never visited).
@@ -1076,9 +1077,8 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
     }
     return true;
   };
-  auto next = [&](int t) {
+  auto next = [&]() {  // end of a step: advance the query tile, meet the stage barrier
     if (++qb > qr.hi) qb = qr.lo;
-    (void)t;
     __syncthreads();
   };
 
@@ -1101,7 +1101,7 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
           for (int dt = 0; dt < D / 32; ++dt) mma(dva[dt], crd.read(dos, 16 * u, dt), pf);
         }
       }
-      next(t);
+      next();
     };
     int t = 0;
     if (steps & 1) step(ic<1>{}, t++);
@@ -1112,8 +1112,8 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
     if (key_ok)
       store_acc_rows<T, D>(static_cast<T*>(a.dv) + (int64_t)(k0 + j) * kstride + g * D, dva, 1.f, half);
   }
-  // pass 2: dK += dS^T Q, dS = P (dP - D); the stages continue where pass 1 left
-  // them (steps & 1 ? stage 0 : stage 1 holds step `steps`)
+  // pass 2: dK += dS^T Q, dS = P (dP - D); its first step was filled into
+  // stage 0 during pass 1's last step
   {
     f32x16 dka[D / 32];
 #pragma unroll
@@ -1142,7 +1142,7 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
           for (int dt = 0; dt < D / 32; ++dt) mma(dka[dt], crd.read(qs, 16 * u, dt), dsf);
         }
       }
-      next(t);
+      next();
     };
     // pass 1 always ends on stage 1 (an odd count starts on stage 1), so step
     // `steps` sits in stage 0; an odd count ends this pass with a lone stage 0
