@@ -28,6 +28,7 @@ CASES = [
     ([129], None, 2, 1, 64, 40, False, "f32", 0.97, 1),
     ([257], None, 4, 4, 64, 300, True, "fp16", 0.15, 4),
     ([97, 200], [120, 230], 2, 1, 256, INT32_MAX, False, "fp16", 0.5, 1),
+    ([150, 45], [160, 90], 3, 1, 256, 70, True, "bf16", 0.6, 2),  # odd group at 256
     # groups split into head chunks (forward / dQ workgroups take 4 or 2 heads)
     ([170, 90], None, 16, 2, 128, 80, True, "bf16", 0.6, 2),
     ([140], [200], 6, 1, 64, 60, False, "f32", 0.7, 1),

@@ -64,6 +64,10 @@ SMALL = [
     ([300, 1, 517, 64], None, 8, 2, 128, 65, False, "bf16"),  # two-sided windows
     ([100, 40], [700, 300], 4, 1, 64, 16, False, "f32"),
     ([257, 130], None, 4, 2, 256, 100, False, "fp16"),
+    # head_dim 256 with odd KV groups: odd (head, query tile) step counts in the
+    # two-pass dK/dV kernel (its stage order depends on the count's parity)
+    ([300, 77], None, 3, 1, 256, 100, True, "bf16"),
+    ([190, 64], None, 5, 5, 256, 33, False, "fp16"),
     ([200, 333], None, 4, 2, 128, 200, False, "f32"),
 ]
 
