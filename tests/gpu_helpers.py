@@ -18,6 +18,10 @@ BF16_MAX_ABS = 2e-2
 BF16_REL_FRO = 1e-2
 FP16_MAX_ABS = BF16_MAX_ABS / 4
 FP16_REL_FRO = BF16_REL_FRO / 4
+# The fp32 bar is stated for outputs of order one (the fp32 configuration).
+# fp32 rounding is relative, so the random sweeps, whose grouped heads and
+# longer rows give outputs up to ~10, apply it relative to the output's largest
+# magnitude: max-abs <= 1e-5 * max(1, max |ref|) (scale_f32=True).
 # Where the exact result is identically zero (window 1: dQ, dK; scale 0), only
 # rounding is left; the bar is max-abs 1e-4 in bf16 and 1e-6 in fp32.
 ZERO_REF_ABS = {"bf16": 1e-4, "fp16": 1e-4, "f32": 1e-6}
@@ -78,7 +82,7 @@ def host64(t) -> np.ndarray:
     return t.detach().to(torch.float64).cpu().numpy()
 
 
-def compare(name: str, got, ref, dtype: str, zero_ref: bool = False) -> dict:
+def compare(name: str, got, ref, dtype: str, zero_ref: bool = False, scale_f32: bool = False) -> dict:
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
@@ -92,7 +96,8 @@ def compare(name: str, got, ref, dtype: str, zero_ref: bool = False) -> dict:
     if zero_ref:
         assert max_abs <= ZERO_REF_ABS[dtype], f"{name}: {stats} (zero reference)"
     elif dtype == "f32":
-        assert max_abs <= F32_MAX_ABS, f"{name}: {stats}"
+        bar = F32_MAX_ABS * (max(1.0, float(np.abs(ref[fin]).max(initial=0.0))) if scale_f32 else 1.0)
+        assert max_abs <= bar, f"{name}: {stats} (bar {bar:.2e})"
     elif dtype == "fp16":
         assert max_abs <= FP16_MAX_ABS and rel <= FP16_REL_FRO, f"{name}: {stats}"
     else:
@@ -107,14 +112,15 @@ def full_reference(w: Workload, x: dict, window=None, mask=None) -> dict:
                                 window, w.causal, **kw)
 
 
-def compare_full(w: Workload, x: dict, got: dict, window=None, zero=(), mask=None) -> dict:
-    """``mask``: the boolean mask rows (oracle side) when the run used one."""
+def compare_full(w: Workload, x: dict, got: dict, window=None, zero=(), mask=None, scale_f32=False) -> dict:
+    """``mask``: the boolean mask rows (oracle side) when the run used one;
+    ``scale_f32``: the fp32 bar relative to the output's largest magnitude."""
     ref = full_reference(w, x, window, mask)
     out = {}
     for key in ("o", "lse", "dq", "dk", "dv"):
         if key in got:
             out[key] = compare(f"{w.name} {key}", host64(got[key]), ref[key], w.dtype,
-                               zero_ref=key in zero)
+                               zero_ref=key in zero, scale_f32=scale_f32)
     return out
 
 

@@ -9,6 +9,8 @@ windows, queries shorter than keys, several tiles with ragged tails, masks
 from nearly empty to nearly full, rows that allow no key at all, document
 (block-diagonal) masks, and the 32K-token document workload on sampled rows.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -41,17 +43,16 @@ def _device_mask(m, max_lk):
     return torch.from_numpy(bits.view(np.int32)).cuda()
 
 
-@pytest.mark.parametrize("n", range(len(CASES)))
-def test_masked_small_full_oracle(n):
-    lq, lk, hq, hkv, d, win, causal, dt, dens, empty = CASES[n]
+def _run_masked(case, seed, scale_f32=False):
+    lq, lk, hq, hkv, d, win, causal, dt, dens, empty = case
     w = small_case(lq, lk, heads_q=hq, heads_kv=hkv, head_dim=d, window=win, causal=causal,
-                   dtype=dt, do_scale=1.0 if dt == "f32" else 0.1, seed=700 + n)
-    H.say(f"masked case {n}: {w}")
+                   dtype=dt, do_scale=1.0 if dt == "f32" else 0.1, seed=seed)
+    H.say(f"masked case {case}: {w}")
     x = make_inputs(w)
-    m = W.random_mask(w, dens, seed=750 + n, empty_rows=empty)
+    m = W.random_mask(w, dens, seed=seed + 50, empty_rows=empty)
     dev = H.to_device(w, x)
     got = H.run_hip(w, dev, mask=_device_mask(m, max(w.lengths_k)))
-    stats = H.compare_full(w, x, got, mask=m)
+    stats = H.compare_full(w, x, got, mask=m, scale_f32=scale_f32)
     H.say("   ", {k: {a: f"{b:.2e}" for a, b in v.items()} for k, v in stats.items()})
     # a row that allows no key: O = 0, LSE = -inf, dQ = 0
     dead = np.nonzero(~m.any(axis=1))[0]
@@ -59,6 +60,39 @@ def test_masked_small_full_oracle(n):
         assert np.all(H.host64(got["o"])[dead] == 0)
         assert np.all(H.host64(got["lse"])[:, dead] == -np.inf)
         assert np.all(H.host64(got["dq"])[dead] == 0)
+
+
+@pytest.mark.parametrize("n", range(len(CASES)))
+def test_masked_small_full_oracle(n):
+    _run_masked(CASES[n], 700 + n)
+
+
+def _mask_grid(n, seed):
+    """Seeded random draw over the same axes as CASES (every dtype and head_dim,
+    KV groups 1 to 8, causal and two-sided windows, L_q < L_k, densities and
+    rows that allow no key)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    windows = (1, 7, 33, 64, 100, 129, 300, INT32_MAX)
+    while len(out) < n:
+        dt = ("f32", "bf16", "fp16")[rng.integers(3)]
+        d = int(rng.choice([64, 128, 256] if dt != "f32" else [64, 128]))
+        hkv = int(rng.choice([1, 2]))
+        g = int(rng.choice([1, 2, 3, 4, 8]))
+        lq = [int(x) for x in rng.integers(1, 300, int(rng.integers(1, 3)))]
+        lk = [q + int(rng.integers(1, 150)) for q in lq] if rng.random() < 0.35 else None
+        out.append((lq, lk, hkv * g, hkv, d, int(windows[rng.integers(len(windows))]), bool(rng.random() < 0.6), dt,
+                    float(rng.uniform(0.1, 0.98)), int(rng.integers(0, 4))))
+    return out
+
+
+# SWA_MASK_SWEEP_CASES widens the draw for a longer run; the default is 16 cases
+MASK_SWEEP = _mask_grid(int(os.environ.get("SWA_MASK_SWEEP_CASES", "16")), int(os.environ.get("SWA_MASK_SWEEP_SEED", "31")))
+
+
+@pytest.mark.parametrize("n", range(len(MASK_SWEEP)))
+def test_masked_sweep(n):
+    _run_masked(MASK_SWEEP[n], 900 + n, scale_f32=True)
 
 
 @pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64), ("fp16", 256)])
