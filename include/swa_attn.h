@@ -167,14 +167,14 @@ attn_status_t attn_bwd_stages(const attn_params_t* p, int32_t stages, const void
  * Ownership: device memory owned by the caller, only read. */
 typedef struct {
   const uint32_t* bits; /* device, [total_q, row_words], 16-byte aligned */
-  int64_t row_words;    /* a multiple of 4, >= ceil(max_seqlen_k / 32), <= 2^24 */
+  int64_t row_words;    /* a multiple of 4, >= ceil(max_seqlen_k / 32), < 2^24 */
 } attn_mask_t;
 
 /* attn_fwd with a mask. Same outputs and errors as attn_fwd; also
  * ATTN_ERR_NULL if `mask` or (total_q > 0) `mask->bits` is NULL, ATTN_ERR_ALIGN
  * if `bits` is not 16-byte aligned, ATTN_ERR_SHAPE if `row_words` is not a
  * multiple of 4 or is below ceil(max_seqlen_k / 32), ATTN_ERR_UNSUPPORTED if it
- * is above 2^24. */
+ * is 2^24 or more (a 64-row tile of the mask must span fewer than 2^32 bytes). */
 attn_status_t attn_fwd_masked(const attn_params_t* p, const attn_mask_t* mask, const void* q,
                               const void* k, const void* v, const int32_t* cu_seqlens_q,
                               const int32_t* cu_seqlens_k, void* o, float* lse, void* stream);

@@ -197,18 +197,67 @@ def params_for(q, k, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=INT32_MAX
 
 
 def _require(t, name):
-    torch = _torch()
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous device tensor")
     return t
 
 
+def _expect(t, name, shape, dtype):
+    """``t`` must have exactly this shape and dtype (checked before any pointer
+    is taken: the C ABI takes every size from q and k alone, so a mismatched
+    tensor would be read or written out of its bounds)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _check_attn(q, k, v, cu_q, cu_k, *, o=None, lse=None, do=None, dq=None, dk=None, dv=None,
+                mask=None, workspace=None, need_ws=0, devices=True):
+    """Shapes and dtypes of every tensor against q ([T_q, Hq, d]) and k
+    ([T_k, Hkv, d]), then (``devices``) device residency and contiguity.
+    Raises ValueError."""
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [total_q, heads_q, head_dim] and k [total_k, heads_kv, head_dim]")
+    tq, hq, d = q.shape
+    tk, hkv, dk_ = k.shape
+    if dk_ != d:
+        raise ValueError(f"k head_dim {dk_} differs from q head_dim {d}")
+    if k.dtype != q.dtype:
+        raise ValueError(f"k has dtype {k.dtype}, expected {q.dtype}")
+    _expect(v, "v", k.shape, q.dtype)
+    if cu_q.dim() != 1 or cu_k.dim() != 1 or cu_q.numel() < 2 or cu_q.numel() != cu_k.numel():
+        raise ValueError("cu_q and cu_k must be 1-D with batch + 1 (>= 2) elements each")
+    for t, n in ((cu_q, "cu_q"), (cu_k, "cu_k")):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{n} has dtype {t.dtype}, expected torch.int32")
+    named = [(o, "o", q.shape, q.dtype), (do, "do", q.shape, q.dtype), (dq, "dq", q.shape, q.dtype),
+             (dk, "dk", k.shape, q.dtype), (dv, "dv", k.shape, q.dtype),
+             (lse, "lse", (hq, tq), torch.float32)]
+    for t, n, shp, dt in named:
+        if t is not None:
+            _expect(t, n, shp, dt)
+    if mask is not None:
+        if mask.dim() != 2 or mask.element_size() != 4 or mask.shape[0] != tq:
+            raise ValueError(f"mask must be [total_q = {tq}, row_words] of 32-bit words, "
+                             f"got {tuple(mask.shape)} of {mask.dtype}")
+    if workspace is not None and workspace.numel() * workspace.element_size() < need_ws:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                         f"needs {need_ws}")
+    if not devices:
+        return
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (cu_q, "cu_q"), (cu_k, "cu_k"), (o, "o"), (lse, "lse"),
+                 (do, "do"), (dq, "dq"), (dk, "dk"), (dv, "dv"), (mask, "mask"), (workspace, "workspace")):
+        if t is not None:
+            _require(t, n)
+            if t.device != q.device:
+                raise ValueError(f"{n} is on {t.device}, q on {q.device}")
+
+
 def _mask_arg(mask):
     """attn_mask_t for a device tensor of packed rows ([T_q, row_words], 32-bit
     words; bit j % 32 of word j // 32 allows key j of the row's sequence)."""
-    _require(mask, "mask")
-    if mask.dim() != 2 or mask.element_size() != 4:
-        raise ValueError("mask must be [total_q, row_words] of 32-bit words")
     return AttnMask(mask.data_ptr(), mask.shape[1])
 
 
@@ -217,8 +266,7 @@ def fwd(q, k, v, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=INT32_MAX, ca
     """O [T_q, Hq, d] (q.dtype) and LSE [Hq, T_q] (fp32) through attn_fwd, or
     attn_fwd_masked when ``mask`` (packed rows, see :func:`_mask_arg`) is given."""
     torch = _torch()
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (cu_q, "cu_q"), (cu_k, "cu_k")):
-        _require(t, n)
+    _check_attn(q, k, v, cu_q, cu_k, o=out, lse=lse, mask=mask)
     p = params_for(q, k, cu_q, cu_k, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
                    window=window, causal=causal, scale=scale)
     if out is None:
@@ -243,15 +291,15 @@ def bwd(q, k, v, o, lse, do, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=I
     selects a subset of the backward's launches (all three by default). With
     ``mask`` (the forward's), through attn_bwd_masked (all stages)."""
     torch = _torch()
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (do, "do"),
-                 (cu_q, "cu_q"), (cu_k, "cu_k")):
-        _require(t, n)
+    _check_attn(q, k, v, cu_q, cu_k, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv, mask=mask, devices=False)
     p = params_for(q, k, cu_q, cu_k, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
                    window=window, causal=causal, scale=scale)
+    nbytes = workspace_bytes(p)
+    _check_attn(q, k, v, cu_q, cu_k, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv, mask=mask,
+                workspace=workspace, need_ws=nbytes)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    nbytes = workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(cu_q), _ptr(cu_k), _ptr(dq),
@@ -282,22 +330,49 @@ def ce_params_for(h, w) -> CEParams:
     return CEParams(h.shape[0], w.shape[0], h.shape[1], dt)
 
 
+def _check_ce(h, w, targets, *, f32=(), dh=None, workspace=None, need_ws=0, devices=True):
+    """Shapes and dtypes against h ([n, hidden]) and w ([vocab, hidden]), then
+    device residency and contiguity. ``f32``: (tensor, name) pairs that must
+    be fp32 [n]. Raises ValueError."""
+    torch = _torch()
+    if h.dim() != 2 or w.dim() != 2 or h.shape[1] != w.shape[1]:
+        raise ValueError(f"h must be [n, hidden] and w [vocab, hidden], got {tuple(h.shape)}, {tuple(w.shape)}")
+    n = h.shape[0]
+    _expect(targets, "targets", (n,), torch.int32)
+    for t, nme in f32:
+        if t is not None:
+            _expect(t, nme, (n,), torch.float32)
+    if dh is not None:
+        _expect(dh, "dh", h.shape, h.dtype)
+    if workspace is not None and workspace.numel() * workspace.element_size() < need_ws:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                         f"needs {need_ws}")
+    if not devices:
+        return
+    for t, nme in [(h, "h"), (w, "w"), (targets, "targets"), (dh, "dh"), (workspace, "workspace")] + list(f32):
+        if t is not None:
+            _require(t, nme)
+            if t.device != h.device:
+                raise ValueError(f"{nme} is on {t.device}, h on {h.device}")
+
+
 def ce_fwd(h, w, targets, *, nll=None, lse=None, tgt=None, workspace=None, stream=None):
     """Per-token loss, LSE and target logit (fp32 [n] each) of the linear
     cross-entropy with logits h @ w.T, through ce_fwd (no logits tensor)."""
     torch = _torch()
-    for t, nme in ((h, "h"), (w, "w"), (targets, "targets")):
-        _require(t, nme)
+    f32 = ((nll, "nll"), (lse, "lse"), (tgt, "tgt"))
+    _check_ce(h, w, targets, f32=f32, devices=False)
     p = ce_params_for(h, w)
+    need = int(lib().ce_fwd_workspace_bytes(ctypes.byref(p)))
+    _check_ce(h, w, targets, f32=f32, workspace=workspace, need_ws=need)
     n = h.shape[0]
     nll = torch.empty(n, dtype=torch.float32, device=h.device) if nll is None else nll
     lse = torch.empty(n, dtype=torch.float32, device=h.device) if lse is None else lse
     tgt = torch.empty(n, dtype=torch.float32, device=h.device) if tgt is None else tgt
     if workspace is None:
-        workspace = torch.empty(max(lib().ce_fwd_workspace_bytes(ctypes.byref(p)), 1), dtype=torch.uint8,
-                                device=h.device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=h.device)
     st = lib().ce_fwd(ctypes.byref(p), _ptr(h), _ptr(w), _ptr(targets), _ptr(nll), _ptr(lse), _ptr(tgt),
-                      _ptr(workspace), workspace.numel(), _stream_ptr(stream))
+                      _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_ptr(stream))
     if st:
         raise AttnError(st, "ce_fwd")
     return nll, lse, tgt
@@ -306,15 +381,16 @@ def ce_fwd(h, w, targets, *, nll=None, lse=None, tgt=None, workspace=None, strea
 def ce_bwd(h, w, targets, lse, dnll, *, dh=None, workspace=None, stream=None):
     """dH [n, hidden] (h.dtype) of sum(dnll * nll), through ce_bwd."""
     torch = _torch()
-    for t, nme in ((h, "h"), (w, "w"), (targets, "targets"), (lse, "lse"), (dnll, "dnll")):
-        _require(t, nme)
+    f32 = ((lse, "lse"), (dnll, "dnll"))
+    _check_ce(h, w, targets, f32=f32, dh=dh, devices=False)
     p = ce_params_for(h, w)
+    need = int(lib().ce_bwd_workspace_bytes(ctypes.byref(p)))
+    _check_ce(h, w, targets, f32=f32, dh=dh, workspace=workspace, need_ws=need)
     dh = torch.empty_like(h) if dh is None else dh
     if workspace is None:
-        workspace = torch.empty(max(lib().ce_bwd_workspace_bytes(ctypes.byref(p)), 1), dtype=torch.uint8,
-                                device=h.device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=h.device)
     st = lib().ce_bwd(ctypes.byref(p), _ptr(h), _ptr(w), _ptr(targets), _ptr(lse), _ptr(dnll), _ptr(dh),
-                      _ptr(workspace), workspace.numel(), _stream_ptr(stream))
+                      _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_ptr(stream))
     if st:
         raise AttnError(st, "ce_bwd")
     return dh

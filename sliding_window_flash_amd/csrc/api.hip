@@ -90,8 +90,9 @@ static attn_status_t check_mask(const attn_params_t* p, const attn_mask_t* m) {
   if (m == nullptr) return ATTN_ERR_NULL;
   if (m->row_words < 1 || m->row_words % 4 != 0 || m->row_words < ((int64_t)p->max_seqlen_k + 31) / 32)
     return ATTN_ERR_SHAPE;
-  // a 64-row mask tile is addressed with 32-bit byte offsets
-  if (m->row_words > (1 << 24)) return ATTN_ERR_UNSUPPORTED;
+  // a 64-row mask tile is addressed with 32-bit byte offsets: 64 rows x
+  // row_words x 4 bytes must stay below 2^32
+  if (m->row_words >= (1 << 24)) return ATTN_ERR_UNSUPPORTED;
   return check_tensor(m->bits, (int64_t)p->total_q * m->row_words, true);
 }
 

@@ -147,6 +147,12 @@ def test_masked_entry_points_refuse_before_launch():
     big = good(total_q=200, total_k=200, max_seqlen_k=200, max_seqlen_q=200)
     assert fw(ctypes.byref(_mask(row_words=4)), p=big) == 2   # 200 keys need 7 words
     assert fw(ctypes.byref(_mask(row_words=(1 << 24) + 4))) == 4
+    # a 64-row mask tile spans 64 x row_words x 4 bytes, which must stay below
+    # 2^32: 2^24 words is refused, the largest multiple of 4 below it accepted
+    # (the call then stops at the NULL LSE that follows the mask checks)
+    assert fw(ctypes.byref(_mask(row_words=1 << 24))) == 4
+    assert L.attn_fwd_masked(ctypes.byref(p), ctypes.byref(_mask(row_words=(1 << 24) - 4)), 16, 16, 16, 16, 16,
+                             16, None, None) == 1
     assert fw(ctypes.byref(_mask()), p=good(window=0)) == 3  # parameter checks come first
     need = swa.workspace_bytes(p)
     args = [16] * 11
