@@ -96,19 +96,36 @@ def check_host_ram(nbytes: int, ceiling: Optional[int] = None) -> None:
 
 
 def visible_cells(lq: int, lk: int, window: int, causal: bool,
-                  rows: Optional[np.ndarray] = None, allowed: Optional[np.ndarray] = None) -> np.ndarray:
-    """Boolean [len(rows), lk] mask of visible (query, key) cells. ``allowed``,
-    if given, is the caller's mask for these rows ([len(rows), >= lk])."""
+                  rows: Optional[np.ndarray] = None, allowed: Optional[np.ndarray] = None,
+                  cols: Optional[tuple] = None) -> np.ndarray:
+    """Boolean [len(rows), c1 - c0] mask of visible (query, key) cells over
+    keys [c0, c1) = ``cols`` (default: all lk keys). ``allowed``, if given, is
+    the caller's mask for these rows ([len(rows), >= lk])."""
+    c0, c1 = (0, lk) if cols is None else cols
     i = np.arange(lq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
-    j = np.arange(lk, dtype=np.int64)
+    j = np.arange(c0, c1, dtype=np.int64)
     pos = (i + (lk - lq))[:, None]
     if not causal:
         vis = np.abs(pos - j[None, :]) < window
     else:
         vis = (j[None, :] <= pos) & (pos - j[None, :] < window)
     if allowed is not None:
-        vis = vis & np.asarray(allowed, dtype=bool)[:, :lk]
+        vis = vis & np.asarray(allowed, dtype=bool)[:, c0:c1]
     return vis
+
+
+def key_band(r0: int, r1: int, lq: int, lk: int, window: int, causal: bool) -> tuple:
+    """Keys [c0, c1) outside which query rows [r0, r1) of one sequence see
+    nothing: their positions run from p0 = r0 + (lk - lq) to p1 = r1 - 1 +
+    (lk - lq), a causal row sees keys (p - window, p] and a two-sided row keys
+    (p - window, p + window). Every cell outside the band is masked (-inf),
+    so its exp is exactly 0 and it adds nothing to any sum: leaving it out
+    changes no result beyond the order of the sums."""
+    delta = lk - lq
+    p0, p1 = r0 + delta, r1 - 1 + delta
+    c0 = max(0, p0 - window + 1)
+    c1 = min(lk, p1 + 1) if causal else min(lk, p1 + window)
+    return c0, max(c0, c1)
 
 
 def _mask_rows(mask, q0, rows):
@@ -156,7 +173,8 @@ def _check_shapes(q, k, v, do, cu_q, cu_k):
 def sdpa_reference(q, k, v, do, cu_q, cu_k, scale: float, window: int, causal: bool, *,
                    with_backward: bool = True, panel_rows: int = 512,
                    ram_ceiling: Optional[int] = None, heads: Optional[Iterable[int]] = None,
-                   query_rows: Optional[tuple] = None, mask: Optional[np.ndarray] = None) -> dict:
+                   query_rows: Optional[tuple] = None, mask: Optional[np.ndarray] = None,
+                   band: bool = False) -> dict:
     """Full forward (and backward) over a packed batch.
 
     q, do: [T_q, Hq, d]; k, v: [T_k, Hkv, d]; cu_q, cu_k: [B+1] offsets.
@@ -167,6 +185,9 @@ def sdpa_reference(q, k, v, do, cu_q, cu_k, scale: float, window: int, causal: b
     heads and to rows r0 <= i < r1 of every sequence (a timing sample; rows
     and heads left out stay at their initial values, and dK/dV then hold only
     the contributions of the rows computed). ``mask``: see the module header.
+    ``band``: each panel takes only the keys of :func:`key_band` instead of all
+    L_k keys (the cells left out are masked, so the result is the same up to
+    summation order; at a window far below L_k it is far cheaper).
     """
     tq, tk, hq, hkv, d = _check_shapes(q, k, v, do if with_backward else None, cu_q, cu_k)
     grp = hq // hkv
@@ -196,18 +217,20 @@ def sdpa_reference(q, k, v, do, cu_q, cu_k, scale: float, window: int, causal: b
             for r0 in range(row_lo, row_hi, rows_per):
                 r1 = min(row_hi, r0 + rows_per)
                 rr = np.arange(r0, r1)
-                vis = visible_cells(lq, lk, window, causal, rr, _mask_rows(mask, q0, rr))
+                c0, c1 = key_band(r0, r1, lq, lk, window, causal) if band else (0, lk)
+                vis = visible_cells(lq, lk, window, causal, rr, _mask_rows(mask, q0, rr), cols=(c0, c1))
                 qh = _as64(q[q0 + r0:q0 + r1, h, :])
                 doh = _as64(do[q0 + r0:q0 + r1, h, :]) if with_backward else None
-                res = _panel(qh, kg, vg, doh, vis, scale, with_backward)
+                kb, vb = kg[c0:c1], vg[c0:c1]
+                res = _panel(qh, kb, vb, doh, vis, scale, with_backward)
                 o[q0 + r0:q0 + r1, h, :] = res["o"]
                 lse[h, q0 + r0:q0 + r1] = res["lse"]
                 if with_backward:
                     ds = res["ds"]
                     delta[h, q0 + r0:q0 + r1] = res["delta"]
-                    dq[q0 + r0:q0 + r1, h, :] = scale * (ds @ kg)
-                    dk[k0:k1, g, :] += scale * (ds.T @ qh)
-                    dv[k0:k1, g, :] += res["p"].T @ doh
+                    dq[q0 + r0:q0 + r1, h, :] = scale * (ds @ kb)
+                    dk[k0 + c0:k0 + c1, g, :] += scale * (ds.T @ qh)
+                    dv[k0 + c0:k0 + c1, g, :] += res["p"].T @ doh
     return out
 
 

@@ -6,7 +6,7 @@ import pytest
 
 import oracle_pins as pins
 from oracle import dense
-from sliding_window_flash_amd.workloads import INT32_MAX, make_inputs, small_case
+from sliding_window_flash_amd.workloads import INT32_MAX, make_inputs, random_mask, small_case
 
 
 @pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
@@ -108,3 +108,52 @@ def test_row_and_head_sample_matches_full_reference():
         np.testing.assert_allclose(part["dq"][r, 2], full["dq"][r, 2], atol=1e-13)
         np.testing.assert_allclose(part["lse"][2, r], full["lse"][2, r], atol=1e-13)
     assert np.all(part["o"][:, [0, 1, 3]] == 0)
+
+
+@pytest.mark.parametrize("lq,lk", [(300, 300), (40, 300), (1, 1), (7, 200), (0, 5), (513, 600)])
+@pytest.mark.parametrize("window", [1, 2, 31, 64, 129, 700, INT32_MAX])
+@pytest.mark.parametrize("causal", [True, False])
+def test_key_band_holds_every_visible_cell(lq, lk, window, causal):
+    """Brute force over every row panel: no visible cell lies outside the band,
+    and the band's first and last keys are visible to some row of the panel
+    (so the band is exactly the span of the visible keys when that span is not
+    empty)."""
+    full = dense.visible_cells(lq, lk, window, causal)
+    for rows_per in (1, 5, 64, 512):
+        for r0 in range(0, lq, rows_per):
+            r1 = min(lq, r0 + rows_per)
+            c0, c1 = dense.key_band(r0, r1, lq, lk, window, causal)
+            part = full[r0:r1]
+            outside = np.ones(lk, bool)
+            outside[c0:c1] = False
+            assert not part[:, outside].any(), (r0, r1, c0, c1)
+            if part.any():
+                cols = np.nonzero(part.any(axis=0))[0]
+                assert (cols[0], cols[-1] + 1) == (c0, c1), (r0, r1, c0, c1, cols[0], cols[-1])
+
+
+@pytest.mark.parametrize("case", [
+    ([300, 1, 517, 64], None, 8, 2, 16, 129, True),
+    ([100, 40], [700, 300], 4, 1, 8, 16, True),     # queries shorter than keys
+    ([200, 0, 333], None, 4, 2, 8, 65, False),      # two-sided, empty sequence
+    ([257], None, 2, 2, 8, 1, True),                # window 1
+    ([257, 90], None, 2, 1, 8, INT32_MAX, True),    # plain causal
+    ([200, 333], None, 2, 1, 8, INT32_MAX, False),  # full attention
+])
+@pytest.mark.parametrize("masked", [False, True])
+def test_band_reference_matches_full_reference(case, masked):
+    lq, lk, hq, hkv, d, win, causal = case
+    w = small_case(lq, lk, heads_q=hq, heads_kv=hkv, head_dim=d, window=win, causal=causal, seed=61)
+    x = make_inputs(w)
+    kw = {}
+    if masked:
+        kw["mask"] = random_mask(w, 0.6, seed=62, empty_rows=3)
+    args = (x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale, w.window, w.causal)
+    full = dense.sdpa_reference(*args, panel_rows=100, **kw)
+    band = dense.sdpa_reference(*args, panel_rows=100, band=True, **kw)
+    for key in ("o", "lse", "delta", "dq", "dk", "dv"):
+        a, b = band[key], full[key]
+        fin = np.isfinite(b)
+        assert np.array_equal(np.isfinite(a), fin), key
+        tol = 1e-12 * max(1.0, float(np.abs(b[fin]).max(initial=0.0)))
+        assert float(np.abs(a[fin] - b[fin]).max(initial=0.0)) <= tol, key
