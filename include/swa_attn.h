@@ -83,7 +83,8 @@ typedef enum {
                                a two-sided window with max_seqlen_k > 2^30 */
   ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than attn_bwd_workspace_bytes */
   ATTN_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
-  ATTN_ERR_ALIGN = 7        /* a tensor pointer is not 16-byte aligned */
+  ATTN_ERR_ALIGN = 7,       /* a tensor pointer is not 16-byte aligned */
+  ATTN_ERR_TOO_LARGE = 8    /* attn_bwd_noalloc: the problem needs more than ATTN_NOALLOC_SCRATCH_BYTES */
 } attn_status_t;
 
 typedef struct {
@@ -121,6 +122,31 @@ attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, con
                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dq,
                        void* dk, void* dv, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* Bytes of the fixed device array attn_bwd_noalloc keeps per GPU. */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* attn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The backward's D and LSE * log2(e) go to a fixed
+ * array of ATTN_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on, from the first call there until the process ends. The call
+ * allocates nothing; the first call on a GPU looks up the array's device
+ * address (the HIP runtime may load the library's code object on that GPU
+ * then), later calls reuse it. Same arguments (minus the workspace), outputs
+ * and errors as attn_bwd, plus ATTN_ERR_TOO_LARGE, returned before any HIP
+ * call, when attn_bwd_workspace_bytes(p) exceeds ATTN_NOALLOC_SCRATCH_BYTES
+ * (heads_q x total_q above about 4.19 million rows). The GPU is the one of
+ * `stream` (the current device for NULL).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that can overlap in time on one GPU (other streams, other
+ * host threads) race and give wrong results; calls ordered on one stream are
+ * safe. Nothing in it needs clearing first: the dQ launch writes every entry
+ * the dK/dV launch reads. */
+attn_status_t attn_bwd_noalloc(const attn_params_t* p, const void* q, const void* k, const void* v,
+                               const void* o, const float* lse, const void* dout,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dq,
+                               void* dk, void* dv, void* stream);
 
 /* The backward's stages, for callers that schedule them themselves:
  *   ATTN_BWD_DELTA: D = rowsum(dO * O) and LSE * log2(e) into the workspace;

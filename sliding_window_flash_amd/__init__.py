@@ -21,13 +21,15 @@ INT32_MAX = 2**31 - 1
 STATUS = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_WINDOW",
     4: "ATTN_ERR_UNSUPPORTED", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP", 7: "ATTN_ERR_ALIGN",
+    8: "ATTN_ERR_TOO_LARGE",
 }
+NOALLOC_SCRATCH_BYTES = 32 << 20   # ATTN_NOALLOC_SCRATCH_BYTES
 
 BWD_DELTA, BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 4, 7
 
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_stages", "attn_bwd_workspace_bytes", "attn_status_str",
             "attn_check_params", "attn_tile_sizes", "attn_query_tile_range",
-            "attn_key_tile_range", "attn_fwd_masked", "attn_bwd_masked",
+            "attn_key_tile_range", "attn_fwd_masked", "attn_bwd_masked", "attn_bwd_noalloc",
             "ce_check_params", "ce_fwd_workspace_bytes", "ce_fwd", "ce_bwd_workspace_bytes", "ce_bwd")
 
 
@@ -78,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_stages.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       vp, vp, ctypes.c_size_t, vp]
         L.attn_bwd_stages.restype = ctypes.c_int
+        L.attn_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.attn_bwd_noalloc.restype = ctypes.c_int
         L.attn_bwd_workspace_bytes.argtypes = [P]
         L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
         M = ctypes.POINTER(AttnMask)
@@ -314,6 +318,25 @@ def bwd(q, k, v, o, lse, do, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=I
         st, what = lib().attn_bwd_masked(ctypes.byref(p), ctypes.byref(m), *args), "attn_bwd_masked"
     if st:
         raise AttnError(st, what)
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, lse, do, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=INT32_MAX,
+                causal=True, scale=None, dq=None, dk=None, dv=None, stream=None):
+    """dQ, dK, dV through attn_bwd_noalloc: no workspace, the library's fixed
+    per-GPU scratch instead (calls that overlap on one GPU race). Pass dq, dk
+    and dv to allocate nothing here either."""
+    torch = _torch()
+    _check_attn(q, k, v, cu_q, cu_k, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv)
+    p = params_for(q, k, cu_q, cu_k, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
+                   window=window, causal=causal, scale=scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    st = lib().attn_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                _ptr(cu_q), _ptr(cu_k), _ptr(dq), _ptr(dk), _ptr(dv), _stream_ptr(stream))
+    if st:
+        raise AttnError(st, "attn_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -158,7 +158,8 @@ static attn_status_t bwd_impl(const attn_params_t* p, const attn_mask_t* mask, i
                               const void* q, const void* k, const void* v, const void* o,
                               const float* lse, const void* dout, const int32_t* cu_seqlens_q,
                               const int32_t* cu_seqlens_k, void* dq, void* dk, void* dv,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              bool use_scratch = false) {
   attn_status_t s = attn_check_params(p);
   if (s != ATTN_OK) return s;
   if (mask != nullptr && (s = check_mask(p, mask)) != ATTN_OK) return s;
@@ -181,6 +182,16 @@ static attn_status_t bwd_impl(const attn_params_t* p, const attn_mask_t* mask, i
   if (st_dkdv) {
     if ((s = check_tensor(dk, nk, true)) != ATTN_OK) return s;
     if ((s = check_tensor(dv, nk, true)) != ATTN_OK) return s;
+  }
+  if (use_scratch) {
+    // the library's fixed per-GPU array instead of a caller workspace: checked
+    // against its size before any HIP call, then looked up for the stream's GPU
+    if (attn_bwd_workspace_bytes(p) > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_TOO_LARGE;
+    int dev = 0;
+    const hipError_t e = stream != nullptr ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev)
+                                           : hipGetDevice(&dev);
+    if (e != hipSuccess || swa::noalloc_scratch(dev, &workspace) != hipSuccess) return ATTN_ERR_HIP;
+    workspace_bytes = ATTN_NOALLOC_SCRATCH_BYTES;
   }
   if (workspace == nullptr || workspace_bytes < attn_bwd_workspace_bytes(p)) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
@@ -225,6 +236,14 @@ attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, con
                   dk, dv, workspace, workspace_bytes, stream);
 }
 
+attn_status_t attn_bwd_noalloc(const attn_params_t* p, const void* q, const void* k, const void* v,
+                               const void* o, const float* lse, const void* dout,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dq,
+                               void* dk, void* dv, void* stream) {
+  return bwd_impl(p, nullptr, ATTN_BWD_ALL, q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, dq,
+                  dk, dv, nullptr, 0, stream, /*use_scratch=*/true);
+}
+
 attn_status_t attn_bwd_masked(const attn_params_t* p, const attn_mask_t* mask, const void* q,
                               const void* k, const void* v, const void* o, const float* lse,
                               const void* dout, const int32_t* cu_seqlens_q,
@@ -247,6 +266,7 @@ const char* attn_status_str(attn_status_t s) {
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_HIP: return "HIP launch error";
     case ATTN_ERR_ALIGN: return "pointer not aligned (tensors need 16 bytes)";
+    case ATTN_ERR_TOO_LARGE: return "the backward's D and LSE*log2(e) exceed the no-allocation entry point's fixed scratch (ATTN_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

@@ -32,8 +32,10 @@
 // step into the other stage and waited for at the step's one barrier.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
+#include "../../include/swa_attn.h"
 #include "kernel_common.hpp"
 #include "launch.hpp"
 #include "sched.hpp"
@@ -1418,6 +1420,39 @@ hipError_t launch_bwd(int dtype, int head_dim, int stages, const AttnArgs& a, hi
   if (dtype == 0 && head_dim == 128) return launch_bwd_t<float, 128>(stages, a, st);
   if (dtype == 0 && head_dim == 64) return launch_bwd_t<float, 64>(stages, a, st);
   return hipErrorInvalidValue;
+}
+
+// ------------------------------------------ scratch of the no-allocation backward
+// D and LSE * log2(e) for callers that cannot allocate device memory: a fixed
+// array in the code object, one copy per GPU, held until the process ends. On
+// the host `scratch` names a host-side stand-in, never the device memory: its
+// device address is looked up once per GPU, with that GPU current, and only
+// that address reaches kernels.
+static __device__ __align__(256) char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(int device, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[device] == nullptr) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != device) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[device] = p;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
 }
 
 template <int D> static void tiles_of(int* fwd_bm, int* fwd_bn, int* bwd_bn, int* bwd_bm) {

@@ -79,7 +79,7 @@ def test_parameter_checks(kw, code):
 
 def test_status_strings():
     L = swa.lib()
-    for code in range(8):
+    for code in range(9):
         s = L.attn_status_str(code).decode()
         assert s and s != "unknown status"
     assert L.attn_status_str(99).decode() == "unknown status"
@@ -199,3 +199,17 @@ def test_ce_refuses_before_launch():
     # several vocabulary chunks need the fp32 dH accumulator as well
     big = swa.ce_params(64, 40000, 256, swa.ATTN_BF16)
     assert L.ce_bwd_workspace_bytes(ctypes.byref(big)) >= 64 * 16384 * 2 + 64 * 256 * 4
+
+
+def test_noalloc_backward_refuses_before_any_hip_call():
+    L = swa.lib()
+    args = [16] * 11
+    assert L.attn_bwd_noalloc(ctypes.byref(good(window=0)), *args, None) == 3
+    bad = list(args)
+    bad[8] = None  # dq
+    assert L.attn_bwd_noalloc(ctypes.byref(good()), *bad, None) == 1
+    # 2 x 32 heads x 140,000 tokens x 4 bytes of D and LSE*log2e exceed the fixed scratch
+    big = good(heads_q=32, heads_kv=8, total_q=140000, total_k=140000, max_seqlen_q=140000,
+               max_seqlen_k=140000)
+    assert swa.workspace_bytes(big) > swa.NOALLOC_SCRATCH_BYTES
+    assert L.attn_bwd_noalloc(ctypes.byref(big), *args, None) == 8
