@@ -823,38 +823,63 @@ bwd_dkdv_kernel(AttnArgs a) {
   // tile) has no steps and writes zeros.
   const int nq = qr.hi >= qr.lo ? qr.hi - qr.lo + 1 : 0;
   const int steps = grp * nq;
-  int nh = g * grp, nqb = qr.lo;  // (head, query tile) of the next step to fill
   const uint32_t qsb = (uint32_t)(qstride * sizeof(T));
   TileLoader<T, BM, D, NT> qld;
   qld.init(qsb, w, lane);
-  // Query rows past L_q in a tile arrive as zeros (LSE*log2e and D too); they are masked.
+  // Fill state, kept as running offsets so that a step costs a few scalar
+  // adds: the next (head, query tile)'s element offset into Q and dO, its
+  // index into the [Hq, T_q] LSE*log2e and D arrays and (with M) its word
+  // offset into the mask. A fill advances one tile; after the range's last
+  // tile it returns to the first tile of the next head (the mask is shared by
+  // the heads, so its offset returns to the first tile's). Only the range's
+  // last tile can be partial: its rows past L_q arrive as zeros (LSE*log2e
+  // and D too) and are masked.
+  const int64_t tile_elems = (int64_t)BM * qstride;
+  int64_t qoff = (int64_t)(q0 + qr.lo * BM) * qstride + (int64_t)g * grp * D;
+  int64_t soff = (int64_t)g * grp * a.total_q + q0 + qr.lo * BM;
+  int64_t moff = (int64_t)(q0 + qr.lo * BM) * a.mask_words + 4 * kb;
+  const int64_t qwrap = D - (int64_t)(nq - 1) * tile_elems;
+  const int64_t swrap = (int64_t)a.total_q - (int64_t)(nq - 1) * BM;
+  const int64_t mstep = (int64_t)BM * a.mask_words;
+  const uint32_t last_rows = (uint32_t)min(BM, lq - qr.hi * BM);
+  int nqb = qr.lo;  // query tile of the next step to fill
   auto fill = [&](char* st) {
-    const int qvalid = min(BM, lq - nqb * BM);
-    const int64_t qoff = (int64_t)(q0 + nqb * BM) * qstride + nh * D;
+    const bool last = nqb == qr.hi;
+    const uint32_t qvalid = last ? last_rows : (uint32_t)BM;
     qld.issue(st, Qg + qoff, qsb, qvalid);
     qld.issue(st + QTile::kBytes, Dg + qoff, qsb, qvalid);
     if (w == 0) {
-      const int64_t idx = (int64_t)nh * a.total_q + q0 + nqb * BM;
-      buffer_to_lds4(buffer_rsrc(a.lse2 + idx, (uint32_t)qvalid * 4u), st + 2 * QTile::kBytes, (uint32_t)lane * 4u);
-      buffer_to_lds4(buffer_rsrc(a.delta + idx, (uint32_t)qvalid * 4u), st + 2 * QTile::kBytes + BM * 4,
-                       (uint32_t)lane * 4u);
+      buffer_to_lds4(buffer_rsrc(a.lse2 + soff, qvalid * 4u), st + 2 * QTile::kBytes, (uint32_t)lane * 4u);
+      buffer_to_lds4(buffer_rsrc(a.delta + soff, qvalid * 4u), st + 2 * QTile::kBytes + BM * 4,
+                     (uint32_t)lane * 4u);
     }
     if constexpr (M) {
       if (w == 1) {  // lane r: row r's words 4 kb .. 4 kb + 3; rows past L_q arrive as zeros
         const uint32_t rb = (uint32_t)a.mask_words * 4u;
-        buffer_to_lds16(buffer_rsrc(a.mask + (int64_t)(q0 + nqb * BM) * a.mask_words + 4 * kb, (uint32_t)qvalid * rb),
-                        st + kMaskOff, (uint32_t)lane * rb);
+        buffer_to_lds16(buffer_rsrc(a.mask + moff, qvalid * rb), st + kMaskOff, (uint32_t)lane * rb);
       }
     }
-    if (++nqb > qr.hi) {
+    if (last) {
       nqb = qr.lo;
-      ++nh;
+      qoff += qwrap;
+      soff += swrap;
+      moff -= (int64_t)(nq - 1) * mstep;
+    } else {
+      ++nqb;
+      qoff += tile_elems;
+      soff += BM;
+      moff += mstep;
     }
   };
   // odd step counts start in stage 1: the loop below runs whole stage pairs
   if (steps > 0) fill(steps & 1 ? st1 : st0);
   __syncthreads();
 
+  // The query tiles whose tile with this key tile has every cell visible (no
+  // per-cell mask), and those in which this wave's 32 keys x 32 queries see
+  // at least one cell: intervals computed once, tested per step.
+  const QbRange full_q = key_tile_full_query_tiles(sg, kb, BN, BM);
+  const QbRange seen_q = block_seen_query_tiles(sg, BM, 32 * mh, 32, kb * BN + 32 * kt, 32);
   int qb = qr.lo;  // query tile of the current step
   auto step = [&](auto stage_c, int t) {
     constexpr int stage = decltype(stage_c)::value;
@@ -862,15 +887,15 @@ bwd_dkdv_kernel(AttnArgs a) {
     const char* dos = qs + QTile::kBytes;
     const float* lse2s = reinterpret_cast<const float*>(qs + 2 * QTile::kBytes);
     const float* dlts = lse2s + BM;
-    const bool edge = !tile_full_i32(lq, lk, a.window, causal, qb, BM, kb, BN);
-    // this wave's 32 keys x 32 queries all masked: P = dS = 0, nothing to add
-    if (edge && block_masked(lq, lk, a.window, causal, qb * BM + 32 * mh, 32, kb * BN + 32 * kt, 32)) {
-      if (t + 1 < steps) fill(stage ? st0 : st1);
-      if (++qb > qr.hi) qb = qr.lo;
-      __syncthreads();
-      return;
-    }
-    f32x16 s = f32x16{}, dp = f32x16{};
+    const bool edge = qb < full_q.lo || qb > full_q.hi;
+    // this wave's 32 keys x 32 queries all masked: P = dS = 0, nothing to add;
+    // the wave skips both contraction phases but still fills and meets the
+    // barrier
+    const bool work = !edge || (seen_q.lo <= qb && qb <= seen_q.hi);
+    f32x16 s, dp;  // set and read only when `work`
+    if (work) {
+    s = f32x16{};
+    dp = f32x16{};
 #pragma unroll
     for (int ss = 0; ss < D / 16; ++ss) {
       mma(s, rrd.read(qs, 32 * mh, ss), rrd.read(klds, 32 * kt, ss));
@@ -903,10 +928,12 @@ bwd_dkdv_kernel(AttnArgs a) {
         dp[r] = pv * (dp[r] - d4[e]);  // dS
       }
     }
+    }
     // the next step's stage is filled here, after this step's row reads and
     // softmax, not at the top of the step, where the loads met the burst of
     // row reads every wave makes (moving them here cut dK/dV time by 4%)
     if (t + 1 < steps) fill(stage ? st0 : st1);
+    if (work) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const Frag<T> pf = acc_frag<T>(s, u);
@@ -916,6 +943,7 @@ bwd_dkdv_kernel(AttnArgs a) {
         mma(dva[dt], crd.read(dos, 32 * mh + 16 * u, dt), pf);
         mma(dka[dt], crd.read(qs, 32 * mh + 16 * u, dt), dsf);
       }
+    }
     }
     if (++qb > qr.hi) qb = qr.lo;
     __syncthreads();

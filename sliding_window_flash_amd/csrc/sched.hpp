@@ -178,6 +178,58 @@ SWA_HD bool block_masked(int32_t lq, int32_t lk, int32_t window, bool causal, in
   return (int64_t)b > p_last || too_old;
 }
 
+SWA_HD int64_t ceil_div(int64_t a, int64_t b) { return -floor_div(-a, b); }  // b > 0
+
+struct QbRange {
+  int32_t lo, hi;  // query tiles [lo, hi]; empty when lo > hi
+};
+
+// Query tiles qb (of bm rows) for which the block of rows [qb*bm + r0,
+// qb*bm + r0 + rows) and keys [c0, c0 + cols) of one sequence holds at least
+// one visible cell: exactly the qb for which block_masked() is false. Keys
+// [c0, b_last] are visible to rows [c0 - delta, b_last - delta + window - 1]
+// (causal) or [c0 - delta - window + 1, b_last - delta + window - 1]
+// (two-sided), clipped to [0, L_q); the block's rows meet that interval for a
+// contiguous run of qb. Computed once per key block, it replaces a per-step
+// test by two compares.
+SWA_HD QbRange block_seen_query_tiles(const SeqGeom& s, int32_t bm, int32_t r0, int32_t rows, int32_t c0,
+                                      int32_t cols) {
+  QbRange r{0, -1};
+  if (c0 >= s.lk || s.lq <= 0 || rows <= 0 || cols <= 0) return r;
+  const int64_t b_last = (int64_t)c0 + cols - 1 < s.lk - 1 ? (int64_t)c0 + cols - 1 : s.lk - 1;
+  int64_t ilo = s.causal ? (int64_t)c0 - s.delta() : (int64_t)c0 - s.delta() - s.window + 1;
+  int64_t ihi = b_last - s.delta() + s.window - 1;
+  if (ilo < 0) ilo = 0;
+  if (ihi > s.lq - 1) ihi = s.lq - 1;
+  if (ilo > ihi) return r;
+  int64_t lo = ceil_div(ilo - r0 - rows + 1, bm), hi = floor_div(ihi - r0, bm);
+  if (lo < 0) lo = 0;
+  if (lo > hi) return r;
+  r.lo = (int32_t)lo;
+  r.hi = (int32_t)hi;
+  return r;
+}
+
+// Query tiles qb (of bm rows) for which tile (qb, key tile kb of bn keys) has
+// every cell visible: exactly the qb for which tile_full_i32() is true. All bm
+// rows and bn keys must exist; causal: kb*bn + bn - 1 <= qb*bm + delta and
+// qb*bm + bm - 1 + delta - kb*bn < window; two-sided: the second condition and
+// kb*bn + bn - 1 - (qb*bm + delta) < window.
+SWA_HD QbRange key_tile_full_query_tiles(const SeqGeom& s, int32_t kb, int32_t bn, int32_t bm) {
+  QbRange r{0, -1};
+  const int64_t j0 = (int64_t)kb * bn;
+  if (j0 + bn > s.lk || s.lq < bm) return r;
+  int64_t lo = s.causal ? ceil_div(j0 + bn - 1 - s.delta(), bm) : ceil_div(j0 + bn - s.delta() - s.window, bm);
+  int64_t hi = floor_div(j0 + s.window - bm - s.delta(), bm);
+  const int64_t hi_rows = floor_div(s.lq - bm, bm);
+  if (hi > hi_rows) hi = hi_rows;
+  if (lo < 0) lo = 0;
+  if (lo > hi) return r;
+  r.lo = (int32_t)lo;
+  r.hi = (int32_t)hi;
+  return r;
+}
+
 // Is tile (query tile qb, key tile kb) free of masked cells?
 SWA_HD bool tile_is_full(const SeqGeom& s, int32_t qb, int32_t bm, int32_t kb, int32_t bn) {
   const TileRange r = query_tile_keys(s, qb, bm, bn);

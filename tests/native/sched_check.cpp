@@ -57,6 +57,54 @@ int main() {
         }
   printf("blocks checked %ld, mismatches %ld\n", bchecked, bbad);
   bad += bbad;
+  // the per-key-block intervals of query tiles against the per-step tests
+  // they replace: block_seen_query_tiles == !block_masked and
+  // key_tile_full_query_tiles == tile_full_i32, for every query tile
+  long ichecked = 0, ibad = 0;
+  for (int lq = 0; lq <= 200; lq += 7)
+    for (int dl : {0, 1, 37, 130})
+      for (int w : wins)
+        for (int causal = 0; causal <= 1; ++causal) {
+          const int lk = lq + dl;
+          const swa::SeqGeom g{lq, lk, w, causal != 0};
+          for (int bm : {32, 64})
+            for (int bn : {32, 64, 128})
+              for (int kb = 0; kb * bn < lk; ++kb) {
+                const swa::QbRange f = swa::key_tile_full_query_tiles(g, kb, bn, bm);
+                for (int qb = 0; qb * bm < lq + bm; ++qb) {
+                  const bool want = qb * bm < lq && swa::tile_full_i32(lq, lk, w, causal != 0, qb, bm, kb, bn);
+                  const bool got = f.lo <= qb && qb <= f.hi;
+                  ++ichecked;
+                  if (want != got) {
+                    if (ibad < 5)
+                      printf("full-range mismatch lq=%d lk=%d w=%d causal=%d bm=%d bn=%d kb=%d qb=%d: %d vs %d [%d,%d]\n",
+                             lq, lk, w, causal, bm, bn, kb, qb, want, got, f.lo, f.hi);
+                    ++ibad;
+                  }
+                }
+                for (int r0 : {0, 32})
+                  for (int c : {0, 32, 96})
+                    for (int rows : {32})
+                      for (int cols : {32}) {
+                        if (r0 + rows > bm || c + cols > bn) continue;
+                        const int c0 = kb * bn + c;
+                        const swa::QbRange v = swa::block_seen_query_tiles(g, bm, r0, rows, c0, cols);
+                        for (int qb = 0; qb * bm < lq + bm; ++qb) {
+                          const bool want = !swa::block_masked(lq, lk, w, causal != 0, qb * bm + r0, rows, c0, cols);
+                          const bool got = v.lo <= qb && qb <= v.hi;
+                          ++ichecked;
+                          if (want != got) {
+                            if (ibad < 5)
+                              printf("seen-range mismatch lq=%d lk=%d w=%d causal=%d bm=%d r0=%d c0=%d qb=%d: %d vs %d [%d,%d]\n",
+                                     lq, lk, w, causal, bm, r0, c0, qb, want, got, v.lo, v.hi);
+                            ++ibad;
+                          }
+                        }
+                      }
+              }
+        }
+  printf("intervals checked %ld, mismatches %ld\n", ichecked, ibad);
+  bad += ibad;
   printf("checked %ld, mismatches %ld\n", checked, bad);
   return bad != 0;
 }
