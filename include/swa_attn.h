@@ -110,7 +110,11 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
 
 /* Bytes of device workspace attn_bwd needs for these parameters: D =
  * rowsum(dO * O) and LSE * log2(e), each fp32 [heads_q, total_q] and 256-byte
- * aligned. 0 if the parameters are invalid. */
+ * aligned; plus, when the key tiles (128 keys) x heads_kv x batch are fewer
+ * than the GPU's 256 compute units, fp32 partial dK and dV [parts][2][total_k,
+ * heads_kv, head_dim] for the dK/dV launch, which then splits each KV group's
+ * query heads over 2, 4, ... workgroups (bf16 and fp16 at head_dim 64 and 128)
+ * and adds the parts in a second launch. 0 if the parameters are invalid. */
 size_t attn_bwd_workspace_bytes(const attn_params_t* p);
 
 /* Backward: the vector-Jacobian product of sum(O * dO). Reads Q, K, V, O, LSE

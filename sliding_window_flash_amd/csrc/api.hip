@@ -36,6 +36,7 @@ swa::AttnArgs base_args(const attn_params_t* p) {
   a.window = p->window;
   a.causal = p->causal;
   a.scale = p->scale;
+  a.kv_split = 1;
   return a;
 }
 
@@ -143,15 +144,28 @@ attn_status_t attn_fwd_masked(const attn_params_t* p, const attn_mask_t* mask, c
 }
 
 // Workspace: D [heads_q, total_q] fp32, then LSE*log2(e) [heads_q, total_q]
-// fp32, each 256-byte aligned.
+// fp32, each 256-byte aligned; then, when the dK/dV launch splits each KV
+// group's query heads over `split` workgroups (too few key tiles to fill the
+// GPU), the parts' fp32 partial dK and dV [split][2][total_k, heads_kv,
+// head_dim].
 static size_t ws_array_bytes(const attn_params_t* p) {
   const size_t n = (size_t)p->heads_q * (size_t)p->total_q * sizeof(float);
   return round_up(n > 0 ? n : 1, 256);
 }
 
+static int dkdv_split(const attn_params_t* p) {
+  return swa::dkdv_split(p->dtype, p->head_dim, p->heads_q, p->heads_kv, p->batch, p->max_seqlen_k);
+}
+
+static size_t ws_bytes(const attn_params_t* p, int split) {
+  size_t b = 2 * ws_array_bytes(p);
+  if (split > 1) b += (size_t)split * 2 * (size_t)p->total_k * p->heads_kv * p->head_dim * sizeof(float);
+  return b;
+}
+
 size_t attn_bwd_workspace_bytes(const attn_params_t* p) {
   if (attn_check_params(p) != ATTN_OK) return 0;
-  return 2 * ws_array_bytes(p);
+  return ws_bytes(p, dkdv_split(p));
 }
 
 static attn_status_t bwd_impl(const attn_params_t* p, const attn_mask_t* mask, int32_t stages,
@@ -183,17 +197,19 @@ static attn_status_t bwd_impl(const attn_params_t* p, const attn_mask_t* mask, i
     if ((s = check_tensor(dk, nk, true)) != ATTN_OK) return s;
     if ((s = check_tensor(dv, nk, true)) != ATTN_OK) return s;
   }
+  // the no-allocation entry point keeps D and LSE*log2(e) only: no head split
+  const int split = use_scratch ? 1 : dkdv_split(p);
   if (use_scratch) {
     // the library's fixed per-GPU array instead of a caller workspace: checked
     // against its size before any HIP call, then looked up for the stream's GPU
-    if (attn_bwd_workspace_bytes(p) > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_TOO_LARGE;
+    if (ws_bytes(p, 1) > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_TOO_LARGE;
     int dev = 0;
     const hipError_t e = stream != nullptr ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev)
                                            : hipGetDevice(&dev);
     if (e != hipSuccess || swa::noalloc_scratch(dev, &workspace) != hipSuccess) return ATTN_ERR_HIP;
     workspace_bytes = ATTN_NOALLOC_SCRATCH_BYTES;
   }
-  if (workspace == nullptr || workspace_bytes < attn_bwd_workspace_bytes(p)) return ATTN_ERR_WORKSPACE;
+  if (workspace == nullptr || workspace_bytes < ws_bytes(p, split)) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
   swa::AttnArgs a = base_args(p);
   a.q = q;
@@ -209,6 +225,8 @@ static attn_status_t bwd_impl(const attn_params_t* p, const attn_mask_t* mask, i
   a.dv = dv;
   a.delta = static_cast<float*>(workspace);
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_array_bytes(p));
+  a.kv_split = split;
+  if (split > 1) a.dkv_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * ws_array_bytes(p));
   if (mask != nullptr) {
     a.mask = mask->bits;
     a.mask_words = mask->row_words;

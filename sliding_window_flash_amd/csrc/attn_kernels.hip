@@ -777,7 +777,11 @@ bwd_dkdv_kernel(AttnArgs a) {
   const int w = wave_uniform(tid >> 6);
   const int kt = w & 3, mh = w >> 2;
   const int nkb = (a.max_seqlen_k + BN - 1) / BN;
-  int L = xcd_remap((int)blockIdx.x, nkb * a.heads_kv * a.batch);
+  // work item: (KV head, sequence, key tile, part of the group's query heads),
+  // the part innermost so that the parts of one key tile share an L2
+  int L = xcd_remap((int)blockIdx.x, nkb * a.heads_kv * a.batch * a.kv_split);
+  const int part = L % a.kv_split;
+  L /= a.kv_split;
   const int kb = L % nkb;
   L /= nkb;
   const int b = L % a.batch;
@@ -786,6 +790,8 @@ bwd_dkdv_kernel(AttnArgs a) {
   const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
   if (kb * BN >= lk) return;
   const int grp = a.heads_q / a.heads_kv;
+  const int hpp = grp / a.kv_split;           // query heads of this part
+  const int h0 = g * grp + part * hpp;        // its first query head
   const bool causal = a.causal != 0;
   const SeqGeom sg{lq, lk, a.window, causal};
   const TileRange qr = key_tile_queries(sg, kb, BN, BM);
@@ -818,11 +824,11 @@ bwd_dkdv_kernel(AttnArgs a) {
   const T* __restrict__ Qg = static_cast<const T*>(a.q);
   const T* __restrict__ Dg = static_cast<const T*>(a.dout);
 
-  // Steps walk (head, query tile) pairs: head g*grp .. g*grp+grp-1 outer,
-  // query tile qr.lo .. qr.hi inner. An empty range (no query sees this key
-  // tile) has no steps and writes zeros.
+  // Steps walk (head, query tile) pairs: head h0 .. h0+hpp-1 outer, query
+  // tile qr.lo .. qr.hi inner. An empty range (no query sees this key tile)
+  // has no steps and writes zeros.
   const int nq = qr.hi >= qr.lo ? qr.hi - qr.lo + 1 : 0;
-  const int steps = grp * nq;
+  const int steps = hpp * nq;
   const uint32_t qsb = (uint32_t)(qstride * sizeof(T));
   TileLoader<T, BM, D, NT> qld;
   qld.init(qsb, w, lane);
@@ -835,8 +841,8 @@ bwd_dkdv_kernel(AttnArgs a) {
   // last tile can be partial: its rows past L_q arrive as zeros (LSE*log2e
   // and D too) and are masked.
   const int64_t tile_elems = (int64_t)BM * qstride;
-  int64_t qoff = (int64_t)(q0 + qr.lo * BM) * qstride + (int64_t)g * grp * D;
-  int64_t soff = (int64_t)g * grp * a.total_q + q0 + qr.lo * BM;
+  int64_t qoff = (int64_t)(q0 + qr.lo * BM) * qstride + (int64_t)h0 * D;
+  int64_t soff = (int64_t)h0 * a.total_q + q0 + qr.lo * BM;
   int64_t moff = (int64_t)(q0 + qr.lo * BM) * a.mask_words + 4 * kb;
   const int64_t qwrap = D - (int64_t)(nq - 1) * tile_elems;
   const int64_t swrap = (int64_t)a.total_q - (int64_t)(nq - 1) * BM;
@@ -973,9 +979,33 @@ bwd_dkdv_kernel(AttnArgs a) {
   }
   if (key_ok) {
     const int64_t roff = (int64_t)(k0 + j) * kstride + g * D;
-    if (mh == 0) store_acc_rows<T, D>(static_cast<T*>(a.dk) + roff, dka, a.scale, half);
-    else store_acc_rows<T, D>(static_cast<T*>(a.dv) + roff, dva, 1.f, half);
+    if (a.kv_split == 1) {
+      if (mh == 0) store_acc_rows<T, D>(static_cast<T*>(a.dk) + roff, dka, a.scale, half);
+      else store_acc_rows<T, D>(static_cast<T*>(a.dv) + roff, dva, 1.f, half);
+    } else {  // this part's fp32 partial sums; bwd_dkdv_sum_kernel adds the parts
+      float* pk = a.dkv_part + (int64_t)part * 2 * a.total_k * kstride;
+      if (mh == 0) store_acc_rows<float, D>(pk + roff, dka, 1.f, half);
+      else store_acc_rows<float, D>(pk + (int64_t)a.total_k * kstride + roff, dva, 1.f, half);
+    }
   }
+}
+
+// dK = scale * (sum of the parts' dK partials) and dV = sum of the dV
+// partials, converted to T: 4 consecutive elements per thread. Every key row
+// of every sequence was written by every part (zeros where no query sees it).
+template <typename T>
+__global__ void __launch_bounds__(256) bwd_dkdv_sum_kernel(AttnArgs a, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const int64_t n = n4 * 4;  // elements of dK (and of dV)
+  f32x4 k4 = {0.f, 0.f, 0.f, 0.f}, v4 = {0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < a.kv_split; ++p) {
+    const float* pk = a.dkv_part + (int64_t)p * 2 * n;
+    k4 += *reinterpret_cast<const f32x4*>(pk + 4 * i);
+    v4 += *reinterpret_cast<const f32x4*>(pk + n + 4 * i);
+  }
+  store4<T>(static_cast<T*>(a.dk) + 4 * i, k4[0] * a.scale, k4[1] * a.scale, k4[2] * a.scale, k4[3] * a.scale);
+  store4<T>(static_cast<T*>(a.dv) + 4 * i, v4[0], v4[1], v4[2], v4[3]);
 }
 
 // ------------------------------------------ backward: dK, dV at head_dim 256
@@ -1410,9 +1440,16 @@ static hipError_t launch_bwd_m(int stages, const AttnArgs& a, hipStream_t st) {
     if constexpr (D > 128)
       hipLaunchKernelGGL((bwd_dkdv_wide_kernel<T, D, TL::kBwdBN, TL::kBwdBM, M>), dim3((unsigned)g2), dim3(256), 0,
                          st, a);
-    else if constexpr (sizeof(T) == 2)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, TL::kBwdBN, TL::kBwdBM, M>), dim3((unsigned)g2),
+    else if constexpr (sizeof(T) == 2) {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, TL::kBwdBN, TL::kBwdBM, M>), dim3((unsigned)(g2 * a.kv_split)),
                          dim3(TL::kBwdBN * 4), 0, st, a);
+      if (a.kv_split > 1) {
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int64_t n4 = (int64_t)a.total_k * a.heads_kv * D / 4;
+        if (n4 > 0)
+          hipLaunchKernelGGL((bwd_dkdv_sum_kernel<T>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, a, n4);
+      }
+    }
     else
       hipLaunchKernelGGL((bwd_dkdv4_kernel<T, D, TL::kBwdBN, TL::kBwdBM, M>), dim3((unsigned)g2),
                          dim3(TL::kBwdBN * 2), 0, st, a);
@@ -1488,6 +1525,19 @@ template <int D> static void tiles_of(int* fwd_bm, int* fwd_bn, int* bwd_bn, int
   *fwd_bn = Tiles<D>::kFwdBN;
   *bwd_bn = Tiles<D>::kBwdBN;
   *bwd_bm = Tiles<D>::kBwdBM;
+}
+
+// Parts the dK/dV launch splits each KV group's query heads into: 1 when the
+// key-major grid (key tiles x KV heads x sequences) already has a workgroup
+// for each of the 256 compute units, else the fewest halvings of the group
+// that reach that many (the 8-wave 16-bit kernel only).
+int dkdv_split(int dtype, int head_dim, int heads_q, int heads_kv, int batch, int max_seqlen_k) {
+  if (dtype == 0 || head_dim > 128) return 1;
+  const int64_t g2 = (int64_t)((max_seqlen_k + Tiles<128>::kBwdBN - 1) / Tiles<128>::kBwdBN) * heads_kv * batch;
+  const int grp = heads_q / heads_kv;
+  int s = 1;
+  while (g2 * s < 256 && grp % (2 * s) == 0) s *= 2;
+  return s;
 }
 
 bool tile_sizes(int dtype, int head_dim, int* fwd_bm, int* fwd_bn, int* bwd_bn, int* bwd_bm) {

@@ -265,13 +265,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
+// The LDS address of a generic pointer into shared memory: the generic
+// aperture keeps the LDS offset in the low 32 bits. Taking them directly,
+// rather than casting the pointer, spares the null check that a generic to
+// LDS cast carries (a compare against the aperture base per call).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wint-to-void-pointer-cast"
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_addr(const void* p) {
+  return (__attribute__((address_space(3))) void*)(uint32_t)(uintptr_t)p;
+}
+#pragma clang diagnostic pop
+
 // One buffer load per lane into LDS, 16 or 4 bytes: lane l's data lands at
 // lds + l * bytes (lds wave-uniform).
 __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, char* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_addr(lds), 16, voff, 0, 0, 0);
 }
 __device__ __forceinline__ void buffer_to_lds4(__amdgpu_buffer_rsrc_t rsrc, char* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_addr(lds), 4, voff, 0, 0, 0);
 }
 
 // Direct global -> LDS copy of a ROWS x D tile into the swizzled layout
@@ -397,6 +408,12 @@ struct AttnArgs {
   void* dv;
   float* delta;  // D = rowsum(dO * O), [heads_q, total_q]
   float* lse2;   // LSE * log2(e) (+inf where LSE = -inf), [heads_q, total_q]
+  // dK/dV with the group's query heads split over kv_split workgroups per key
+  // tile (kv_split > 1 when there are too few key tiles to fill the GPU):
+  // fp32 partial sums [kv_split][dK, dV][total_k, heads_kv, head_dim], added
+  // up by a second launch
+  float* dkv_part;
+  int32_t kv_split;
   // optional mask combined with the window: row t (packed query token) is
   // mask_words uint32 words, bit j % 32 of word j / 32 allows key j of the
   // token's sequence; nullptr = no mask

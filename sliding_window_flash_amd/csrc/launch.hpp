@@ -12,6 +12,8 @@ hipError_t launch_fwd(int dtype, int head_dim, const AttnArgs& a, hipStream_t st
 // 2 = dQ, 4 = dK/dV (run in that order)
 hipError_t launch_bwd(int dtype, int head_dim, int stages, const AttnArgs& a, hipStream_t st);
 bool tile_sizes(int dtype, int head_dim, int* fwd_bm, int* fwd_bn, int* bwd_bn, int* bwd_bm);
+// dK/dV head split for small key-major grids (AttnArgs::kv_split)
+int dkdv_split(int dtype, int head_dim, int heads_q, int heads_kv, int batch, int max_seqlen_k);
 // Device address, on GPU `device`, of the fixed scratch array the
 // no-allocation backward uses for D and LSE * log2(e) (looked up once per
 // device with that device current, then cached).

@@ -1,9 +1,13 @@
 """attn_bwd_noalloc (no workspace argument, the library's fixed per-GPU
 scratch for D and LSE * log2 e) against attn_bwd on the same inputs, through
 the C ABI: two calls in a row, the second on a smaller problem, so the second
-runs on scratch still holding the first call's values. The outputs must equal
-attn_bwd's bit for bit (the same kernels read the same values), and each
-call's outputs must also meet the oracle's tolerance."""
+runs on scratch still holding the first call's values. dQ must equal
+attn_bwd's bit for bit (the same kernel reads the same values); so must dK and
+dV when attn_bwd does not split the dK/dV launch over query heads (the first
+call, whose key tiles fill the GPU). With the split (the second call) attn_bwd
+adds the heads' partial sums in another order, so dK and dV are held to the
+oracle's tolerance against it. Each call's outputs must also meet the
+oracle's tolerance."""
 import numpy as np
 import pytest
 
@@ -21,7 +25,7 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-def _case(w):
+def _case(w, bitwise_dkdv):
     import torch
     H.say(f"no-alloc case {w.name}: lengths_q={w.lengths_q} lengths_k={w.lengths_k} Hq={w.heads_q} "
           f"Hkv={w.heads_kv} d={w.head_dim} window={w.window} dtype={w.dtype}")
@@ -35,20 +39,25 @@ def _case(w):
     got = [torch.full_like(t, float("nan")) for t in ref]
     swa.bwd_noalloc(q, k, v, o, lse, do, dev["cu_q"], dev["cu_k"], dq=got[0], dk=got[1], dv=got[2], **kw)
     torch.cuda.synchronize()
-    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
-        assert torch.equal(a, b), f"{name} differs from attn_bwd"
+    assert torch.equal(got[0], ref[0]), "dq differs from attn_bwd"
+    for name, a, b in zip(("dk", "dv"), got[1:], ref[1:]):
+        if bitwise_dkdv:
+            assert torch.equal(a, b), f"{name} differs from attn_bwd"
+        else:
+            H.compare(f"{name} against attn_bwd", H.host64(a), H.host64(b), w.dtype)
     stats = H.compare_full(w, x, dict(dq=got[0], dk=got[1], dv=got[2]))
     H.say("  ", {kk: {k2: f"{v2:.2e}" for k2, v2 in vv.items()} for kk, vv in stats.items()})
 
 
 def test_two_calls_second_smaller():
-    first = small_case([700, 1, 517, 300], None, heads_q=8, heads_kv=2, head_dim=128, window=129,
+    # 32 key tiles x 8 KV heads = 256 dK/dV workgroups: attn_bwd does not split
+    first = small_case([4096], None, heads_q=16, heads_kv=8, head_dim=128, window=129,
                        dtype="bf16", do_scale=0.1, seed=41)
     second = small_case([100, 40], [700, 300], heads_q=4, heads_kv=1, head_dim=64, window=16,
                         dtype="bf16", do_scale=0.1, seed=42)
     assert first.heads_q * first.total_q > second.heads_q * second.total_q
-    _case(first)
-    _case(second)
+    _case(first, bitwise_dkdv=True)
+    _case(second, bitwise_dkdv=False)
 
 
 def test_refuses_beyond_scratch():
