@@ -61,9 +61,10 @@ attn_status_t attn_check_params(const attn_params_t* p) {
     return ATTN_ERR_SHAPE;
   if (p->window < 1) return ATTN_ERR_WINDOW;
   if (p->dtype != ATTN_F32 && p->dtype != ATTN_BF16 && p->dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
-  // head_dim 256 is built for the 16-bit types (fp32 at 256 would need twice
-  // the registers and LDS of the 16-bit kernels)
-  if (p->head_dim != 64 && p->head_dim != 128 && !(p->head_dim == 256 && p->dtype != ATTN_F32))
+  // head_dim 256 and 512 are built for the 16-bit types (fp32 there would need
+  // twice the registers and LDS of the 16-bit kernels)
+  if (p->head_dim != 64 && p->head_dim != 128 &&
+      !((p->head_dim == 256 || p->head_dim == 512) && p->dtype != ATTN_F32))
     return ATTN_ERR_UNSUPPORTED;
   if (p->causal != 0 && p->causal != 1) return ATTN_ERR_UNSUPPORTED;
   // a two-sided window (no causal mask, window < max_seqlen_k) forms p + window
@@ -72,9 +73,11 @@ attn_status_t attn_check_params(const attn_params_t* p) {
   // the kernels fold the scale into exp2 arguments and take row maxima on raw
   // scores, which needs a positive scale
   if (!(p->scale > 0.f) || !isfinite(p->scale)) return ATTN_ERR_UNSUPPORTED;
-  // tile loads address a 128-row tile with 32-bit byte offsets (128 rows x
-  // heads x head_dim x 4 bytes < 2^31)
-  if (p->heads_q > 16384) return ATTN_ERR_SHAPE;
+  // tile loads address a 128-row tile with 32-bit byte offsets: 128 rows x
+  // heads x head_dim x element bytes must stay below 2^31
+  const int64_t esize = p->dtype == ATTN_F32 ? 4 : 2;
+  if (p->heads_q > 16384 || 128 * (int64_t)p->heads_q * p->head_dim * esize >= (int64_t(1) << 31))
+    return ATTN_ERR_SHAPE;
   // packed element counts must stay addressable
   if ((int64_t)p->total_q * p->heads_q > INT32_MAX || (int64_t)p->total_k * p->heads_kv > INT32_MAX)
     return ATTN_ERR_SHAPE;

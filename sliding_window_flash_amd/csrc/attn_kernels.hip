@@ -174,13 +174,17 @@ constexpr float kRescaleSlack = 8.0f;
 template <int NW>
 __device__ __forceinline__ void row_mask_words(const AttnArgs& a, int64_t t, bool ok, int kb,
                                                uint32_t (&mw)[NW]) {
-  static_assert(NW == 2, "64-key tiles");
-  if (ok) {
-    const uint2 v = *reinterpret_cast<const uint2*>(a.mask + t * a.mask_words + (int64_t)NW * kb);
-    mw[0] = v.x;
-    mw[1] = v.y;
+  static_assert(NW == 1 || NW == 2, "32- or 64-key tiles");
+  if constexpr (NW == 2) {
+    if (ok) {
+      const uint2 v = *reinterpret_cast<const uint2*>(a.mask + t * a.mask_words + (int64_t)NW * kb);
+      mw[0] = v.x;
+      mw[1] = v.y;
+    } else {
+      mw[0] = mw[1] = 0u;
+    }
   } else {
-    mw[0] = mw[1] = 0u;
+    mw[0] = ok ? a.mask[t * a.mask_words + kb] : 0u;
   }
 }
 
@@ -206,12 +210,17 @@ __device__ __forceinline__ void apply_col_mask(f32x16& s, const uint32_t (&words
   for (int r = 0; r < 16; ++r)
     if (!((words[r] >> bit) & 1u)) s[r] = -INFINITY;
 }
-// Both blocks of a 64-key tile; skipped when every lane's words are all ones
-// (a tile inside one document, say), which the wave decides as a whole.
-__device__ __forceinline__ void apply_row_mask2(f32x16 (&s)[2], const uint32_t (&mw)[2], int half) {
-  if (__all((mw[0] & mw[1]) == 0xFFFFFFFFu)) return;
-  apply_row_mask(s[0], mw[0], half);
-  apply_row_mask(s[1], mw[1], half);
+// Every block of a 32- or 64-key tile; skipped when every lane's words are
+// all ones (a tile inside one document, say), which the wave decides as a
+// whole.
+template <int NW>
+__device__ __forceinline__ void apply_row_masks(f32x16 (&s)[NW], const uint32_t (&mw)[NW], int half) {
+  uint32_t all = mw[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) all &= mw[i];
+  if (__all(all == 0xFFFFFFFFu)) return;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) apply_row_mask(s[i], mw[i], half);
 }
 
 template <int N> using ic = std::integral_constant<int, N>;
@@ -298,7 +307,7 @@ template <typename T> constexpr int waves_per_simd(int d) { return d > 128 || (s
 template <typename T, int D, int BM, int BN, bool M>
 __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(waves_per_simd<T>(D), waves_per_simd<T>(D))))
 fwd_kernel(AttnArgs a) {
-  static_assert(BN == 64, "mask words cover 64-key tiles");
+  static_assert(BN == 64 || (BN == 32 && D > 256), "64-key tiles (32 at head_dim 512)");
   constexpr int NT = BM * 2;
   constexpr bool kPipe = sizeof(T) == 2 && D <= 128;  // software-pipelined loop (see below)
   using KTile = LdsTile<T, BN, D>;
@@ -339,11 +348,20 @@ fwd_kernel(AttnArgs a) {
   const RowWindow rw = row_window(i + (it.lk - it.lq), it.lk, a.window, a.causal != 0);
   const uint32_t mpos = rw.mpos, mlim = rw.mlim;
 
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
-  float m = -INFINITY, lsum = 0.f;
   const float c = a.scale * kLog2e;
+  // O = acc / l (columns col0 ..), LSE = m + log2(l) in natural log
+  auto finish = [&](auto& acc_, float m_, float lsum_, int col0, bool with_lse) __attribute__((always_inline)) {
+    constexpr int DW = 32 * (int)(sizeof(acc_) / sizeof(acc_[0]));
+    const float ltot = sum_halves(lsum_);
+    if (row_ok) {
+      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+      T* orow = static_cast<T*>(a.out_o) + (int64_t)(it.q0 + i) * qstride + it.h * D + col0;
+      store_acc_rows<T, DW>(orow, acc_, inv, half);
+      if (with_lse && half == 0)
+        a.out_lse[(int64_t)it.h * a.total_q + it.q0 + i] =
+            ltot > 0.f ? (m_ + fast_log2(ltot)) * kLn2 : -INFINITY;
+    }
+  };
 
   TileLoader<T, BN, D, NT> kvld;
   kvld.init((uint32_t)(kstride * sizeof(T)), w, lane);
@@ -352,6 +370,10 @@ fwd_kernel(AttnArgs a) {
   // accumulators keep their registers across the loop (no copies)
   const int ntiles = kr.hi - kr.lo + 1;
   if constexpr (kPipe) {
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+    float m = -INFINITY, lsum = 0.f;
     // Software pipeline over key tiles: step j puts tile j+1's scores on the
     // MFMA unit while the VALU turns tile j's scores into probabilities, then
     // adds tile j's P V. K and V tiles rotate through their own two stages:
@@ -392,7 +414,7 @@ fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int kt = 0; kt < BN / 32; ++kt) apply_visible(cur[kt], (uint32_t)(vis >> (32 * kt)));
       }
-      if constexpr (M) apply_row_mask2(cur, mcur, half);
+      if constexpr (M) apply_row_masks(cur, mcur, half);
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < BN / 32; ++kt)
@@ -450,8 +472,19 @@ fwd_kernel(AttnArgs a) {
       }
       pstep(ic<0>{}, std::false_type{}, kb, sa, sb, ma, mb);
     }
+    finish(acc, m, lsum, 0, true);
   } else {
-  const int ntiles = kr.hi - kr.lo + 1;
+  // O columns per pass over the key tiles: all of them up to head_dim 256; at
+  // 512 four passes of 128 (the accumulator and the Q fragments together would
+  // exceed the registers of one wave), each recomputing S and the softmax
+  // statistics exactly as the others do
+  constexpr int DO = D > 256 ? 128 : D;
+#pragma unroll 1
+  for (int pass = 0; pass < D / DO; ++pass) {
+  f32x16 acc[DO / 32];
+#pragma unroll
+  for (int dt = 0; dt < DO / 32; ++dt) acc[dt] = f32x16{};
+  float m = -INFINITY, lsum = 0.f;
   if (ntiles > 0) {
     if (ntiles & 1) fill_kv(kvld, st1, K, V, kstride, kr.lo, it.lk);
     else fill_kv(kvld, st0, K, V, kstride, kr.lo, it.lk);
@@ -484,7 +517,7 @@ fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int kt = 0; kt < BN / 32; ++kt) apply_visible(s[kt], (uint32_t)(vis >> (32 * kt)));
     }
-    if constexpr (M) apply_row_mask2(s, mw, half);
+    if constexpr (M) apply_row_masks(s, mw, half);
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt)
@@ -498,7 +531,7 @@ fwd_kernel(AttnArgs a) {
       const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mnew);
       lsum *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+      for (int dt = 0; dt < DO / 32; ++dt) acc[dt] *= alpha;
       m = mnew;
     }
     const float mu = m == -INFINITY ? 0.f : m;
@@ -518,7 +551,7 @@ fwd_kernel(AttnArgs a) {
       const Frag<T> pf = acc_frag<T>(s[u >> 1], u & 1);
       if constexpr (sizeof(T) == 2) rs = frag_sum(pf, rs);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) mma(acc[dt], crd.read(vs, 16 * u, dt), pf);
+      for (int dt = 0; dt < DO / 32; ++dt) mma(acc[dt], crd.read(vs, 16 * u, pass * (DO / 32) + dt), pf);
     }
     lsum += rs;
     __syncthreads();
@@ -529,17 +562,8 @@ fwd_kernel(AttnArgs a) {
     step(ic<0>{}, kb);
     step(ic<1>{}, kb + 1);
   }
-
+  finish(acc, m, lsum, pass * DO, pass == 0);
   }
-
-  const float ltot = sum_halves(lsum);
-  if (row_ok) {
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    T* orow = static_cast<T*>(a.out_o) + (int64_t)(it.q0 + i) * qstride + it.h * D;
-    store_acc_rows<T, D>(orow, acc, inv, half);
-    if (half == 0)
-      a.out_lse[(int64_t)it.h * a.total_q + it.q0 + i] =
-          ltot > 0.f ? (m + fast_log2(ltot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -596,7 +620,12 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(AttnArgs a) {
 template <typename T, int D, int BM, int BN, bool M>
 __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(waves_per_simd<T>(D), waves_per_simd<T>(D))))
 bwd_dq_kernel(AttnArgs a) {
-  static_assert(BN == 64, "mask words cover 64-key tiles");
+  static_assert(BN == 64 || (BN == 32 && D > 256), "64-key tiles (32 at head_dim 512)");
+  // dQ columns accumulated per pass over the key tiles: all of them up to
+  // head_dim 256; at 512 four passes of 128 (the accumulator, Q and dO
+  // fragments together would exceed the registers of one wave), each
+  // recomputing S and dP
+  constexpr int DO = D > 256 ? 128 : D;
   constexpr int NT = BM * 2;
   using KTile = LdsTile<T, BN, D>;
   __shared__ __attribute__((aligned(1024))) char st0[2 * KTile::kBytes];
@@ -657,18 +686,20 @@ bwd_dq_kernel(AttnArgs a) {
   crd.init(lane);
   const RowWindow rw = row_window(i + (it.lk - it.lq), it.lk, a.window, a.causal != 0);
   const uint32_t mpos = rw.mpos, mlim = rw.mlim;
-  // cleared before the first visited key tile (kr.lo), not on key tile zero
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
   const float c = a.scale * kLog2e;
 
   TileLoader<T, BN, D, NT> kvld;
   kvld.init((uint32_t)(kstride * sizeof(T)), w, lane);
+  const int ntiles = kr.hi - kr.lo + 1;
+#pragma unroll 1
+  for (int pass = 0; pass < D / DO; ++pass) {
+  // cleared before the first visited key tile (kr.lo), not on key tile zero
+  f32x16 acc[DO / 32];
+#pragma unroll
+  for (int dt = 0; dt < DO / 32; ++dt) acc[dt] = f32x16{};
   // an odd number of tiles starts in stage 1, so that the loop below runs
   // whole (stage 0, stage 1) pairs: with no exit between the two steps the
   // accumulators keep their registers across the loop (no copies)
-  const int ntiles = kr.hi - kr.lo + 1;
   if (ntiles > 0) {
     if (ntiles & 1) fill_kv(kvld, st1, K, V, kstride, kr.lo, it.lk);
     else fill_kv(kvld, st0, K, V, kstride, kr.lo, it.lk);
@@ -712,7 +743,7 @@ bwd_dq_kernel(AttnArgs a) {
       for (int u = 0; u < 2; ++u) {
         const Frag<T> dsf = acc_frag<T>(s, u);
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) mma(acc[dt], crd.read(ks, 32 * kt + 16 * u, dt), dsf);
+        for (int dt = 0; dt < DO / 32; ++dt) mma(acc[dt], crd.read(ks, 32 * kt + 16 * u, pass * (DO / 32) + dt), dsf);
       }
     }
     __syncthreads();
@@ -724,8 +755,9 @@ bwd_dq_kernel(AttnArgs a) {
     step(ic<1>{}, kb + 1);
   }
   if (row_ok) {
-    T* row = static_cast<T*>(a.dq) + (int64_t)(it.q0 + i) * qstride + it.h * D;
-    store_acc_rows<T, D>(row, acc, a.scale, half);
+    T* row = static_cast<T*>(a.dq) + (int64_t)(it.q0 + i) * qstride + it.h * D + pass * DO;
+    store_acc_rows<T, DO>(row, acc, a.scale, half);
+  }
   }
 }
 
@@ -1021,7 +1053,12 @@ template <typename T, int D, int BN, int BM, bool M>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_dkdv_wide_kernel(AttnArgs a) {
   constexpr int NT = 256;
-  static_assert(D == 256 && BN == 128 && BM == 32, "wave layout assumes 4 key blocks of 32 keys, all dims per wave");
+  static_assert((D == 256 || D == 512) && BN == 128 && BM == 32,
+                "wave layout assumes 4 key blocks of 32 keys, all dims per wave");
+  // accumulator columns per pass: all 256 at head_dim 256; at 512 the dV and
+  // dK passes each run four times, over columns 0-127, ..., 384-511
+  constexpr int DA = D > 256 ? 128 : D;
+  constexpr int NH = D / DA;
   using QTile = LdsTile<T, BM, D>;
   constexpr int kStats = 64 * 4;  // one 64-lane 4-byte load's worth
   // with M, the step's mask tile follows: one 16-byte load per lane (rows past
@@ -1099,10 +1136,10 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
     }
     if (++nqb > qr.hi) {
       nqb = qr.lo;
-      if (++nh == g * grp + grp) nh = g * grp;  // the second pass starts over
+      if (++nh == g * grp + grp) nh = g * grp;  // the next pass starts over
     }
   };
-  const int total = 2 * steps;
+  const int total = 2 * NH * steps;
   // odd step counts start in stage 1: the loops below run whole stage pairs
   if (total > 0) fill(steps & 1 ? st1 : st0);
   __syncthreads();
@@ -1142,11 +1179,27 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
     __syncthreads();
   };
 
-  // pass 1: dV += P^T dO
-  {
-    f32x16 dva[D / 32];
+  // Steps t0 .. t0 + steps - 1 of one pass: global step t runs on stage
+  // (t + steps % 2) % 2 (the first fill went to stage steps % 2), so a pass
+  // may start with a lone stage-1 step and end with a lone stage-0 step, with
+  // whole stage pairs between
+  auto run = [&](auto step, int t0) __attribute__((always_inline)) {
+    int t = t0;
+    const int end = t0 + steps;
+    if (t < end && ((t + (steps & 1)) & 1)) step(ic<1>{}, t++);
+    for (; t + 1 < end; t += 2) {
+      step(ic<0>{}, t);
+      step(ic<1>{}, t + 1);
+    }
+    if (t < end) step(ic<0>{}, t);
+  };
+
+  // dV passes: dV += P^T dO, columns DA h .. DA h + DA - 1
+  auto dv_pass = [&](auto h_c) __attribute__((always_inline)) {
+    constexpr int h = decltype(h_c)::value;
+    f32x16 dva[DA / 32];
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) dva[dt] = f32x16{};
+    for (int dt = 0; dt < DA / 32; ++dt) dva[dt] = f32x16{};
     auto step = [&](auto stage_c, int t) {
       constexpr int stage = decltype(stage_c)::value;
       const char* qs = stage ? st1 : st0;
@@ -1158,26 +1211,21 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
         for (int u = 0; u < 2; ++u) {
           const Frag<T> pf = acc_frag<T>(s, u);
 #pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) mma(dva[dt], crd.read(dos, 16 * u, dt), pf);
+          for (int dt = 0; dt < DA / 32; ++dt) mma(dva[dt], crd.read(dos, 16 * u, h * (DA / 32) + dt), pf);
         }
       }
       next();
     };
-    int t = 0;
-    if (steps & 1) step(ic<1>{}, t++);
-    for (; t < steps; t += 2) {
-      step(ic<0>{}, t);
-      step(ic<1>{}, t + 1);
-    }
+    run(step, h * steps);
     if (key_ok)
-      store_acc_rows<T, D>(static_cast<T*>(a.dv) + (int64_t)(k0 + j) * kstride + g * D, dva, 1.f, half);
-  }
-  // pass 2: dK += dS^T Q, dS = P (dP - D); its first step was filled into
-  // stage 0 during pass 1's last step
-  {
-    f32x16 dka[D / 32];
+      store_acc_rows<T, DA>(static_cast<T*>(a.dv) + (int64_t)(k0 + j) * kstride + g * D + h * DA, dva, 1.f, half);
+  };
+  // dK passes: dK += dS^T Q with dS = P (dP - D), columns DA h .. DA h + DA - 1
+  auto dk_pass = [&](auto h_c) __attribute__((always_inline)) {
+    constexpr int h = decltype(h_c)::value;
+    f32x16 dka[DA / 32];
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) dka[dt] = f32x16{};
+    for (int dt = 0; dt < DA / 32; ++dt) dka[dt] = f32x16{};
     auto step = [&](auto stage_c, int t) {
       constexpr int stage = decltype(stage_c)::value;
       const char* qs = stage ? st1 : st0;
@@ -1199,21 +1247,27 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
         for (int u = 0; u < 2; ++u) {
           const Frag<T> dsf = acc_frag<T>(dp, u);
 #pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) mma(dka[dt], crd.read(qs, 16 * u, dt), dsf);
+          for (int dt = 0; dt < DA / 32; ++dt) mma(dka[dt], crd.read(qs, 16 * u, h * (DA / 32) + dt), dsf);
         }
       }
       next();
     };
-    // pass 1 always ends on stage 1 (an odd count starts on stage 1), so step
-    // `steps` sits in stage 0; an odd count ends this pass with a lone stage 0
-    int t = steps;
-    for (; t + 1 < total; t += 2) {
-      step(ic<0>{}, t);
-      step(ic<1>{}, t + 1);
-    }
-    if (t < total) step(ic<0>{}, t);
+    run(step, (NH + h) * steps);
     if (key_ok)
-      store_acc_rows<T, D>(static_cast<T*>(a.dk) + (int64_t)(k0 + j) * kstride + g * D, dka, a.scale, half);
+      store_acc_rows<T, DA>(static_cast<T*>(a.dk) + (int64_t)(k0 + j) * kstride + g * D + h * DA, dka, a.scale,
+                            half);
+  };
+  dv_pass(ic<0>{});
+  if constexpr (NH > 1) dv_pass(ic<1>{});
+  if constexpr (NH > 2) {
+    dv_pass(ic<2>{});
+    dv_pass(ic<3>{});
+  }
+  dk_pass(ic<0>{});
+  if constexpr (NH > 1) dk_pass(ic<1>{});
+  if constexpr (NH > 2) {
+    dk_pass(ic<2>{});
+    dk_pass(ic<3>{});
   }
 }
 
@@ -1390,7 +1444,7 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
 // time; at head_dim 256 it takes 128 keys (4 waves of 32 keys, two passes) and
 // steps over queries 32 at a time.
 template <int D> struct Tiles {
-  static constexpr int kFwdBM = 128, kFwdBN = 64;
+  static constexpr int kFwdBM = 128, kFwdBN = D > 256 ? 32 : 64;
   static constexpr int kBwdBN = 128, kBwdBM = D > 128 ? 32 : 64;
 };
 
@@ -1462,8 +1516,11 @@ static hipError_t launch_bwd_t(int stages, const AttnArgs& a, hipStream_t st) {
   return a.mask != nullptr ? launch_bwd_m<T, D, true>(stages, a, st) : launch_bwd_m<T, D, false>(stages, a, st);
 }
 
-// head_dim 256 exists for the 16-bit types only (the C ABI refuses fp32 there)
+// head_dim 256 and 512 exist for the 16-bit types only (the C ABI refuses
+// fp32 there)
 hipError_t launch_fwd(int dtype, int head_dim, const AttnArgs& a, hipStream_t st) {
+  if (dtype == 2 && head_dim == 512) return launch_fwd_t<fp16, 512>(a, st);
+  if (dtype == 1 && head_dim == 512) return launch_fwd_t<bf16, 512>(a, st);
   if (dtype == 2 && head_dim == 256) return launch_fwd_t<fp16, 256>(a, st);
   if (dtype == 2 && head_dim == 128) return launch_fwd_t<fp16, 128>(a, st);
   if (dtype == 2 && head_dim == 64) return launch_fwd_t<fp16, 64>(a, st);
@@ -1476,6 +1533,8 @@ hipError_t launch_fwd(int dtype, int head_dim, const AttnArgs& a, hipStream_t st
 }
 
 hipError_t launch_bwd(int dtype, int head_dim, int stages, const AttnArgs& a, hipStream_t st) {
+  if (dtype == 2 && head_dim == 512) return launch_bwd_t<fp16, 512>(stages, a, st);
+  if (dtype == 1 && head_dim == 512) return launch_bwd_t<bf16, 512>(stages, a, st);
   if (dtype == 2 && head_dim == 256) return launch_bwd_t<fp16, 256>(stages, a, st);
   if (dtype == 2 && head_dim == 128) return launch_bwd_t<fp16, 128>(stages, a, st);
   if (dtype == 2 && head_dim == 64) return launch_bwd_t<fp16, 64>(stages, a, st);
@@ -1545,6 +1604,7 @@ bool tile_sizes(int dtype, int head_dim, int* fwd_bm, int* fwd_bn, int* bwd_bn, 
   if (head_dim == 64) tiles_of<64>(fwd_bm, fwd_bn, bwd_bn, bwd_bm);
   else if (head_dim == 128) tiles_of<128>(fwd_bm, fwd_bn, bwd_bn, bwd_bm);
   else if (head_dim == 256 && dtype != 0) tiles_of<256>(fwd_bm, fwd_bn, bwd_bn, bwd_bm);
+  else if (head_dim == 512 && dtype != 0) tiles_of<512>(fwd_bm, fwd_bn, bwd_bn, bwd_bm);
   else return false;
   return true;
 }

@@ -180,29 +180,35 @@ __device__ __forceinline__ Frag<T> col_frag(const char* lds, int kbase, int nbas
 // swizzle depends only on row % 16, so for a row block starting at a multiple
 // of 16 rows every address is (block start x row bytes) + a per-lane offset:
 // with the block start and the LDS stage known at compile time, each read is
-// one register plus an immediate.
+// one register plus an immediate. In rows of 16 chunks or more the swizzle
+// changes only the low 4 bits of a chunk index, so the offsets repeat every
+// 16 chunks (256 bytes) apart: a reader keeps one period of them and adds the
+// rest as an immediate.
 template <typename T, int D>
 struct RowReader {
   using Tile = LdsTile<T, 16, D>;
   static constexpr int kSteps = D / 16;
   static constexpr int kParts = sizeof(T) == 2 ? 1 : 2;  // 16-byte chunks per fragment
-  int off[kSteps][kParts];
+  // steps per 16 chunks (a step advances 2 kParts chunks)
+  static constexpr int kPeriod = Tile::kChunks >= 16 && kSteps > 8 / kParts ? 8 / kParts : kSteps;
+  int off[kPeriod][kParts];
   __device__ __forceinline__ void init(int l32, int half) {
 #pragma unroll
-    for (int ss = 0; ss < kSteps; ++ss)
+    for (int ss = 0; ss < kPeriod; ++ss)
 #pragma unroll
       for (int q = 0; q < kParts; ++q) off[ss][q] = Tile::chunk_off(l32, kParts * (2 * ss + half) + q);
   }
   // same as row_frag(base, row16 + lane%32, 2*ss + half); row16 % 16 == 0
   __device__ __forceinline__ Frag<T> read(const char* base, int row16, int ss) const {
-    const char* p = base + row16 * Tile::kRowBytes;
+    const char* p = base + row16 * Tile::kRowBytes + (ss / kPeriod) * 256;
+    const int si = ss % kPeriod;
     Frag<T> f;
     if constexpr (sizeof(T) == 2) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(p + off[ss][0]);
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(p + off[si][0]);
       f.v = __builtin_bit_cast(decltype(f.v), raw);
     } else {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(p + off[ss][0]);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(p + off[ss][1]);
+      const f32x4 a = *reinterpret_cast<const f32x4*>(p + off[si][0]);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(p + off[si][1]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         f.v[j] = a[j];
@@ -218,11 +224,14 @@ struct ColReader {
   using Tile = LdsTile<T, 16, D>;
   static constexpr int kBlocks = D / 32;
   static constexpr int kParts = sizeof(T) == 2 ? 2 : 8;  // transposing reads / scalar reads
-  int off[kBlocks][kParts];
+  // 32-column blocks per 16 chunks (a block spans 32 * sizeof(T) / 16 chunks)
+  static constexpr int kPer16 = 16 / (2 * (int)sizeof(T));
+  static constexpr int kPeriod = Tile::kChunks >= 16 && kBlocks > kPer16 ? kPer16 : kBlocks;
+  int off[kPeriod][kParts];
   __device__ __forceinline__ void init(int lane) {
     const int half = lane >> 5;
 #pragma unroll
-    for (int dt = 0; dt < kBlocks; ++dt) {
+    for (int dt = 0; dt < kPeriod; ++dt) {
       if constexpr (sizeof(T) == 2) {
         const int r = lane & 15;
         const int col = 32 * dt + (lane & 16) + 4 * (r & 3);
@@ -238,19 +247,20 @@ struct ColReader {
   }
   // same as col_frag(base, kbase, 32*dt, lane); kbase % 16 == 0
   __device__ __forceinline__ Frag<T> read(const char* base, int kbase, int dt) const {
-    const char* p = base + kbase * Tile::kRowBytes;
+    const char* p = base + kbase * Tile::kRowBytes + (dt / kPeriod) * 256;
+    const int di = dt % kPeriod;
     Frag<T> f;
     if constexpr (sizeof(T) == 2) {
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(p + off[dt][0]));
+          (__attribute__((address_space(3))) i16x4*)(p + off[di][0]));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(p + off[dt][1]));
+          (__attribute__((address_space(3))) i16x4*)(p + off[di][1]));
       short s8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
       for (int j = 0; j < 8; ++j) f.v[j] = __builtin_bit_cast(T, s8[j]);
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) f.v[j] = *reinterpret_cast<const float*>(p + off[dt][j]);
+      for (int j = 0; j < 8; ++j) f.v[j] = *reinterpret_cast<const float*>(p + off[di][j]);
     }
     return f;
   }

@@ -106,10 +106,12 @@ def compare(name: str, got, ref, dtype: str, zero_ref: bool = False, scale_f32: 
 
 
 def full_reference(w: Workload, x: dict, window=None, mask=None) -> dict:
+    """The whole oracle output; each row panel takes the key band that can be
+    visible to it (the cells outside are masked and add exactly zero)."""
     window = w.window if window is None else window
     kw = {} if mask is None else dict(mask=mask)
     return dense.sdpa_reference(x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale,
-                                window, w.causal, **kw)
+                                window, w.causal, band=True, **kw)
 
 
 def compare_full(w: Workload, x: dict, got: dict, window=None, zero=(), mask=None, scale_f32=False) -> dict:

@@ -48,7 +48,13 @@ def good(**kw):
     (dict(window=0), 3),
     (dict(window=-5), 3),
     (dict(head_dim=96), 4),
-    (dict(head_dim=512), 4),
+    (dict(head_dim=512), 0),
+    (dict(head_dim=512, dtype=swa.ATTN_F16), 0),
+    (dict(head_dim=512, dtype=swa.ATTN_F32), 4),
+    (dict(head_dim=1024), 4),
+    # a 128-row tile of 16384 heads x 512 bf16 columns spans 2^31 bytes
+    (dict(heads_q=16384, heads_kv=16384, head_dim=512), 2),
+    (dict(heads_q=8192, heads_kv=8192, head_dim=512), 0),
     (dict(dtype=7), 4),
     (dict(causal=False, window=50), 0),     # two-sided window
     (dict(heads_q=1, heads_kv=1, total_q=2**30 + 8, total_k=2**30 + 8, max_seqlen_q=2**30 + 8,
@@ -123,8 +129,11 @@ def test_tile_sizes():
     assert bm % 32 == 0 and bn % 32 == 0 and kbn % 32 == 0 and kbm % 32 == 0
     assert swa.tile_sizes(128, swa.ATTN_F16) == (bm, bn, kbn, kbm)
     assert swa.tile_sizes(256, swa.ATTN_BF16)[2:] == (128, 32)
+    assert swa.tile_sizes(512, swa.ATTN_BF16) == (128, 32, 128, 32)
     with pytest.raises(swa.AttnError):
         swa.tile_sizes(256, swa.ATTN_F32)
+    with pytest.raises(swa.AttnError):
+        swa.tile_sizes(512, swa.ATTN_F32)
     with pytest.raises(swa.AttnError):
         swa.tile_sizes(96, swa.ATTN_BF16)
 

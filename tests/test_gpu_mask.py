@@ -34,6 +34,9 @@ CASES = [
     # groups split into head chunks (forward / dQ workgroups take 4 or 2 heads)
     ([170, 90], None, 16, 2, 128, 80, True, "bf16", 0.6, 2),
     ([140], [200], 6, 1, 64, 60, False, "f32", 0.7, 1),
+    # head_dim 512: 32-key forward / dQ tiles, one mask word per row and tile
+    ([150, 45], [160, 90], 4, 2, 512, 70, True, "bf16", 0.6, 2),
+    ([211], None, 2, 1, 512, 90, False, "fp16", 0.4, 1),
 ]
 
 
@@ -76,7 +79,7 @@ def _mask_grid(n, seed):
     windows = (1, 7, 33, 64, 100, 129, 300, INT32_MAX)
     while len(out) < n:
         dt = ("f32", "bf16", "fp16")[rng.integers(3)]
-        d = int(rng.choice([64, 128, 256] if dt != "f32" else [64, 128]))
+        d = int(rng.choice([64, 128, 256, 512] if dt != "f32" else [64, 128]))
         hkv = int(rng.choice([1, 2]))
         g = int(rng.choice([1, 2, 3, 4, 8]))
         lq = [int(x) for x in rng.integers(1, 300, int(rng.integers(1, 3)))]

@@ -69,6 +69,12 @@ SMALL = [
     ([300, 77], None, 3, 1, 256, 100, True, "bf16"),
     ([190, 64], None, 5, 5, 256, 33, False, "fp16"),
     ([200, 333], None, 4, 2, 128, 200, False, "f32"),
+    # head_dim 512: output-column passes in the forward, dQ and dK/dV
+    ([300, 1, 517, 64], None, 8, 2, 512, 129, True, "bf16"),
+    ([100, 40], [700, 300], 4, 2, 512, 16, True, "fp16"),
+    ([200, 333], None, 4, 2, 512, INT32_MAX, False, "bf16"),
+    ([257, 130], None, 4, 2, 512, 100, False, "fp16"),
+    ([300, 77], None, 3, 1, 512, 100, True, "bf16"),
 ]
 
 
@@ -80,7 +86,7 @@ def test_small_cases_full_oracle(case):
     _run_full(w)
 
 
-@pytest.mark.parametrize("dt,d", [("bf16", 128), ("fp16", 64), ("bf16", 256), ("f32", 64)])
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("fp16", 64), ("bf16", 256), ("f32", 64), ("fp16", 512)])
 def test_window_one_closed_form(dt, d):
     w = small_case([300, 130], [300, 200], heads_q=4, heads_kv=2, head_dim=d, window=1, dtype=dt,
                    do_scale=0.1, seed=31)
@@ -136,7 +142,7 @@ def test_backward_is_deterministic():
 
 
 @pytest.mark.parametrize("order", ["delta-dkdv-dq", "dq-dkdv"])
-@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64), ("fp16", 256)])
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64), ("fp16", 256), ("bf16", 512)])
 def test_stages_run_separately(dt, d, order):
     """attn_bwd_stages one stage at a time against the oracle, on a workspace
     poisoned with NaN: the D preprocess as its own launch with dK/dV before dQ,

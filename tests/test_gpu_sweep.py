@@ -20,14 +20,28 @@ RULE_MIN_WINDOW = 7
 # error of rounding one exact output to it (2^-9 bf16, 2^-12 fp16, 2^-25 fp32)
 HALF_ULP = {"bf16": 2.0 ** -9, "fp16": 2.0 ** -12, "f32": 2.0 ** -25}
 WINDOWS = (1, 2, 7, 31, 64, 100, 128, 129, 300, 1000, INT32_MAX)
+LONG_WINDOWS = (1000, 2000, 5000)
 
 
 def _grid(n=60, seed=2024):
+    """The record's grid: head dims 64 to 512, windows 1 to 5,000 (and none),
+    grouped-query ratios, queries shorter than keys, causal and not. One case
+    in ten is a single long sequence (1,500 to 6,000 tokens) under a window of
+    1,000 to 5,000, so that the long windows bite."""
     rng = np.random.default_rng(seed)
     cases = []
     while len(cases) < n:
         dt = DTYPES[rng.integers(3)]
-        d = int(rng.choice([64, 128, 256] if dt != "f32" else [64, 128]))
+        if rng.random() < 0.1:
+            d = int(rng.choice([64, 128]))
+            lq = [int(rng.integers(1500, 6000))]
+            lk = None
+            hkv, g = 1, int(rng.choice([1, 2, 4]))
+            causal = rng.random() < 0.7
+            window = int(LONG_WINDOWS[rng.integers(len(LONG_WINDOWS))])
+            cases.append((tuple(lq), lk, hkv * g, hkv, d, window, causal, dt))
+            continue
+        d = int(rng.choice([64, 128, 256, 512] if dt != "f32" else [64, 128]))
         hkv = int(rng.choice([1, 2]))
         g = int(rng.choice([1, 2, 3, 4, 5, 8]))   # odd groups: forward/dQ head chunks of 1, odd dK/dV step counts
         nseq = int(rng.integers(1, 4))
@@ -55,6 +69,7 @@ def _gpu():
 def test_grid_covers_its_corners():
     seen = {(c[7], c[4]) for c in CASES}
     assert {("f32", 64), ("bf16", 128), ("fp16", 256)} <= seen
+    assert any(c[4] == 512 for c in CASES) and any(c[5] == 5000 for c in CASES)
     assert any(c[5] == 1 for c in CASES) and any(not c[6] for c in CASES)
     assert any(c[1] is not None for c in CASES) and any(c[2] // c[3] == 4 for c in CASES)
 

@@ -83,7 +83,7 @@ def test_int32_max_window_does_not_overflow():
     assert (lo, hi) == (0, (40000 - 1) // 64)
 
 
-@pytest.mark.parametrize("head_dim", [128, 256])
+@pytest.mark.parametrize("head_dim", [128, 256, 512])
 def test_compiled_tiles_hit_both_silent_cases(head_dim):
     """With the tile sizes the kernels use, N=1024 / w=32 has query tiles whose
     first visited key tile is not tile zero, and L_q < L_k with a short window
