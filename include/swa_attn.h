@@ -76,10 +76,11 @@ typedef enum {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
-  ATTN_ERR_SHAPE = 2,       /* sizes inconsistent (batch < 1, heads_q % heads_kv, heads_q > 16384, totals,
-                               more than 2^31 - 1 work items: ceil(max_seqlen / 32) x heads x batch ...) */
+  ATTN_ERR_SHAPE = 2,       /* sizes inconsistent (batch < 1, heads_q % heads_kv, heads_q > 16384 or
+                               128 x heads_q x head_dim x element bytes >= 2^31, totals, more than
+                               2^31 - 1 work items: ceil(max_seqlen / 32) x heads x batch ...) */
   ATTN_ERR_WINDOW = 3,      /* window < 1 */
-  ATTN_ERR_UNSUPPORTED = 4, /* head_dim not 64/128 (256: 16-bit dtypes only), unknown dtype, scale <= 0,
+  ATTN_ERR_UNSUPPORTED = 4, /* head_dim not 64/128 (256, 512: 16-bit dtypes only), unknown dtype, scale <= 0,
                                a two-sided window with max_seqlen_k > 2^30 */
   ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than attn_bwd_workspace_bytes */
   ATTN_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
@@ -91,7 +92,7 @@ typedef struct {
   int32_t batch;        /* B >= 1 packed sequences */
   int32_t heads_q;      /* query heads, a multiple of heads_kv */
   int32_t heads_kv;     /* key/value heads; G = heads_q / heads_kv queries share one */
-  int32_t head_dim;     /* 64 or 128; 256 for bf16 and fp16 */
+  int32_t head_dim;     /* 64 or 128; 256 and 512 for bf16 and fp16 */
   int32_t total_q;      /* cu_seqlens_q[B] */
   int32_t total_k;      /* cu_seqlens_k[B] */
   int32_t max_seqlen_q; /* >= every L_q; sizes the launch grid (no device reads) */
