@@ -270,34 +270,34 @@ def main() -> int:
     pairs = in_window_pairs(w)
     flops_counted = 14 * d * pairs
     value = flops_counted / (ms_per_step * 1e-3) / 1e12
-    # algorithmic work of each launch (per visible pair: fwd 2 contractions,
-    # dQ 3 (S, dP recomputed, dS K; its D = rowsum(dO * O) per row adds no
-    # contraction), dK/dV 4 (S, dP, P^T dO, dS^T Q))
-    algo = {
-        "fwd": ("mfma", 4 * d * pairs),
-        "bwd_dq": ("mfma", 6 * d * pairs),
-        "bwd_dkdv": ("mfma", 8 * d * pairs),
-    }
+    # Work of each launch per visible (query, key) pair, in head_dim units d:
+    # counted = the metric's in-window FLOPs (forward Q K^T and P V: 4d;
+    # backward 10d, of which dQ's launch does dS K: 2d, and dK/dV's launch
+    # Q K^T, dO V^T, P^T dO, dS^T Q: 8d); executed = what the launch runs
+    # (dQ also recomputes S and dP: 6d). D = rowsum(dO * O), formed in dQ's
+    # prologue, adds no contraction.
+    algo = {"fwd": (4, 4), "bwd_dq": (2, 6), "bwd_dkdv": (8, 8)}
     kernels = {}
     for n in names:
-        bound, work = algo[n]
+        counted, executed = algo[n]
         sec = kern_ms[n] * 1e-3
-        if bound == "mfma":
-            ach, peak, unit = work / sec / 1e12, BF16_DENSE_PEAK_TFLOPS, "TFLOP/s"
-        else:
-            ach, peak, unit = work / sec / 1e9, HBM_PEAK_GBS, "GB/s"
-        kernels[n] = {"ms": round(kern_ms[n], 4), "bound": bound, "achieved": round(ach, 2),
-                      "peak": peak, "unit": unit, "frac": round(ach / peak, 4)}
+        ach = counted * d * pairs / sec / 1e12
+        ach_x = executed * d * pairs / sec / 1e12
+        kernels[n] = {"ms": round(kern_ms[n], 4), "bound": "mfma", "achieved": round(ach, 2),
+                      "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(ach / BF16_DENSE_PEAK_TFLOPS, 4),
+                      "flop_per_pair_counted": counted * d, "flop_per_pair_executed": executed * d,
+                      "achieved_executed": round(ach_x, 2),
+                      "frac_executed": round(ach_x / BF16_DENSE_PEAK_TFLOPS, 4)}
     dom = max(("fwd", "bwd_dq", "bwd_dkdv"), key=lambda n: kern_ms[n])
     traffic = load_traffic(dom)
-    roofline = dict(kernels[dom])
-    roofline.pop("ms")
+    roofline = {k: v for k, v in kernels[dom].items() if k in ("bound", "achieved", "peak", "unit", "frac")}
     roofline["kernel"] = dom
     roofline["traffic"] = traffic
 
     # synthetic device inputs of a workload (N(0,1); dO scaled like the workloads)
-    def device_inputs(wl):
-        g = torch.Generator(device=dev).manual_seed(0)
+    def device_inputs(wl, seed=0):
+        g = torch.Generator(device=dev).manual_seed(seed)
         t = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
         dh = wl.head_dim
         qq = torch.randn((wl.total_q, wl.heads_q, dh), generator=g, device=dev).to(t)
@@ -391,15 +391,22 @@ def main() -> int:
         for name in ("bf16_n2048_w1024_32q8kv_d128", "bf16_n8192_causal_32q8kv_d128",
                      "bf16_varlen4_w1024_32q8kv_d128"):
             cw = W.WORKLOADS[name]
-            (qq, kk, vv, dd, cq, ck), ckw = device_inputs(cw)
-            oo = torch.empty_like(qq)
-            ll = torch.empty((cw.heads_q, cw.total_q), dtype=torch.float32, device=dev)
-            dq4, dk4, dv4 = torch.empty_like(qq), torch.empty_like(kk), torch.empty_like(vv)
-            ws4 = torch.empty(swa.workspace_bytes(swa.params_for(qq, kk, cq, ck, **ckw)), dtype=torch.uint8,
-                              device=dev)
+            # two input and output sets, used in turn: the 2K and 8K workloads
+            # (40 and 160 MB) would otherwise stay in the 256 MB last-level
+            # cache from one step to the next
+            sets = []
+            for seed in (0, 1):
+                (qq, kk, vv, dd, cq, ck), ckw = device_inputs(cw, seed)
+                oo = torch.empty_like(qq)
+                ll = torch.empty((cw.heads_q, cw.total_q), dtype=torch.float32, device=dev)
+                dq4, dk4, dv4 = torch.empty_like(qq), torch.empty_like(kk), torch.empty_like(vv)
+                ws4 = torch.empty(swa.workspace_bytes(swa.params_for(qq, kk, cq, ck, **ckw)), dtype=torch.uint8,
+                                  device=dev)
+                sets.append((qq, kk, vv, dd, cq, ck, oo, ll, dq4, dk4, dv4, ws4))
             ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.config_steps)]
 
-            def cstep(e=None):
+            def cstep(n, e=None):
+                qq, kk, vv, dd, cq, ck, oo, ll, dq4, dk4, dv4, ws4 = sets[n % 2]
                 if e is not None:
                     e[0].record(stream)
                 swa.fwd(qq, kk, vv, cq, ck, out=oo, lse=ll, **ckw)
@@ -409,11 +416,11 @@ def main() -> int:
                 if e is not None:
                     e[2].record(stream)
 
-            for _ in range(3):
-                cstep()
+            for n in range(4):
+                cstep(n)
             torch.cuda.synchronize()
-            for e in ev:
-                cstep(e)
+            for n, e in enumerate(ev):
+                cstep(n, e)
             torch.cuda.synchronize()
             f_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
             b_ms = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
@@ -424,44 +431,74 @@ def main() -> int:
                 "fwd_tflops": round(4 * d_ * cp / (f_ms * 1e-3) / 1e12, 2),
                 "bwd_tflops": round(10 * d_ * cp / (b_ms * 1e-3) / 1e12, 2),
                 "tflops": round(14 * d_ * cp / ((f_ms + b_ms) * 1e-3) / 1e12, 2),
-                "in_window_pairs": cp, "steps": args.config_steps}
+                "in_window_pairs": cp, "steps": args.config_steps, "input_sets": 2}
             if name == "bf16_n8192_causal_32q8kv_d128":
                 configs[name]["pages_m1_max_s"] = {"fwd": 0.186, "bwd": 0.576}
-            del qq, kk, vv, dd, oo, ll, dq4, dk4, dv4, ws4
+            del sets
 
     # The workload with an arbitrary mask combined with the window: its tokens
     # packed from corpus-like documents (block-diagonal mask, bit-packed rows).
     # Counted FLOPs are 14d per cell that both the window and the mask show.
     masked = None
     if not args.no_masked and w.batch == 1 and w.causal and w.lengths_q == w.lengths_k:
-        docs = W.document_lengths(91, w.lengths_k[0])
-        mt = torch.from_numpy(W.document_mask_bits(w, [docs]).view(np.int32)).to(dev)
-
-        def mstep():
-            swa.fwd(q, k, v, cu_q, cu_k, out=o2, lse=l2, mask=mt, **kw)
-            swa.bwd(q, k, v, o2, l2, do, cu_q, cu_k, dq=dq3, dk=dk3, dv=dv3, workspace=ws3, mask=mt, **kw)
-
         o2, l2 = torch.empty_like(q), torch.empty((w.heads_q, w.total_q), dtype=torch.float32, device=dev)
         dq3, dk3, dv3 = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         ws3 = torch.empty(swa.workspace_bytes(p), dtype=torch.uint8, device=dev)
-        for _ in range(3):
-            mstep()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.masked_steps):
-            mstep()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        m_ms = e0.elapsed_time(e1) / args.masked_steps
-        m_pairs = document_pairs(w, docs)
-        m_tf = 14 * d * m_pairs / (m_ms * 1e-3) / 1e12
-        masked = {"workload": w.name + " packed from documents", "documents": docs,
-                  "mask_bytes": int(mt.numel() * 4), "ms_per_step": round(m_ms, 4),
-                  "steps": args.masked_steps, "visible_pairs": m_pairs, "tflops": round(m_tf, 2),
-                  "pct_bf16_peak": round(100 * m_tf / BF16_DENSE_PEAK_TFLOPS, 2),
-                  "time_vs_unmasked": round(m_ms / ms_per_step, 3)}
-        del mt, o2, l2, dq3, dk3, dv3, ws3
+
+        def time_masked(mt, rng=None):
+            def mstep():
+                swa.fwd(q, k, v, cu_q, cu_k, out=o2, lse=l2, mask=mt, mask_ranges=rng, **kw)
+                swa.bwd(q, k, v, o2, l2, do, cu_q, cu_k, dq=dq3, dk=dk3, dv=dv3, workspace=ws3, mask=mt,
+                        mask_ranges=rng, **kw)
+            for _ in range(3):
+                mstep()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(args.masked_steps):
+                mstep()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.masked_steps
+
+        def leg(name, docs):
+            """One document-packed workload, timed without and with the mask's
+            ranges (attn_mask_ranges, computed once beside the timed region
+            and also timed alone). Counted FLOPs are 14d per cell that both the
+            window and the mask show."""
+            mt = torch.from_numpy(W.document_mask_bits(w, [docs]).view(np.int32)).to(dev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            rng = swa.mask_ranges(q, k, cu_q, cu_k, mt, **kw)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            rng = swa.mask_ranges(q, k, cu_q, cu_k, mt, out=rng, **kw)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            r_ms = e0.elapsed_time(e1)
+            plain_ms = time_masked(mt)
+            skip_ms = time_masked(mt, rng)
+            m_pairs = document_pairs(w, docs)
+            m_tf = 14 * d * m_pairs / (skip_ms * 1e-3) / 1e12
+            out = {"workload": w.name + " " + name, "documents": len(docs), "longest_document": max(docs),
+                   "mask_bytes": int(mt.numel() * 4), "ms_per_step": round(skip_ms, 4),
+                   "ms_per_step_without_ranges": round(plain_ms, 4), "mask_ranges_ms": round(r_ms, 4),
+                   "steps": args.masked_steps, "visible_pairs": m_pairs,
+                   "visible_over_window_pairs": round(m_pairs / pairs, 4), "tflops": round(m_tf, 2),
+                   "pct_bf16_peak": round(100 * m_tf / BF16_DENSE_PEAK_TFLOPS, 2),
+                   "time_vs_unmasked": round(skip_ms / ms_per_step, 3),
+                   "time_vs_unmasked_without_ranges": round(plain_ms / ms_per_step, 3)}
+            del mt, rng
+            return out
+
+        docs = W.document_lengths(91, w.lengths_k[0])
+        masked = leg("packed from documents", docs)
+        masked["document_lengths"] = docs
+        # documents of at most 512 tokens under the 1,024-token window: most
+        # of each query tile's window belongs to other documents
+        masked_short = leg("packed from documents of at most 512 tokens",
+                           W.short_document_lengths(92, w.lengths_k[0], 512))
+        masked["short_documents"] = masked_short
+        del o2, l2, dq3, dk3, dv3, ws3
 
     # The second workload: the linear cross-entropy without the logits tensor
     # at the mlx-train-perf README's loss-layer shape. Forward 2 n V D FLOPs

@@ -199,7 +199,32 @@ attn_status_t attn_bwd_stages(const attn_params_t* p, int32_t stages, const void
 typedef struct {
   const uint32_t* bits; /* device, [total_q, row_words], 16-byte aligned */
   int64_t row_words;    /* a multiple of 4, >= ceil(max_seqlen_k / 32), < 2^24 */
+  const int32_t* ranges; /* optional (NULL: none): device, what attn_mask_ranges wrote for this
+                            mask, these cu_seqlens and these parameters; 4-byte aligned */
 } attn_mask_t;
+
+/* Bytes of the `ranges` buffer attn_mask_ranges fills for these parameters:
+ * 2 x batch x (ceil(max_seqlen_q / 32) + ceil(max_seqlen_k / 32)) int32. 0 if
+ * the parameters are invalid. */
+size_t attn_mask_ranges_bytes(const attn_params_t* p);
+
+/* Where the mask's allowed bits lie, so that the masked calls skip the tiles
+ * the mask empties (the lab's list of what is not proved: a window combined
+ * with an arbitrary mask still falls back to the full score matrix; here the
+ * window's tiles are visited as without a mask, and with these ranges only
+ * those that hold an allowed bit). For each sequence and 32-row block of its
+ * queries, the first and last 32-key block in which some row of the block
+ * allows a key the window can show it; for each 32-key block, the first and
+ * last 32-row block in which some row the window lets see it allows one of
+ * its keys ((1, 0) when none). One launch on `stream`, reading the mask words
+ * inside the window's band only. The kernels narrow each query tile's key
+ * range and each key tile's query range to these; a tile outside them has
+ * every cell masked and would add nothing, so outputs are the same as without
+ * ranges. Compute once per mask and reuse it across calls (layers) that share
+ * the mask and the parameters. Same checks as attn_fwd_masked, plus
+ * ATTN_ERR_NULL / ATTN_ERR_ALIGN for `ranges`. */
+attn_status_t attn_mask_ranges(const attn_params_t* p, const attn_mask_t* mask, const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k, int32_t* ranges, void* stream);
 
 /* attn_fwd with a mask. Same outputs and errors as attn_fwd; also
  * ATTN_ERR_NULL if `mask` or (total_q > 0) `mask->bits` is NULL, ATTN_ERR_ALIGN

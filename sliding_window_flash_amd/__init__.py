@@ -30,6 +30,7 @@ BWD_DELTA, BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 4, 7
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_stages", "attn_bwd_workspace_bytes", "attn_status_str",
             "attn_check_params", "attn_tile_sizes", "attn_query_tile_range",
             "attn_key_tile_range", "attn_fwd_masked", "attn_bwd_masked", "attn_bwd_noalloc",
+            "attn_mask_ranges_bytes", "attn_mask_ranges",
             "ce_check_params", "ce_fwd_workspace_bytes", "ce_fwd", "ce_bwd_workspace_bytes", "ce_bwd")
 
 
@@ -56,8 +57,9 @@ class CEParams(ctypes.Structure):
 
 
 class AttnMask(ctypes.Structure):
-    """attn_mask_t: bit-packed rows of a boolean mask combined with the window."""
-    _fields_ = [("bits", ctypes.c_void_p), ("row_words", ctypes.c_int64)]
+    """attn_mask_t: bit-packed rows of a boolean mask combined with the window,
+    and optionally the ranges attn_mask_ranges wrote for it."""
+    _fields_ = [("bits", ctypes.c_void_p), ("row_words", ctypes.c_int64), ("ranges", ctypes.c_void_p)]
 
 
 _LIB = None
@@ -90,6 +92,10 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_masked.argtypes = [P, M, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       ctypes.c_size_t, vp]
         L.attn_bwd_masked.restype = ctypes.c_int
+        L.attn_mask_ranges_bytes.argtypes = [P]
+        L.attn_mask_ranges_bytes.restype = ctypes.c_size_t
+        L.attn_mask_ranges.argtypes = [P, M, vp, vp, vp, vp]
+        L.attn_mask_ranges.restype = ctypes.c_int
         C = ctypes.POINTER(CEParams)
         L.ce_check_params.argtypes = [C]
         L.ce_check_params.restype = ctypes.c_int
@@ -259,20 +265,57 @@ def _check_attn(q, k, v, cu_q, cu_k, *, o=None, lse=None, do=None, dq=None, dk=N
                 raise ValueError(f"{n} is on {t.device}, q on {q.device}")
 
 
-def _mask_arg(mask):
+def _mask_arg(mask, ranges=None):
     """attn_mask_t for a device tensor of packed rows ([T_q, row_words], 32-bit
-    words; bit j % 32 of word j // 32 allows key j of the row's sequence)."""
-    return AttnMask(mask.data_ptr(), mask.shape[1])
+    words; bit j % 32 of word j // 32 allows key j of the row's sequence) and
+    optional ranges from :func:`mask_ranges`."""
+    return AttnMask(mask.data_ptr(), mask.shape[1], _ptr(ranges))
+
+
+def _check_ranges(ranges, p, mask, q):
+    torch = _torch()
+    if ranges is None:
+        return
+    if mask is None:
+        raise ValueError("mask_ranges given without a mask")
+    n = int(lib().attn_mask_ranges_bytes(ctypes.byref(p))) // 4
+    _expect(ranges, "mask_ranges", (n,), torch.int32)
+    _require(ranges, "mask_ranges")
+    if ranges.device != q.device:
+        raise ValueError(f"mask_ranges is on {ranges.device}, q on {q.device}")
+
+
+def mask_ranges(q, k, cu_q, cu_k, mask, *, max_seqlen_q, max_seqlen_k, window=INT32_MAX, causal=True,
+                scale=None, out=None, stream=None):
+    """attn_mask_ranges: where the mask's allowed bits lie (int32 device
+    tensor), for fwd/bwd's ``mask_ranges``; q and k give the shapes."""
+    torch = _torch()
+    _check_attn(q, k, k, cu_q, cu_k, mask=mask)
+    p = params_for(q, k, cu_q, cu_k, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
+                   window=window, causal=causal, scale=scale)
+    n = int(lib().attn_mask_ranges_bytes(ctypes.byref(p))) // 4
+    out = torch.empty(max(n, 1), dtype=torch.int32, device=q.device) if out is None else out
+    if out.numel() < n or out.dtype != torch.int32:
+        raise ValueError(f"mask_ranges out must be int32 with {n} elements")
+    m = _mask_arg(mask)
+    st = lib().attn_mask_ranges(ctypes.byref(p), ctypes.byref(m), _ptr(cu_q), _ptr(cu_k), _ptr(out),
+                                _stream_ptr(stream))
+    if st:
+        raise AttnError(st, "attn_mask_ranges")
+    return out[:n]
 
 
 def fwd(q, k, v, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=INT32_MAX, causal=True,
-        scale=None, out=None, lse=None, stream=None, mask=None):
+        scale=None, out=None, lse=None, stream=None, mask=None, mask_ranges=None):
     """O [T_q, Hq, d] (q.dtype) and LSE [Hq, T_q] (fp32) through attn_fwd, or
-    attn_fwd_masked when ``mask`` (packed rows, see :func:`_mask_arg`) is given."""
+    attn_fwd_masked when ``mask`` (packed rows, see :func:`_mask_arg`) is given
+    (with ``mask_ranges`` from :func:`mask_ranges`: tiles the mask empties are
+    skipped)."""
     torch = _torch()
     _check_attn(q, k, v, cu_q, cu_k, o=out, lse=lse, mask=mask)
     p = params_for(q, k, cu_q, cu_k, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
                    window=window, causal=causal, scale=scale)
+    _check_ranges(mask_ranges, p, mask, q)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -281,7 +324,7 @@ def fwd(q, k, v, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=INT32_MAX, ca
     if mask is None:
         st, what = lib().attn_fwd(ctypes.byref(p), *args), "attn_fwd"
     else:
-        m = _mask_arg(mask)
+        m = _mask_arg(mask, mask_ranges)
         st, what = lib().attn_fwd_masked(ctypes.byref(p), ctypes.byref(m), *args), "attn_fwd_masked"
     if st:
         raise AttnError(st, what)
@@ -290,10 +333,11 @@ def fwd(q, k, v, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=INT32_MAX, ca
 
 def bwd(q, k, v, o, lse, do, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=INT32_MAX,
         causal=True, scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None,
-        stages=BWD_ALL, mask=None):
+        stages=BWD_ALL, mask=None, mask_ranges=None):
     """dQ, dK, dV through attn_bwd_stages (the VJP of sum(O * dO)); ``stages``
     selects a subset of the backward's launches (all three by default). With
-    ``mask`` (the forward's), through attn_bwd_masked (all stages)."""
+    ``mask`` (the forward's), through attn_bwd_masked (all stages), and with
+    ``mask_ranges`` skipping the tiles the mask empties."""
     torch = _torch()
     _check_attn(q, k, v, cu_q, cu_k, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv, mask=mask, devices=False)
     p = params_for(q, k, cu_q, cu_k, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
@@ -301,6 +345,7 @@ def bwd(q, k, v, o, lse, do, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=I
     nbytes = workspace_bytes(p)
     _check_attn(q, k, v, cu_q, cu_k, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv, mask=mask,
                 workspace=workspace, need_ws=nbytes)
+    _check_ranges(mask_ranges, p, mask, q)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -314,7 +359,7 @@ def bwd(q, k, v, o, lse, do, cu_q, cu_k, *, max_seqlen_q, max_seqlen_k, window=I
     else:
         if stages != BWD_ALL:
             raise ValueError("the masked backward runs all stages")
-        m = _mask_arg(mask)
+        m = _mask_arg(mask, mask_ranges)
         st, what = lib().attn_bwd_masked(ctypes.byref(p), ctypes.byref(m), *args), "attn_bwd_masked"
     if st:
         raise AttnError(st, what)

@@ -97,7 +97,12 @@ static attn_status_t check_mask(const attn_params_t* p, const attn_mask_t* m) {
   // a 64-row mask tile is addressed with 32-bit byte offsets: 64 rows x
   // row_words x 4 bytes must stay below 2^32
   if (m->row_words >= (1 << 24)) return ATTN_ERR_UNSUPPORTED;
+  if (m->ranges != nullptr && !aligned4(m->ranges)) return ATTN_ERR_ALIGN;
   return check_tensor(m->bits, (int64_t)p->total_q * m->row_words, true);
+}
+
+static size_t ranges_entries(const attn_params_t* p) {
+  return 2 * (size_t)p->batch * (size_t)(((int64_t)p->max_seqlen_q + 31) / 32 + ((int64_t)p->max_seqlen_k + 31) / 32);
 }
 
 static attn_status_t fwd_impl(const attn_params_t* p, const attn_mask_t* mask, const void* q,
@@ -125,6 +130,7 @@ static attn_status_t fwd_impl(const attn_params_t* p, const attn_mask_t* mask, c
   if (mask != nullptr) {
     a.mask = mask->bits;
     a.mask_words = mask->row_words;
+    a.mask_ranges = mask->ranges;
   }
   if (swa::launch_fwd(p->dtype, p->head_dim, a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return ATTN_ERR_HIP;
@@ -135,6 +141,28 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o,
                        float* lse, void* stream) {
   return fwd_impl(p, nullptr, q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, stream);
+}
+
+size_t attn_mask_ranges_bytes(const attn_params_t* p) {
+  if (attn_check_params(p) != ATTN_OK) return 0;
+  return ranges_entries(p) * sizeof(int32_t);
+}
+
+attn_status_t attn_mask_ranges(const attn_params_t* p, const attn_mask_t* mask, const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k, int32_t* ranges, void* stream) {
+  attn_status_t s = attn_check_params(p);
+  if (s != ATTN_OK) return s;
+  if ((s = check_mask(p, mask)) != ATTN_OK) return s;
+  if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return ATTN_ERR_NULL;
+  if (!aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k)) return ATTN_ERR_ALIGN;
+  if ((s = check_tensor(ranges, (int64_t)ranges_entries(p), false)) != ATTN_OK) return s;
+  swa::AttnArgs a = base_args(p);
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.mask = mask->bits;
+  a.mask_words = mask->row_words;
+  if (swa::launch_mask_ranges(a, ranges, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
 }
 
 attn_status_t attn_fwd_masked(const attn_params_t* p, const attn_mask_t* mask, const void* q,
@@ -233,6 +261,7 @@ static attn_status_t bwd_impl(const attn_params_t* p, const attn_mask_t* mask, i
   if (mask != nullptr) {
     a.mask = mask->bits;
     a.mask_words = mask->row_words;
+    a.mask_ranges = mask->ranges;
   }
   if (swa::launch_bwd(p->dtype, p->head_dim, stages, a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return ATTN_ERR_HIP;

@@ -223,6 +223,87 @@ __device__ __forceinline__ void apply_row_masks(f32x16 (&s)[NW], const uint32_t 
   for (int i = 0; i < NW; ++i) apply_row_mask(s[i], mw[i], half);
 }
 
+// ------------------------------------------- ranges of the mask's allowed bits
+// For each sequence and each 32-row block of its queries: the first and last
+// 32-key block (mask word) in which some row of the block has an allowed bit
+// among the keys the window can show that block (row ranges); for each
+// 32-key block of its keys: the first and last 32-row block with such a bit
+// among the rows the window lets see that block (column ranges). Empty ranges
+// are (1, 0). The kernels intersect their tile ranges with these, so tiles
+// at a range's ends that the mask empties are never visited; a tile whose
+// cells are all masked contributes nothing, so the results are unchanged.
+// Words are tested whole: bits of a word the window partly hides still count,
+// which can only widen a range. One wave per block: the first `nrb_total`
+// waves take row blocks, the rest key blocks.
+__global__ void __launch_bounds__(64) mask_range_kernel(AttnArgs a, int32_t* ranges, int nrb, int nkb32) {
+  const int lane = threadIdx.x;
+  const int64_t nrows = (int64_t)a.batch * nrb;
+  int64_t id = blockIdx.x;
+  const bool rows = id < nrows;
+  if (!rows) id -= nrows;
+  const int per = rows ? nrb : nkb32;
+  const int b = (int)(id / per), blk = (int)(id % per);
+  const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
+  const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
+  const SeqGeom sg{lq, lk, a.window, a.causal != 0};
+  int first = INT32_MAX, last = -1;
+  if (rows) {
+    // keys the window shows rows [32 blk, 32 blk + 31]
+    const TileRange kr = query_tile_keys(sg, blk, 32, 32);
+    const int i = 32 * blk + (lane & 31);
+    if (i < lq)
+      for (int w = kr.lo + (lane >> 5); w <= kr.hi; w += 2)
+        if (a.mask[(int64_t)(q0 + i) * a.mask_words + w] != 0u) {
+          first = min(first, w);
+          last = max(last, w);
+        }
+  } else {
+    // rows the window lets see keys [32 blk, 32 blk + 31]
+    const TileRange qr = key_tile_queries(sg, blk, 32, 1);
+    for (int i = qr.lo + lane; i <= qr.hi; i += 64)
+      if (a.mask[(int64_t)(q0 + i) * a.mask_words + blk] != 0u) {
+        first = min(first, i >> 5);
+        last = max(last, i >> 5);
+      }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    first = min(first, __shfl_xor(first, off, 64));
+    last = max(last, __shfl_xor(last, off, 64));
+  }
+  if (lane == 0) {
+    int32_t* r = ranges + 2 * ((rows ? 0 : nrows) + id);
+    r[0] = last >= 0 ? first : 1;
+    r[1] = last >= 0 ? last : 0;
+  }
+}
+
+// The union of the ranges of blocks [blk0, blk0 + nblk) (row or key blocks of
+// sequence b, `row` picks which table), in units of `unit` 32-blocks,
+// intersected with [lo, hi]. Returns an empty range (lo > hi) when no block
+// has an allowed bit.
+__device__ __forceinline__ void narrow_by_mask(const AttnArgs& a, bool row, int b, int blk0, int nblk, int unit,
+                                               int32_t& lo, int32_t& hi) {
+  const int nrb = (a.max_seqlen_q + 31) / 32, nkb32 = (a.max_seqlen_k + 31) / 32;
+  const int per = row ? nrb : nkb32;
+  const int32_t* r = a.mask_ranges + 2 * ((row ? 0 : (int64_t)a.batch * nrb) + (int64_t)b * per);
+  int first = INT32_MAX, last = -1;
+  for (int k = blk0; k < blk0 + nblk && k < per; ++k) {
+    const int f = r[2 * k], l = r[2 * k + 1];
+    if (f <= l) {
+      first = min(first, f);
+      last = max(last, l);
+    }
+  }
+  if (last < 0) {
+    lo = 0;
+    hi = -1;
+    return;
+  }
+  lo = max(lo, first / unit);
+  hi = min(hi, last / unit);
+}
+
 template <int N> using ic = std::integral_constant<int, N>;
 
 // Per-query visibility as one unsigned range test with a wave-uniform limit:
@@ -322,7 +403,11 @@ fwd_kernel(AttnArgs a) {
   if (it.qb * it.rows >= it.lq) return;
   const int g = it.g;
   const SeqGeom sg{it.lq, it.lk, a.window, a.causal != 0};
-  const TileRange kr = query_tile_keys(sg, it.qb, it.rows, BN);
+  TileRange kr = query_tile_keys(sg, it.qb, it.rows, BN);
+  // with the mask's ranges: only key tiles in which some row of the tile has
+  // an allowed bit
+  if constexpr (M)
+    if (a.mask_ranges != nullptr) narrow_by_mask(a, true, it.b, it.qb * it.rows / 32, it.rows / 32, BN / 32, kr.lo, kr.hi);
 
   const int64_t qstride = (int64_t)a.heads_q * D;
   const int64_t kstride = (int64_t)a.heads_kv * D;
@@ -637,7 +722,11 @@ bwd_dq_kernel(AttnArgs a) {
   if (it.qb * it.rows >= it.lq) return;
   const int g = it.g;
   const SeqGeom sg{it.lq, it.lk, a.window, a.causal != 0};
-  const TileRange kr = query_tile_keys(sg, it.qb, it.rows, BN);
+  TileRange kr = query_tile_keys(sg, it.qb, it.rows, BN);
+  // with the mask's ranges: only key tiles in which some row of the tile has
+  // an allowed bit
+  if constexpr (M)
+    if (a.mask_ranges != nullptr) narrow_by_mask(a, true, it.b, it.qb * it.rows / 32, it.rows / 32, BN / 32, kr.lo, kr.hi);
 
   const int64_t qstride = (int64_t)a.heads_q * D;
   const int64_t kstride = (int64_t)a.heads_kv * D;
@@ -826,7 +915,11 @@ bwd_dkdv_kernel(AttnArgs a) {
   const int h0 = g * grp + part * hpp;        // its first query head
   const bool causal = a.causal != 0;
   const SeqGeom sg{lq, lk, a.window, causal};
-  const TileRange qr = key_tile_queries(sg, kb, BN, BM);
+  TileRange qr = key_tile_queries(sg, kb, BN, BM);
+  // with the mask's ranges: only query tiles in which some row has an allowed
+  // bit for a key of this tile
+  if constexpr (M)
+    if (a.mask_ranges != nullptr) narrow_by_mask(a, false, b, kb * BN / 32, BN / 32, BM / 32, qr.lo, qr.hi);
 
   const int64_t qstride = (int64_t)a.heads_q * D;
   const int64_t kstride = (int64_t)a.heads_kv * D;
@@ -1082,7 +1175,11 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
   const int grp = a.heads_q / a.heads_kv;
   const bool causal = a.causal != 0;
   const SeqGeom sg{lq, lk, a.window, causal};
-  const TileRange qr = key_tile_queries(sg, kb, BN, BM);
+  TileRange qr = key_tile_queries(sg, kb, BN, BM);
+  // with the mask's ranges: only query tiles in which some row has an allowed
+  // bit for a key of this tile
+  if constexpr (M)
+    if (a.mask_ranges != nullptr) narrow_by_mask(a, false, b, kb * BN / 32, BN / 32, BM / 32, qr.lo, qr.hi);
 
   const int64_t qstride = (int64_t)a.heads_q * D;
   const int64_t kstride = (int64_t)a.heads_kv * D;
@@ -1299,7 +1396,11 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
   if (kb * BN >= lk) return;
   const int grp = a.heads_q / a.heads_kv;
   const SeqGeom sg{lq, lk, a.window, a.causal != 0};
-  const TileRange qr = key_tile_queries(sg, kb, BN, BM);
+  TileRange qr = key_tile_queries(sg, kb, BN, BM);
+  // with the mask's ranges: only query tiles in which some row has an allowed
+  // bit for a key of this tile
+  if constexpr (M)
+    if (a.mask_ranges != nullptr) narrow_by_mask(a, false, b, kb * BN / 32, BN / 32, BM / 32, qr.lo, qr.hi);
 
   const int64_t qstride = (int64_t)a.heads_q * D;
   const int64_t kstride = (int64_t)a.heads_kv * D;
@@ -1597,6 +1698,14 @@ int dkdv_split(int dtype, int head_dim, int heads_q, int heads_kv, int batch, in
   int s = 1;
   while (g2 * s < 256 && grp % (2 * s) == 0) s *= 2;
   return s;
+}
+
+hipError_t launch_mask_ranges(const AttnArgs& a, int32_t* ranges, hipStream_t st) {
+  const int nrb = (a.max_seqlen_q + 31) / 32, nkb32 = (a.max_seqlen_k + 31) / 32;
+  const int64_t blocks = (int64_t)a.batch * (nrb + nkb32);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(mask_range_kernel, dim3((unsigned)blocks), dim3(64), 0, st, a, ranges, nrb, nkb32);
+  return hipGetLastError();
 }
 
 bool tile_sizes(int dtype, int head_dim, int* fwd_bm, int* fwd_bn, int* bwd_bn, int* bwd_bm) {

@@ -429,6 +429,10 @@ struct AttnArgs {
   // token's sequence; nullptr = no mask
   const uint32_t* mask;
   int64_t mask_words;
+  // optional per-block ranges of the mask's allowed bits (mask_range_kernel):
+  // [batch][nrb][2] first/last 32-key block per 32-row block, then
+  // [batch][nkb32][2] first/last 32-row block per 32-key block; nullptr = none
+  const int32_t* mask_ranges;
   int32_t batch, heads_q, heads_kv, total_q, total_k, max_seqlen_q, max_seqlen_k;
   int32_t window, causal;
   float scale;

@@ -271,6 +271,19 @@ def document_lengths(seed: int, total: int) -> list:
     return out
 
 
+def short_document_lengths(seed: int, total: int, longest: int = 512) -> list:
+    """Short documents, lengths uniform on [64, longest], drawn until ``total``
+    keys are covered (the last one cut to fit): packed rows in which most of
+    a 1,024-token window's tiles belong to other documents."""
+    rng = np.random.default_rng(seed)
+    out, left = [], int(total)
+    while left > 0:
+        n = int(rng.integers(64, longest + 1))
+        out.append(min(n, left))
+        left -= out[-1]
+    return out
+
+
 # ------------------------------------------- linear cross-entropy (second workload)
 # The mlx-train-perf README measures its loss layer at n = 8,192 tokens,
 # vocabulary 151,936, hidden size 4,096, bf16. The hidden states and head are

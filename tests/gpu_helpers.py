@@ -46,10 +46,12 @@ def to_device(w: Workload, x: dict) -> dict:
     return out
 
 
-def run_hip(w: Workload, dev: dict, *, window=None, poison=True, with_backward=True, mask=None) -> dict:
+def run_hip(w: Workload, dev: dict, *, window=None, poison=True, with_backward=True, mask=None,
+            mask_ranges=None) -> dict:
     """Forward then backward through the C ABI. Outputs and workspace are
     filled with NaN first, so any element the kernels fail to write shows.
-    ``mask``: packed mask rows on the device (the masked entry points)."""
+    ``mask``: packed mask rows on the device (the masked entry points);
+    ``mask_ranges``: the ranges attn_mask_ranges wrote for it."""
     import torch
     window = w.window if window is None else window
     kw = dict(max_seqlen_q=w.max_seqlen_q, max_seqlen_k=w.max_seqlen_k, window=window,
@@ -60,7 +62,7 @@ def run_hip(w: Workload, dev: dict, *, window=None, poison=True, with_backward=T
     if poison:
         o.fill_(float("nan"))
         lse.fill_(float("nan"))
-    o, lse = swa.fwd(q, k, v, dev["cu_q"], dev["cu_k"], out=o, lse=lse, mask=mask, **kw)
+    o, lse = swa.fwd(q, k, v, dev["cu_q"], dev["cu_k"], out=o, lse=lse, mask=mask, mask_ranges=mask_ranges, **kw)
     res = dict(o=o, lse=lse)
     if with_backward:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -71,7 +73,7 @@ def run_hip(w: Workload, dev: dict, *, window=None, poison=True, with_backward=T
                 t.fill_(float("nan"))
             ws.fill_(0xFF)
         swa.bwd(q, k, v, o, lse, do, dev["cu_q"], dev["cu_k"], dq=dq, dk=dk, dv=dv, workspace=ws, mask=mask,
-                **kw)
+                mask_ranges=mask_ranges, **kw)
         res.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return res

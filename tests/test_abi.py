@@ -222,3 +222,20 @@ def test_noalloc_backward_refuses_before_any_hip_call():
                max_seqlen_k=140000)
     assert swa.workspace_bytes(big) > swa.NOALLOC_SCRATCH_BYTES
     assert L.attn_bwd_noalloc(ctypes.byref(big), *args, None) == 8
+
+
+def test_mask_ranges_refuses_before_launch():
+    L = swa.lib()
+    p = good()   # batch 1, 100 queries and keys: 4 + 4 blocks -> 16 int32
+    assert L.attn_mask_ranges_bytes(ctypes.byref(p)) == 2 * (4 + 4) * 4
+    assert L.attn_mask_ranges_bytes(ctypes.byref(good(window=0))) == 0
+    m = swa.AttnMask(16, 4)
+    assert L.attn_mask_ranges(ctypes.byref(good(window=0)), ctypes.byref(m), 16, 16, 16, None) == 3
+    assert L.attn_mask_ranges(ctypes.byref(p), None, 16, 16, 16, None) == 1
+    assert L.attn_mask_ranges(ctypes.byref(p), ctypes.byref(swa.AttnMask(16, 2)), 16, 16, 16, None) == 2
+    assert L.attn_mask_ranges(ctypes.byref(p), ctypes.byref(m), None, 16, 16, None) == 1
+    assert L.attn_mask_ranges(ctypes.byref(p), ctypes.byref(m), 16, 16, None, None) == 1
+    assert L.attn_mask_ranges(ctypes.byref(p), ctypes.byref(m), 16, 16, 18, None) == 7
+    # the forward refuses a misaligned ranges pointer in the mask
+    bad = swa.AttnMask(16, 4, 18)
+    assert L.attn_fwd_masked(ctypes.byref(p), ctypes.byref(bad), 16, 16, 16, 16, 16, 16, 16, None) == 7
