@@ -1378,11 +1378,12 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
   constexpr int NT = BN * 2;
   using QTile = LdsTile<T, BM, D>;
   // with M, the step's mask tile follows: BM rows x 4 words (this key tile's
-  // 128 keys), one word per thread
-  static_assert(!M || BM * 4 == NT, "one mask word per thread");
+  // 128 keys)
+  static_assert(BM == 64, "one 64-lane load per row for LSE*log2e, D and the mask");
   constexpr int kMaskOff = 2 * QTile::kBytes + 2 * BM * 4;
   constexpr int kStage = kMaskOff + (M ? BM * 16 : 0);  // Q, dO, LSE*log2e, D[, mask]
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  __shared__ __attribute__((aligned(1024))) char st0[kStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const int nkb = (a.max_seqlen_k + BN - 1) / BN;
@@ -1433,54 +1434,49 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
   // (no query sees this key tile) has no steps and writes zeros.
   const int nq = qr.hi >= qr.lo ? qr.hi - qr.lo + 1 : 0;
   const int steps = grp * nq;
-  TileStage<T, BM, D, NT> sq, sd;
-  float l2v = INFINITY, dlv = 0.f;  // LSE*log2e and D of row tid (tid < BM)
-  uint32_t mword = 0u;               // with M: word tid % 4 of row tid / 4
-  auto issue = [&](int t) {
+  // The streamed tiles go from HBM straight into LDS (no staging registers:
+  // with K and V rows and both accumulators in registers, a register-staged
+  // copy made this kernel spill). Rows past L_q arrive as zeros (LSE*log2e
+  // and D too) and are masked.
+  const uint32_t qsb = (uint32_t)(qstride * sizeof(T));
+  TileLoader<T, BM, D, NT> qld;
+  qld.init(qsb, w, lane);
+  auto fill = [&](int t, char* st) {
     const int h = g * grp + t / nq;
     const int qb = qr.lo + t % nq;
-    const int qvalid = min(BM, lq - qb * BM);
+    const uint32_t qvalid = (uint32_t)min(BM, lq - qb * BM);
     const int64_t qoff = (int64_t)(q0 + qb * BM) * qstride + h * D;
-    sq.load(Qg + qoff, qstride, qvalid, tid);
-    sd.load(Dg + qoff, qstride, qvalid, tid);
-    l2v = INFINITY;
-    dlv = 0.f;
-    if (tid < qvalid) {
-      const int64_t idx = (int64_t)h * a.total_q + q0 + qb * BM + tid;
-      l2v = a.lse2[idx];
-      dlv = a.delta[idx];
+    qld.issue(st, Qg + qoff, qsb, qvalid);
+    qld.issue(st + QTile::kBytes, Dg + qoff, qsb, qvalid);
+    if (w == 0) {
+      const int64_t idx = (int64_t)h * a.total_q + q0 + qb * BM;
+      buffer_to_lds4(buffer_rsrc(a.lse2 + idx, qvalid * 4u), st + 2 * QTile::kBytes, (uint32_t)lane * 4u);
+      buffer_to_lds4(buffer_rsrc(a.delta + idx, qvalid * 4u), st + 2 * QTile::kBytes + BM * 4,
+                     (uint32_t)lane * 4u);
     }
     if constexpr (M) {
-      const int row = tid >> 2;
-      mword = row < qvalid ? a.mask[(int64_t)(q0 + qb * BM + row) * a.mask_words + 4 * kb + (tid & 3)] : 0u;
+      if (w == 1) {  // lane r: row r's words 4 kb .. 4 kb + 3
+        const uint32_t rb = (uint32_t)a.mask_words * 4u;
+        buffer_to_lds16(buffer_rsrc(a.mask + (int64_t)(q0 + qb * BM) * a.mask_words + 4 * kb, qvalid * rb),
+                        st + kMaskOff, (uint32_t)lane * rb);
+      }
     }
   };
-  auto commit = [&](char* st) {
-    sq.store(st, tid);
-    sd.store(st + QTile::kBytes, tid);
-    if (tid < BM) {
-      reinterpret_cast<float*>(st + 2 * QTile::kBytes)[tid] = l2v;
-      reinterpret_cast<float*>(st + 2 * QTile::kBytes + BM * 4)[tid] = dlv;
-    }
-    if constexpr (M) reinterpret_cast<uint32_t*>(st + kMaskOff)[tid] = mword;
-  };
-  if (steps > 0) {
-    issue(0);
-    commit(smem);
-  }
+  if (steps > 0) fill(0, st0);
   __syncthreads();
 
   for (int t = 0; t < steps; ++t) {
     const int stage = t & 1;
-    const char* qs = smem + stage * kStage;
+    const char* qs = stage ? st1 : st0;
     const char* dos = qs + QTile::kBytes;
     const float* lse2s = reinterpret_cast<const float*>(qs + 2 * QTile::kBytes);
     const float* dlts = lse2s + BM;
     const int qb = qr.lo + t % nq;
-    const bool more = t + 1 < steps;
-    if (more) issue(t + 1);
+    if (t + 1 < steps) fill(t + 1, stage ? st0 : st1);
     const bool edge = pw.windowed && !tile_is_full(sg, qb, BM, kb, BN);
-#pragma unroll
+    // one 32-row block at a time (unrolled, the two blocks' fragments were
+    // live together and spilled)
+#pragma unroll 1
     for (int mt = 0; mt < BM / 32; ++mt) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -1527,7 +1523,6 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
         }
       }
     }
-    if (more) commit(smem + (stage ^ 1) * kStage);
     __syncthreads();
   }
   if (key_ok) {
