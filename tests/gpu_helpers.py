@@ -99,6 +99,8 @@ def compare(name: str, got, ref, dtype: str, zero_ref: bool = False, scale_f32: 
         assert max_abs <= ZERO_REF_ABS[dtype], f"{name}: {stats} (zero reference)"
     elif dtype == "f32":
         bar = F32_MAX_ABS * (max(1.0, float(np.abs(ref[fin]).max(initial=0.0))) if scale_f32 else 1.0)
+        if scale_f32:
+            say(f"  {name}: max-abs {max_abs:.2e} (scaled bar {bar:.2e}), rel-Fro {rel:.2e}")
         assert max_abs <= bar, f"{name}: {stats} (bar {bar:.2e})"
     elif dtype == "fp16":
         assert max_abs <= FP16_MAX_ABS and rel <= FP16_REL_FRO, f"{name}: {stats}"
