@@ -109,8 +109,8 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o,
                        float* lse, void* stream);
 
-/* Bytes of device workspace attn_bwd needs for these parameters: D =
- * rowsum(dO * O) and LSE * log2(e), each fp32 [heads_q, total_q] and 256-byte
+/* Bytes of device workspace attn_bwd needs for these parameters: -D =
+ * -rowsum(dO * O) and LSE * log2(e), each fp32 [heads_q, total_q] and 256-byte
  * aligned; plus, when the key tiles (128 keys) x heads_kv x batch are fewer
  * than the GPU's 256 compute units, fp32 partial dK and dV [parts][2][total_k,
  * heads_kv, head_dim] for the dK/dV launch, which then splits each KV group's
@@ -154,7 +154,7 @@ attn_status_t attn_bwd_noalloc(const attn_params_t* p, const void* q, const void
                                void* dk, void* dv, void* stream);
 
 /* The backward's stages, for callers that schedule them themselves:
- *   ATTN_BWD_DELTA: D = rowsum(dO * O) and LSE * log2(e) into the workspace;
+ *   ATTN_BWD_DELTA: -D = -rowsum(dO * O) and LSE * log2(e) into the workspace;
  *   ATTN_BWD_DQ:    dQ (reads Q, K, V, O, LSE and dO); it forms D and
  *                   LSE * log2(e) for its rows itself and writes them into the
  *                   workspace as DELTA does, so a call that selects both runs

@@ -694,7 +694,7 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(AttnArgs a) {
     const int64_t t = t0 + p * RPP + rs;
     if (sub == 0 && t < a.total_q) {
       const int64_t idx = (int64_t)h * a.total_q + t;
-      a.delta[idx] = acc;
+      a.delta[idx] = -acc;
       const float l = a.lse[idx];
       a.lse2[idx] = l == -INFINITY ? INFINITY : l * kLog2e;
     }
@@ -764,11 +764,16 @@ bwd_dq_kernel(AttnArgs a) {
       const float l = a.lse[idx];
       lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
       if (half == 0) {
-        a.delta[idx] = dlt;
+        a.delta[idx] = -dlt;
         a.lse2[idx] = lse2;
       }
     }
   }
+  // dP - D: every dP accumulator starts at -D (this lane's row) instead of 0,
+  // so dS = P * dP needs no subtraction per cell
+  f32x16 ndlt;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndlt[r] = -dlt;
   RowReader<T, D> rrd;
   rrd.init(l32, half);
   ColReader<T, D> crd;
@@ -809,7 +814,7 @@ bwd_dq_kernel(AttnArgs a) {
     if constexpr (M) row_mask_words(a, mrow, row_ok, kb, mw);
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+      f32x16 s = f32x16{}, dp = ndlt;
       // the mask test is skipped when the whole wave's words for this block are all ones
 #pragma unroll
       for (int ss = 0; ss < D / 16; ++ss) {
@@ -818,7 +823,13 @@ bwd_dq_kernel(AttnArgs a) {
       }
       if (edge) {
         const int jb = kb * BN + 32 * kt + 4 * half;  // two-sided: the keys past L_k are masked as well
-        apply_visible(s, (uint32_t)row_keys_visible(mpos - (uint32_t)jb, mlim, rw.pad_keys ? max(it.lk - jb, 0) : -1));
+        uint32_t vis = (uint32_t)row_keys_visible(mpos - (uint32_t)jb, mlim, rw.pad_keys ? max(it.lk - jb, 0) : -1);
+        // at head_dim 512 the Q and dO fragments alone take 256 registers; the
+        // compiler hoisted a tile's 16 per-cell masks out of the key loop and
+        // spilled them (16 scratch reloads per edge tile). An empty asm
+        // statement that claims to change vis keeps them here.
+        if constexpr (D > 256) asm volatile("" : "+v"(vis));
+        apply_visible(s, vis);
       }
       if constexpr (M) {
         if (!__all(mw[kt] == 0xFFFFFFFFu)) apply_row_mask(s, mw[kt], half);
@@ -826,7 +837,7 @@ bwd_dq_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pv = fast_exp2(fmaf(s[r], c, -lse2));
-        s[r] = pv * (dp[r] - dlt);  // dS
+        s[r] = pv * dp[r];  // dS = P (dP - D)
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -1026,7 +1037,14 @@ bwd_dkdv_kernel(AttnArgs a) {
     f32x16 s, dp;  // set and read only when `work`
     if (work) {
     s = f32x16{};
-    dp = f32x16{};
+    // dP - D: the dP accumulator starts at -D of its rows (the workspace holds
+    // -D), so dS = P * dP needs no subtraction per cell
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlts + 32 * mh + 8 * r4 + 4 * half);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = d4[e];
+    }
 #pragma unroll
     for (int ss = 0; ss < D / 16; ++ss) {
       mma(s, rrd.read(qs, 32 * mh, ss), rrd.read(klds, 32 * kt, ss));
@@ -1050,13 +1068,12 @@ bwd_dkdv_kernel(AttnArgs a) {
     for (int r4 = 0; r4 < 4; ++r4) {
       const int rr = 32 * mh + 8 * r4 + 4 * half;
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + rr);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlts + rr);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * r4 + e;
         const float pv = fast_exp2(fmaf(s[r], c, -l4[e]));
         s[r] = pv;
-        dp[r] = pv * (dp[r] - d4[e]);  // dS
+        dp[r] = pv * dp[r];  // dS = P (dP - D)
       }
     }
     }
@@ -1338,7 +1355,7 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
         for (int r4 = 0; r4 < 4; ++r4) {
           const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlts + 8 * r4 + 4 * half);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = s[4 * r4 + e] * (dp[4 * r4 + e] - d4[e]);  // dS
+          for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = s[4 * r4 + e] * (dp[4 * r4 + e] + d4[e]);  // dS (d4: -D)
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -1509,7 +1526,7 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
           const int r = 4 * r4 + e;
           const float pv = fast_exp2(fmaf(s[r], c, -l4[e]));
           s[r] = pv;
-          dp[r] = pv * (dp[r] - d4[e]);  // dS
+          dp[r] = pv * (dp[r] + d4[e]);  // dS (d4: -D)
         }
       }
 #pragma unroll

@@ -416,7 +416,7 @@ struct AttnArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // D = rowsum(dO * O), [heads_q, total_q]
+  float* delta;  // -D = -rowsum(dO * O), [heads_q, total_q] (negated: the dP accumulators start from it)
   float* lse2;   // LSE * log2(e) (+inf where LSE = -inf), [heads_q, total_q]
   // dK/dV with the group's query heads split over kv_split workgroups per key
   // tile (kv_split > 1 when there are too few key tiles to fill the GPU):
