@@ -205,6 +205,22 @@ def test_measured_workloads_sampled(w):
     _invariants(w, x, got)
 
 
+def test_tensors_past_2gib_sampled():
+    """Two sequences of 150,000 and 150,001 tokens, 32 query / 8 KV heads,
+    head_dim 128, window 1,024: Q, O, dO and dQ are 2.46 GB each, so the
+    second sequence's rows lie past 2^31 bytes into them. Sampled rows of both
+    sequences against the oracle."""
+    w = W.SWA_32K.replace(name="bf16_2x150k_w1024_32q8kv_d128", lengths_q=(150000, 150001),
+                          lengths_k=(150000, 150001), seed=12)
+    assert w.total_q * w.heads_q * w.head_dim * 2 > 2 ** 31
+    H.say(f"case {w.name}: sampled rows, tensors past 2 GiB")
+    x = make_inputs(w)
+    dev = H.to_device(w, x)
+    got = H.run_hip(w, dev)
+    stats = H.compare_sampled(w, x, got, n_q=4, n_k=2, seed=w.seed)
+    H.say("  ", {k: {kk: f"{vv:.2e}" for kk, vv in v.items()} for k, v in stats.items()})
+
+
 @pytest.mark.parametrize("window", W.VARLEN_SWEEP_WINDOWS)
 def test_varlen_window_sweep(window):
     w = W.VARLEN_4.replace(window=window)
