@@ -88,3 +88,54 @@ def test_varlen_window_sweep_whole_heads(w, chunk):
     # window 1: each query sees only itself, so the exact dQ and dK are zero
     # and only rounding is left
     _check(w, *chunk, zero=("dq", "dk") if w.window == 1 else ())
+
+
+# The 32K windowed workload with its tokens packed from documents (a
+# block-diagonal mask combined with the window): corpus-like documents, and
+# documents of at most 512 tokens run with the mask's tile ranges (the tiles
+# the mask empties are skipped). Every element of KV groups 0 and Hkv - 1.
+_MCACHE = {}
+
+
+def _run_masked(kind):
+    import torch
+    if kind not in _MCACHE:
+        _MCACHE.clear()
+        w = W.SWA_32K
+        docs = (W.document_lengths(91, w.lengths_k[0]) if kind == "documents"
+                else W.short_document_lengths(92, w.lengths_k[0], 512))
+        bits = W.document_mask_bits(w, [docs])
+        H.say(f"case {w.name} {kind}: {len(docs)} documents, full-size run")
+        x = make_inputs(w)
+        dev = H.to_device(w, x)
+        dmask = torch.from_numpy(bits.view(np.int32)).cuda()
+        kw = dict(max_seqlen_q=w.max_seqlen_q, max_seqlen_k=w.max_seqlen_k, window=w.window, causal=w.causal,
+                  scale=w.scale)
+        ranges = None
+        if kind == "short":
+            import sliding_window_flash_amd as swa
+            ranges = swa.mask_ranges(dev["q"], dev["k"], dev["cu_q"], dev["cu_k"], dmask, **kw)
+        got = H.run_hip(w, dev, mask=dmask, mask_ranges=ranges)
+        _MCACHE[kind] = (w, x, {k: H.host64(v) for k, v in got.items()}, W.PackedMaskRows(bits, w.lengths_k[0]))
+        del got
+        torch.cuda.empty_cache()
+    return _MCACHE[kind]
+
+
+@pytest.mark.parametrize("kind", ["documents", "short"])
+@pytest.mark.parametrize("group", [0, 7])
+def test_masked_documents_whole_heads(kind, group):
+    w, x, got, view = _run_masked(kind)
+    grp = w.heads_q // w.heads_kv
+    heads = list(range(group * grp, (group + 1) * grp))
+    ref = dense.sdpa_reference(x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale, w.window,
+                               w.causal, heads=heads, band=True, mask=view)
+    hs, gs = slice(group * grp, (group + 1) * grp), slice(group, group + 1)
+    stats = {
+        "o": H.compare(f"{kind} O", got["o"][:, hs], ref["o"][:, hs], w.dtype),
+        "lse": H.compare(f"{kind} LSE", got["lse"][hs], ref["lse"][hs], w.dtype),
+        "dq": H.compare(f"{kind} dQ", got["dq"][:, hs], ref["dq"][:, hs], w.dtype),
+        "dk": H.compare(f"{kind} dK", got["dk"][:, gs], ref["dk"][:, gs], w.dtype),
+        "dv": H.compare(f"{kind} dV", got["dv"][:, gs], ref["dv"][:, gs], w.dtype),
+    }
+    H.say(f"  {kind} kv group {group}:", {k: {kk: f"{vv:.2e}" for kk, vv in v.items()} for k, v in stats.items()})
