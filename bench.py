@@ -148,8 +148,21 @@ def cpu_baseline(w, x, rows: int):
         delta = lk - lq
         pairs += sum(min(i + delta + 1, w.window) for i in range(min(rows, lq)))
     flops = 14 * w.head_dim * pairs
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    info = threadpool_info()
+    threads = max([p.get("num_threads", 1) for p in info] + [1])
+    blas = ", ".join(sorted({f"{p.get('internal_api', '?')} {p.get('version', '')}".strip()
+                             for p in info if p.get("user_api") == "blas"})) or "unknown"
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model, "blas": blas,
             "sample": f"query head 0, query rows [0, {rows}) of each sequence; fp64 numpy dense "
                       f"masked score panels, forward + backward; {dt:.1f} s",
             "seconds": round(dt, 2)}
@@ -289,6 +302,22 @@ def main() -> int:
                       "flop_per_pair_counted": counted * d, "flop_per_pair_executed": executed * d,
                       "achieved_executed": round(ach_x, 2),
                       "frac_executed": round(ach_x / BF16_DENSE_PEAK_TFLOPS, 4)}
+    # The stage API's separate D pass (D and LSE * log2 e, for callers that run
+    # dK/dV without dQ): not part of the step, HBM-bound. Algorithmic bytes:
+    # O and dO read once, LSE read, the two fp32 [Hq, T] outputs written.
+    dev_ = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in dev_:
+        e[0].record(stream)
+        swa.bwd(q, k, v, o, lse, do, cu_q, cu_k, dq=dq, dk=dk, dv=dv, workspace=ws, stages=swa.BWD_DELTA, **kw)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    delta_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_]))
+    delta_bytes = 2 * q.numel() * q.element_size() + 3 * lse.numel() * 4
+    delta_gbs = delta_bytes / (delta_ms * 1e-3) / 1e9
+    kernels_other = {"bwd_delta": {"ms": round(delta_ms, 4), "bound": "hbm", "achieved": round(delta_gbs, 1),
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(delta_gbs / HBM_PEAK_GBS, 4),
+                                   "bytes_per_launch": delta_bytes,
+                                   "note": "stage API only; attn_bwd forms D inside dQ"}}
     dom = max(("fwd", "bwd_dq", "bwd_dkdv"), key=lambda n: kern_ms[n])
     traffic = load_traffic(dom)
     roofline = {k: v for k, v in kernels[dom].items() if k in ("bound", "achieved", "peak", "unit", "frac")}
@@ -574,6 +603,7 @@ def main() -> int:
         "fwd_ms": round(kern_ms["fwd"], 4),
         "bwd_ms": round(kern_ms["bwd_dq"] + kern_ms["bwd_dkdv"], 4),
         "kernels": kernels,
+        "kernels_other": kernels_other,
         "roofline": roofline,
         "memory": mem,
         "memory_probe_shape": gemma,
