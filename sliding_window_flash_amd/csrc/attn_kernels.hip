@@ -136,21 +136,20 @@ struct GroupedItem {
 // XCD runs a contiguous logical range.
 __device__ __forceinline__ GroupedItem decode_grouped_item(const AttnArgs& a, int w) {
   GroupedItem it;
-  const int hw = query_heads_per_wg(a.heads_q, a.heads_kv);
-  const int grp = a.heads_q / a.heads_kv;
-  const int nch = grp / hw;
-  it.rows = 128 / hw;
-  const int nqb = (a.max_seqlen_q + it.rows - 1) / it.rows;
-  const int n = nqb * a.heads_kv * nch * a.batch;
-  int L = xcd_remap((int)blockIdx.x, n);
-  const int ch = L % nch;
-  L /= nch;
-  it.qb = nqb - 1 - L % nqb;
-  L /= nqb;
-  it.b = L % a.batch;
-  it.g = L / a.batch;
-  it.h = it.g * grp + ch * hw + w % hw;
-  it.row0 = it.qb * it.rows + 32 * (w / hw);
+  const int hw = 1 << a.q_hw_log2;
+  it.rows = a.q_rows;
+  uint32_t L = (uint32_t)xcd_remap((int)blockIdx.x, a.q_items);
+  uint32_t q = fast_div(L, a.div_nch);
+  const int ch = (int)(L - q * (uint32_t)a.q_nch);
+  L = q;
+  q = fast_div(L, a.div_nqb);
+  it.qb = a.q_nqb - 1 - (int)(L - q * (uint32_t)a.q_nqb);
+  L = q;
+  q = fast_div(L, a.div_batch);
+  it.b = (int)(L - q * (uint32_t)a.batch);
+  it.g = (int)q;
+  it.h = it.g * a.q_grp + ch * hw + (w & (hw - 1));
+  it.row0 = it.qb * it.rows + 32 * (w >> a.q_hw_log2);
   it.q0 = a.cu_q[it.b];
   it.lq = a.cu_q[it.b + 1] - it.q0;
   it.k0 = a.cu_k[it.b];
@@ -908,22 +907,25 @@ bwd_dkdv_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int w = wave_uniform(tid >> 6);
   const int kt = w & 3, mh = w >> 2;
-  const int nkb = (a.max_seqlen_k + BN - 1) / BN;
+  static_assert(BN == 128, "the launch-id decode counts 128-key tiles (AttnArgs::k_nkb)");
   // work item: (KV head, sequence, key tile, part of the group's query heads),
   // the part innermost so that the parts of one key tile share an L2
-  int L = xcd_remap((int)blockIdx.x, nkb * a.heads_kv * a.batch * a.kv_split);
-  const int part = L % a.kv_split;
-  L /= a.kv_split;
-  const int kb = L % nkb;
-  L /= nkb;
-  const int b = L % a.batch;
-  const int g = L / a.batch;
+  uint32_t L = (uint32_t)xcd_remap((int)blockIdx.x, a.k_items);
+  uint32_t qt = fast_div(L, a.div_split);
+  const int part = (int)(L - qt * (uint32_t)a.kv_split);
+  L = qt;
+  qt = fast_div(L, a.div_nkb);
+  const int kb = (int)(L - qt * (uint32_t)a.k_nkb);
+  L = qt;
+  qt = fast_div(L, a.div_batch);
+  const int b = (int)(L - qt * (uint32_t)a.batch);
+  const int g = (int)qt;
   const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
   const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
   if (kb * BN >= lk) return;
-  const int grp = a.heads_q / a.heads_kv;
-  const int hpp = grp / a.kv_split;           // query heads of this part
-  const int h0 = g * grp + part * hpp;        // its first query head
+  const int grp = a.q_grp;
+  const int hpp = a.k_hpp;                // query heads of this part
+  const int h0 = g * grp + part * hpp;  // its first query head
   const bool causal = a.causal != 0;
   const SeqGeom sg{lq, lk, a.window, causal};
   TileRange qr = key_tile_queries(sg, kb, BN, BM);
@@ -1180,16 +1182,19 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int w = wave_uniform(tid >> 6);
-  const int nkb = (a.max_seqlen_k + BN - 1) / BN;
-  int L = xcd_remap((int)blockIdx.x, nkb * a.heads_kv * a.batch);
-  const int kb = L % nkb;
-  L /= nkb;
-  const int b = L % a.batch;
-  const int g = L / a.batch;
+  static_assert(BN == 128, "the launch-id decode counts 128-key tiles (AttnArgs::k_nkb)");
+  const int nkb = a.k_nkb;
+  uint32_t L = (uint32_t)xcd_remap((int)blockIdx.x, a.k_items);  // kv_split is 1 here
+  uint32_t qt = fast_div(L, a.div_nkb);
+  const int kb = (int)(L - qt * (uint32_t)nkb);
+  L = qt;
+  qt = fast_div(L, a.div_batch);
+  const int b = (int)(L - qt * (uint32_t)a.batch);
+  const int g = (int)qt;
   const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
   const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
   if (kb * BN >= lk) return;
-  const int grp = a.heads_q / a.heads_kv;
+  const int grp = a.q_grp;
   const bool causal = a.causal != 0;
   const SeqGeom sg{lq, lk, a.window, causal};
   TileRange qr = key_tile_queries(sg, kb, BN, BM);
@@ -1403,16 +1408,19 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char st1[kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
-  const int nkb = (a.max_seqlen_k + BN - 1) / BN;
-  int L = xcd_remap((int)blockIdx.x, nkb * a.heads_kv * a.batch);
-  const int kb = L % nkb;
-  L /= nkb;
-  const int b = L % a.batch;
-  const int g = L / a.batch;
+  static_assert(BN == 128, "the launch-id decode counts 128-key tiles (AttnArgs::k_nkb)");
+  const int nkb = a.k_nkb;
+  uint32_t L = (uint32_t)xcd_remap((int)blockIdx.x, a.k_items);  // kv_split is 1 here
+  uint32_t qt = fast_div(L, a.div_nkb);
+  const int kb = (int)(L - qt * (uint32_t)nkb);
+  L = qt;
+  qt = fast_div(L, a.div_batch);
+  const int b = (int)(L - qt * (uint32_t)a.batch);
+  const int g = (int)qt;
   const int q0 = a.cu_q[b], lq = a.cu_q[b + 1] - q0;
   const int k0 = a.cu_k[b], lk = a.cu_k[b + 1] - k0;
   if (kb * BN >= lk) return;
-  const int grp = a.heads_q / a.heads_kv;
+  const int grp = a.q_grp;
   const SeqGeom sg{lq, lk, a.window, a.causal != 0};
   TileRange qr = key_tile_queries(sg, kb, BN, BM);
   // with the mask's ranges: only query tiles in which some row has an allowed
@@ -1561,13 +1569,34 @@ template <int D> struct Tiles {
   static constexpr int kBwdBN = 128, kBwdBM = D > 128 ? 32 : 64;
 };
 
+// The launch-invariant parts of the launch-id decode (AttnArgs::q_*, k_*,
+// div_*), for query-major tiles of 128 rows over 1, 2 or 4 heads and
+// key-major tiles of 128 keys. The C ABI bounds both item counts by INT32_MAX.
+static AttnArgs with_decode(const AttnArgs& in) {
+  AttnArgs a = in;
+  const int hw = query_heads_per_wg(a.heads_q, a.heads_kv);
+  a.q_grp = a.heads_q / a.heads_kv;
+  a.q_hw_log2 = hw == 4 ? 2 : (hw == 2 ? 1 : 0);
+  a.q_nch = a.q_grp / hw;
+  a.q_rows = 128 / hw;
+  a.q_nqb = (a.max_seqlen_q + a.q_rows - 1) / a.q_rows;
+  a.q_items = (int32_t)((int64_t)a.q_nqb * a.q_nch * a.heads_kv * a.batch);
+  a.k_nkb = (a.max_seqlen_k + 127) / 128;
+  a.k_hpp = a.q_grp / a.kv_split;
+  a.k_items = (int32_t)((int64_t)a.k_nkb * a.heads_kv * a.batch * a.kv_split);
+  a.div_nch = make_fast_div((uint32_t)a.q_nch);
+  a.div_nqb = make_fast_div((uint32_t)(a.q_nqb > 0 ? a.q_nqb : 1));
+  a.div_batch = make_fast_div((uint32_t)a.batch);
+  a.div_nkb = make_fast_div((uint32_t)(a.k_nkb > 0 ? a.k_nkb : 1));
+  a.div_split = make_fast_div((uint32_t)a.kv_split);
+  return a;
+}
+
 // M: a mask combined with the window (a.mask != nullptr)
 template <typename T, int D, bool M>
 static hipError_t launch_fwd_m(const AttnArgs& a, hipStream_t st) {
   using TL = Tiles<D>;
-  const int hw = query_heads_per_wg(a.heads_q, a.heads_kv);
-  const int64_t nqb = (a.max_seqlen_q + 128 / hw - 1) / (128 / hw);
-  const int64_t grid = nqb * (a.heads_q / hw) * a.batch;
+  const int64_t grid = a.q_items;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((fwd_kernel<T, D, TL::kFwdBM, TL::kFwdBN, M>), dim3((unsigned)grid), dim3(TL::kFwdBM * 2), 0,
                      st, a);
@@ -1592,23 +1621,21 @@ static hipError_t launch_bwd_m(int stages, const AttnArgs& a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 2) {
-    const int hw = query_heads_per_wg(a.heads_q, a.heads_kv);
-    const int64_t nqb = (a.max_seqlen_q + 128 / hw - 1) / (128 / hw);
-    const int64_t g1 = nqb * (a.heads_q / hw) * a.batch;
+    const int64_t g1 = a.q_items;
     if (g1 > 0 && rows > 0) {
       hipLaunchKernelGGL((bwd_dq_kernel<T, D, TL::kFwdBM, TL::kFwdBN, M>), dim3((unsigned)g1), dim3(TL::kFwdBM * 2),
                          0, st, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
-  const int64_t nkb = (a.max_seqlen_k + TL::kBwdBN - 1) / TL::kBwdBN;
-  const int64_t g2 = nkb * a.heads_kv * a.batch;
+  static_assert(TL::kBwdBN == 128, "with_decode counts 128-key tiles");
+  const int64_t g2 = a.k_items;  // key tiles x KV heads x sequences x kv_split
   if ((stages & 4) && g2 > 0) {
     if constexpr (D > 128)
       hipLaunchKernelGGL((bwd_dkdv_wide_kernel<T, D, TL::kBwdBN, TL::kBwdBM, M>), dim3((unsigned)g2), dim3(256), 0,
                          st, a);
     else if constexpr (sizeof(T) == 2) {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, TL::kBwdBN, TL::kBwdBM, M>), dim3((unsigned)(g2 * a.kv_split)),
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, TL::kBwdBN, TL::kBwdBM, M>), dim3((unsigned)g2),
                          dim3(TL::kBwdBN * 4), 0, st, a);
       if (a.kv_split > 1) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1631,7 +1658,8 @@ static hipError_t launch_bwd_t(int stages, const AttnArgs& a, hipStream_t st) {
 
 // head_dim 256 and 512 exist for the 16-bit types only (the C ABI refuses
 // fp32 there)
-hipError_t launch_fwd(int dtype, int head_dim, const AttnArgs& a, hipStream_t st) {
+hipError_t launch_fwd(int dtype, int head_dim, const AttnArgs& in, hipStream_t st) {
+  const AttnArgs a = with_decode(in);
   if (dtype == 2 && head_dim == 512) return launch_fwd_t<fp16, 512>(a, st);
   if (dtype == 1 && head_dim == 512) return launch_fwd_t<bf16, 512>(a, st);
   if (dtype == 2 && head_dim == 256) return launch_fwd_t<fp16, 256>(a, st);
@@ -1645,7 +1673,8 @@ hipError_t launch_fwd(int dtype, int head_dim, const AttnArgs& a, hipStream_t st
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd(int dtype, int head_dim, int stages, const AttnArgs& a, hipStream_t st) {
+hipError_t launch_bwd(int dtype, int head_dim, int stages, const AttnArgs& in, hipStream_t st) {
+  const AttnArgs a = with_decode(in);
   if (dtype == 2 && head_dim == 512) return launch_bwd_t<fp16, 512>(stages, a, st);
   if (dtype == 1 && head_dim == 512) return launch_bwd_t<bf16, 512>(stages, a, st);
   if (dtype == 2 && head_dim == 256) return launch_bwd_t<fp16, 256>(stages, a, st);

@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sched.hpp"
+
 namespace swa {
 
 typedef __bf16 bf16;
@@ -436,6 +438,14 @@ struct AttnArgs {
   int32_t batch, heads_q, heads_kv, total_q, total_k, max_seqlen_q, max_seqlen_k;
   int32_t window, causal;
   float scale;
+  // Launch-invariant parts of the launch-id decode, set by the launchers
+  // (with_decode): query-major items (forward, dQ) take 2^q_hw_log2 query
+  // heads of a group of q_grp, in q_nch chunks, and q_rows rows, in q_nqb row
+  // blocks per sequence (q_items in all); key-major items (dK/dV) take a key
+  // tile of 128 (k_nkb per sequence) and k_hpp of the group's query heads
+  // (k_items in all). The divisions of the decode use the multipliers.
+  int32_t q_grp, q_hw_log2, q_nch, q_rows, q_nqb, q_items, k_nkb, k_hpp, k_items;
+  FastDiv div_nch, div_nqb, div_batch, div_nkb, div_split;
 };
 
 }  // namespace swa

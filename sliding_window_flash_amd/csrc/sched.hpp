@@ -138,6 +138,28 @@ SWA_HD int32_t xcd_remap(int32_t id, int32_t n, int32_t nxcd = 8) {
   return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 
+// Division by a divisor d >= 1 that is fixed for a launch, as a multiply-high,
+// an add and a shift (Granlund and Montgomery, "Division by invariant integers
+// using multiplication", 1994, section 4): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, which is below 2^32, floor(n / d) is
+// (mulhi(m, n) + n) >> l for every 32-bit n. For n < 2^31, as in the kernels'
+// launch-id decode, the sum cannot overflow (mulhi(m, n) <= n). The launchers
+// build the multipliers once per launch on the host; a workgroup then decodes
+// its launch id without the long sequence of a runtime 32-bit division.
+struct FastDiv {
+  uint32_t d, m, l;
+};
+SWA_HD FastDiv make_fast_div(uint32_t d) {  // d >= 1
+  uint32_t l = 0;
+  while (((uint64_t)1 << l) < d) ++l;
+  const uint64_t m = ((uint64_t)1 << 32) * (((uint64_t)1 << l) - d) / d + 1;
+  return FastDiv{d, (uint32_t)m, l};
+}
+SWA_HD uint32_t fast_div(uint32_t n, const FastDiv& f) {  // floor(n / f.d) for n < 2^31
+  const uint32_t hi = (uint32_t)(((uint64_t)f.m * n) >> 32);
+  return (hi + n) >> f.l;
+}
+
 // Per-cell visibility, used inside edge tiles.
 SWA_HD bool cell_visible(const SeqGeom& s, int64_t i, int64_t j) {
   if (i >= s.lq || j >= s.lk) return false;

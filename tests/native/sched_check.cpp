@@ -1,8 +1,11 @@
 // Host build of the kernels' scheduler header: checks the int32 closed-form
 // full-tile test against the int64 tile ranges over an exhaustive grid of
-// small shapes. Exit status 0 = all agree.
+// small shapes, the per-block skip tests against cell enumeration, and the
+// launch-id decode's multiply-high division against plain division. Exit
+// status 0 = all agree.
 #include <cstdio>
 #include <initializer_list>
+#include <vector>
 
 #include "../../sliding_window_flash_amd/csrc/sched.hpp"
 
@@ -105,6 +108,50 @@ int main() {
         }
   printf("intervals checked %ld, mismatches %ld\n", ichecked, ibad);
   bad += ibad;
+  // the launch-id decode's division by multiply-high against plain division:
+  // every numerator below 2^17 for every divisor up to 4,100; for divisors
+  // up to 2^31 - 1 (small, powers of two and their neighbours, large primes,
+  // pseudo-random), the multiples of d and their neighbours across [0, 2^31)
+  // and pseudo-random numerators
+  long fchecked = 0, fbad = 0;
+  auto check_div = [&](uint32_t d, uint32_t n) {
+    const swa::FastDiv f = swa::make_fast_div(d);
+    const uint32_t got = swa::fast_div(n, f), want = n / d;
+    ++fchecked;
+    if (got != want) {
+      if (fbad < 5) printf("fast_div mismatch n=%u d=%u: %u vs %u\n", n, d, got, want);
+      ++fbad;
+    }
+  };
+  for (uint32_t d = 1; d <= 4100; ++d)
+    for (uint32_t n = 0; n < (1u << 17); ++n) check_div(d, n);
+  uint64_t x = 0x9E3779B97F4A7C15ull;
+  auto rnd = [&]() {
+    x ^= x << 13;
+    x ^= x >> 7;
+    x ^= x << 17;
+    return x;
+  };
+  std::vector<uint32_t> divisors;
+  for (int k = 0; k < 31; ++k)
+    for (int e = -1; e <= 1; ++e) {
+      const int64_t d = ((int64_t)1 << k) + e;
+      if (d >= 1 && d < ((int64_t)1 << 31)) divisors.push_back((uint32_t)d);
+    }
+  for (uint32_t d : {3u, 7u, 10u, 641u, 6700417u, 65537u, 2147483647u, 2147483629u, 1000003u, 12345u}) divisors.push_back(d);
+  for (int i = 0; i < 200; ++i) divisors.push_back((uint32_t)(1 + rnd() % 2147483647ull));
+  for (uint32_t d : divisors) {
+    const uint32_t top = 2147483647u;
+    for (uint64_t k = 0; k * d <= top; k += (top / d) / 64 + 1)
+      for (int e = -1; e <= 1; ++e) {
+        const int64_t n = (int64_t)(k * d) + e;
+        if (n >= 0 && n <= top) check_div(d, (uint32_t)n);
+      }
+    check_div(d, top);
+    for (int i = 0; i < 2000; ++i) check_div(d, (uint32_t)(rnd() & 0x7fffffffu));
+  }
+  printf("divisions checked %ld, mismatches %ld\n", fchecked, fbad);
+  bad += fbad;
   printf("checked %ld, mismatches %ld\n", checked, bad);
   return bad != 0;
 }
