@@ -25,6 +25,13 @@ FP16_REL_FRO = BF16_REL_FRO / 4
 # Where the exact result is identically zero (window 1: dQ, dK; scale 0), only
 # rounding is left; the bar is max-abs 1e-4 in bf16 and 1e-6 in fp32.
 ZERO_REF_ABS = {"bf16": 1e-4, "fp16": 1e-4, "f32": 1e-6}
+# The backward forms D = rowsum(dO * O) from the stored O (the forward's
+# output, in the I/O dtype); the oracle forms it from its exact O. Where a
+# row's D lies close to the dP of its visible keys, dS = P (dP - D) cancels and
+# that rounding of O dominates dQ and dK. compare_full adds to their relative
+# Frobenius bar twice the first-order error the rounding causes, computed from
+# the oracle's own values (stored_o_allowance); elsewhere it is far below the
+# bar and changes nothing.
 
 
 def say(*args):
@@ -84,7 +91,10 @@ def host64(t) -> np.ndarray:
     return t.detach().to(torch.float64).cpu().numpy()
 
 
-def compare(name: str, got, ref, dtype: str, zero_ref: bool = False, scale_f32: bool = False) -> dict:
+def compare(name: str, got, ref, dtype: str, zero_ref: bool = False, scale_f32: bool = False,
+            rel_allow: float = 0.0) -> dict:
+    """``rel_allow``: added to the 16-bit relative Frobenius bar (see
+    stored_o_allowance)."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
@@ -102,10 +112,11 @@ def compare(name: str, got, ref, dtype: str, zero_ref: bool = False, scale_f32: 
         if scale_f32:
             say(f"  {name}: max-abs {max_abs:.2e} (scaled bar {bar:.2e}), rel-Fro {rel:.2e}")
         assert max_abs <= bar, f"{name}: {stats} (bar {bar:.2e})"
-    elif dtype == "fp16":
-        assert max_abs <= FP16_MAX_ABS and rel <= FP16_REL_FRO, f"{name}: {stats}"
     else:
-        assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_FRO, f"{name}: {stats}"
+        bar_abs, bar_rel = (FP16_MAX_ABS, FP16_REL_FRO) if dtype == "fp16" else (BF16_MAX_ABS, BF16_REL_FRO)
+        if rel_allow > 0.1 * bar_rel:
+            say(f"  {name}: rel-Fro {rel:.2e}, bar {bar_rel:.1e} + stored-O allowance {rel_allow:.2e}")
+        assert max_abs <= bar_abs and rel <= bar_rel + rel_allow, f"{name}: {stats} (allowance {rel_allow:.2e})"
     return stats
 
 
@@ -118,15 +129,40 @@ def full_reference(w: Workload, x: dict, window=None, mask=None) -> dict:
                                 window, w.causal, band=True, **kw)
 
 
+def stored_o_allowance(w: Workload, x: dict, ref: dict, window=None, mask=None) -> dict:
+    """Twice the relative Frobenius error, to first order, that forming D from
+    O rounded to the I/O dtype causes in dQ and dK, from the oracle's values.
+    With dD = rowsum(dO * (round(O) - O)), dS = P (dP - D) moves by -P dD, so
+    dQ moves by -scale dD (P K) and dK by -scale P^T (dD Q), summed over the
+    group. P K is the oracle's forward with K as the values; P^T (dD Q) its dV
+    with dD Q as the output gradient. Twice: the kernels' O also carries the
+    forward's own rounding (P as a 16-bit operand), of the same order."""
+    from sliding_window_flash_amd.workloads import _round_16
+    window = w.window if window is None else window
+    kw = {} if mask is None else dict(mask=mask)
+    o = ref["o"]
+    dd = ((_round_16(o.astype(np.float32), w.dtype).astype(np.float64) - o) * x["do"]).sum(-1)  # [T_q, Hq]
+    common = (x["cu_q"], x["cu_k"], w.scale, window, w.causal)
+    pk = dense.sdpa_reference(x["q"], x["k"], x["k"], x["do"], *common, with_backward=False, band=True, **kw)["o"]
+    pdq = dense.sdpa_reference(x["q"], x["k"], x["v"], dd[..., None] * x["q"], *common, band=True, **kw)["dv"]
+    out = {}
+    for key, err in (("dq", w.scale * dd[..., None] * pk), ("dk", w.scale * pdq)):
+        nrm = float(np.linalg.norm(ref[key]))
+        out[key] = 2.0 * float(np.linalg.norm(err)) / nrm if nrm > 0 else 0.0
+    return out
+
+
 def compare_full(w: Workload, x: dict, got: dict, window=None, zero=(), mask=None, scale_f32=False) -> dict:
     """``mask``: the boolean mask rows (oracle side) when the run used one;
-    ``scale_f32``: the fp32 bar relative to the output's largest magnitude."""
+    ``scale_f32``: the fp32 bar relative to the output's largest magnitude.
+    In bf16 and fp16 the dQ and dK bars take the stored-O allowance."""
     ref = full_reference(w, x, window, mask)
+    allow = stored_o_allowance(w, x, ref, window, mask) if w.dtype in ("bf16", "fp16") and "dq" in got else {}
     out = {}
     for key in ("o", "lse", "dq", "dk", "dv"):
         if key in got:
             out[key] = compare(f"{w.name} {key}", host64(got[key]), ref[key], w.dtype,
-                               zero_ref=key in zero, scale_f32=scale_f32)
+                               zero_ref=key in zero, scale_f32=scale_f32, rel_allow=allow.get(key, 0.0))
     return out
 
 
