@@ -1579,9 +1579,9 @@ static AttnArgs with_decode(const AttnArgs& in) {
   a.q_hw_log2 = hw == 4 ? 2 : (hw == 2 ? 1 : 0);
   a.q_nch = a.q_grp / hw;
   a.q_rows = 128 / hw;
-  a.q_nqb = (a.max_seqlen_q + a.q_rows - 1) / a.q_rows;
+  a.q_nqb = (int32_t)(((int64_t)a.max_seqlen_q + a.q_rows - 1) / a.q_rows);
   a.q_items = (int32_t)((int64_t)a.q_nqb * a.q_nch * a.heads_kv * a.batch);
-  a.k_nkb = (a.max_seqlen_k + 127) / 128;
+  a.k_nkb = (int32_t)(((int64_t)a.max_seqlen_k + 127) / 128);
   a.k_hpp = a.q_grp / a.kv_split;
   a.k_items = (int32_t)((int64_t)a.k_nkb * a.heads_kv * a.batch * a.kv_split);
   a.div_nch = make_fast_div((uint32_t)a.q_nch);
@@ -1734,7 +1734,7 @@ template <int D> static void tiles_of(int* fwd_bm, int* fwd_bn, int* bwd_bn, int
 // that reach that many (the 8-wave 16-bit kernel only).
 int dkdv_split(int dtype, int head_dim, int heads_q, int heads_kv, int batch, int max_seqlen_k) {
   if (dtype == 0 || head_dim > 128) return 1;
-  const int64_t g2 = (int64_t)((max_seqlen_k + Tiles<128>::kBwdBN - 1) / Tiles<128>::kBwdBN) * heads_kv * batch;
+  const int64_t g2 = (((int64_t)max_seqlen_k + Tiles<128>::kBwdBN - 1) / Tiles<128>::kBwdBN) * heads_kv * batch;
   const int grp = heads_q / heads_kv;
   int s = 1;
   while (g2 * s < 256 && grp % (2 * s) == 0) s *= 2;
@@ -1742,7 +1742,7 @@ int dkdv_split(int dtype, int head_dim, int heads_q, int heads_kv, int batch, in
 }
 
 hipError_t launch_mask_ranges(const AttnArgs& a, int32_t* ranges, hipStream_t st) {
-  const int nrb = (a.max_seqlen_q + 31) / 32, nkb32 = (a.max_seqlen_k + 31) / 32;
+  const int nrb = (int)(((int64_t)a.max_seqlen_q + 31) / 32), nkb32 = (int)(((int64_t)a.max_seqlen_k + 31) / 32);
   const int64_t blocks = (int64_t)a.batch * (nrb + nkb32);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(mask_range_kernel, dim3((unsigned)blocks), dim3(64), 0, st, a, ranges, nrb, nkb32);

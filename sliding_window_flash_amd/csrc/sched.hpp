@@ -149,7 +149,7 @@ SWA_HD int32_t xcd_remap(int32_t id, int32_t n, int32_t nxcd = 8) {
 struct FastDiv {
   uint32_t d, m, l;
 };
-SWA_HD FastDiv make_fast_div(uint32_t d) {  // d >= 1
+SWA_HD FastDiv make_fast_div(uint32_t d) {  // 1 <= d < 2^31, so that l <= 31
   uint32_t l = 0;
   while (((uint64_t)1 << l) < d) ++l;
   const uint64_t m = ((uint64_t)1 << 32) * (((uint64_t)1 << l) - d) / d + 1;
