@@ -36,8 +36,9 @@
  *   Head h of Q uses KV head h / (heads_q / heads_kv) (contiguous groups).
  *
  * Ownership: the caller owns every buffer, including the backward workspace.
- * The library allocates no device memory and keeps no state between calls, so
- * all device memory is visible to the caller's allocator. Every element of
+ * The library allocates no device memory and keeps no state between calls
+ * (except attn_bwd_noalloc's fixed per-GPU array, described there), so all
+ * device memory is visible to the caller's allocator. Every element of
  * every output is written (zeros where the definition gives zero): outputs
  * need no clearing.
  *
