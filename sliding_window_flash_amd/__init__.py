@@ -297,6 +297,9 @@ def mask_ranges(q, k, cu_q, cu_k, mask, *, max_seqlen_q, max_seqlen_k, window=IN
     out = torch.empty(max(n, 1), dtype=torch.int32, device=q.device) if out is None else out
     if out.numel() < n or out.dtype != torch.int32:
         raise ValueError(f"mask_ranges out must be int32 with {n} elements")
+    _require(out, "mask_ranges out")
+    if out.device != q.device:
+        raise ValueError(f"mask_ranges out is on {out.device}, q on {q.device}")
     m = _mask_arg(mask)
     st = lib().attn_mask_ranges(ctypes.byref(p), ctypes.byref(m), _ptr(cu_q), _ptr(cu_k), _ptr(out),
                                 _stream_ptr(stream))
