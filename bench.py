@@ -65,15 +65,15 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str):
+def load_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, or
-    None if absent or taken on different kernel sources."""
+    None if absent, taken on different kernel sources or on another workload."""
     try:
         with open(TRAFFIC_FILE) as fh:
             t = json.load(fh)
     except OSError:
         return None
-    if t.get("source_hash") != source_hash():
+    if t.get("source_hash") != source_hash() or t.get("workload") != workload:
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
@@ -83,7 +83,7 @@ KERNEL_NAMES = {"fwd_kernel": "fwd", "bwd_delta_kernel": "bwd_delta", "bwd_dq_ke
                 "bwd_dkdv_kernel": "bwd_dkdv", "bwd_dkdv4_kernel": "bwd_dkdv"}
 
 
-def write_traffic(fetch_csv: str, write_csv: str, copy_mib: int, commands: list) -> dict:
+def write_traffic(fetch_csv: str, write_csv: str, copy_mib: int, commands: list, workload: str) -> dict:
     """Turn two rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
     of a run made with --copy-calibration-mib into HBM bytes per launch of each
     kernel. The counters' scale is taken from the calibration copy, a kernel
@@ -123,7 +123,7 @@ def write_traffic(fetch_csv: str, write_csv: str, copy_mib: int, commands: list)
     kernels = {k: {"fetch_bytes_per_launch": round(pf[k][0]), "write_bytes_per_launch": round(pw[k][0]),
                    "hbm_bytes_per_launch": round(pf[k][0] + pw[k][0]), "dispatches": pf[k][1]}
                for k in pf if k in pw}
-    return {"source_hash": source_hash(), "workload": "bf16_n32768_w1024_32q8kv_d128",
+    return {"source_hash": source_hash(), "workload": workload,
             "commands": commands,
             "calibration": {"kernel": cw[0], "bytes_read_and_written": known,
                             "fetch_kib": cf[2], "write_kib": cw[2],
@@ -204,7 +204,7 @@ def main() -> int:
         if args.copy_calibration_mib <= 0:
             print("--traffic-from needs the --copy-calibration-mib of the profiled run", file=sys.stderr)
             return 2
-        t = write_traffic(*args.traffic_from, args.copy_calibration_mib, args.traffic_command)
+        t = write_traffic(*args.traffic_from, args.copy_calibration_mib, args.traffic_command, args.workload)
         with open(TRAFFIC_FILE, "w") as fh:
             json.dump(t, fh, indent=1)
             fh.write("\n")
@@ -288,8 +288,12 @@ def main() -> int:
     # backward 10d, of which dQ's launch does dS K: 2d, and dK/dV's launch
     # Q K^T, dO V^T, P^T dO, dS^T Q: 8d); executed = what the launch runs
     # (dQ also recomputes S and dP: 6d). D = rowsum(dO * O), formed in dQ's
-    # prologue, adds no contraction.
-    algo = {"fwd": (4, 4), "bwd_dq": (2, 6), "bwd_dkdv": (8, 8)}
+    # prologue, adds no contraction. At head_dim 256 the dK/dV launch forms S
+    # twice (a dV pass, then a dK pass: 10d); at 512 the forward and dQ run
+    # four passes of 128 output columns, each recomputing S (and dP), and the
+    # dK/dV passes run four times each (forward 10d, dQ 18d, dK/dV 28d).
+    fwd_x, dq_x, dkdv_x = (4, 6, 8) if d <= 128 else ((4, 6, 10) if d == 256 else (10, 18, 28))
+    algo = {"fwd": (4, fwd_x), "bwd_dq": (2, dq_x), "bwd_dkdv": (8, dkdv_x)}
     kernels = {}
     for n in names:
         counted, executed = algo[n]
@@ -319,7 +323,7 @@ def main() -> int:
                                    "bytes_per_launch": delta_bytes,
                                    "note": "stage API only; attn_bwd forms D inside dQ"}}
     dom = max(("fwd", "bwd_dq", "bwd_dkdv"), key=lambda n: kern_ms[n])
-    traffic = load_traffic(dom)
+    traffic = load_traffic(dom, w.name)
     roofline = {k: v for k, v in kernels[dom].items() if k in ("bound", "achieved", "peak", "unit", "frac")}
     roofline["kernel"] = dom
     roofline["traffic"] = traffic
