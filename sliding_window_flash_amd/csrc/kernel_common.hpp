@@ -79,9 +79,6 @@ template <> __device__ __forceinline__ Frag<float> acc_frag<float>(const f32x16&
   return f;
 }
 
-// Row of a result tile held by register r, for lane half `half`.
-__device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
-
 // ---- element conversion ---------------------------------------------------
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(fp16 x) { return (float)x; }

@@ -160,7 +160,8 @@ SWA_HD uint32_t fast_div(uint32_t n, const FastDiv& f) {  // floor(n / f.d) for 
   return (hi + n) >> f.l;
 }
 
-// Per-cell visibility, used inside edge tiles.
+// Per-cell visibility by the definition. The kernels mask edge tiles with bit
+// runs built from the same rule; the host checks enumerate cells with this.
 SWA_HD bool cell_visible(const SeqGeom& s, int64_t i, int64_t j) {
   if (i >= s.lq || j >= s.lk) return false;
   const int64_t p = i + s.delta();
