@@ -14,12 +14,15 @@
  *   mlx-train-perf README, flash-attention passage: O(N) saved state, the
  *   output and the log-sum-exp, tiles recomputed in the backward).
  *
- *   Visibility. Sequence b has L_q query and L_k key tokens, L_q <= L_k;
- *   query i sits at key position p = i + L_k - L_q. Key j is visible to query
- *   i iff j <= p and p - j < window (causal), or iff |p - j| < window (non-causal:
- *   a two-sided window; any window >= L_k is full attention). window = 1 sees
- *   only the token itself (the lab record's gradient-parity sweep runs windows
- *   causal and not).
+ *   Visibility. Sequence b has L_q query and L_k key tokens; query i sits at
+ *   key position p = i + L_k - L_q (the queries are the last positions). Key j
+ *   is visible to query i iff j <= p and p - j < window (causal), or iff
+ *   |p - j| < window (non-causal: a two-sided window; any window >=
+ *   max(L_q, L_k) is full attention). window = 1 sees only the token itself
+ *   (the lab record's gradient-parity sweep runs windows causal and not).
+ *   With L_q > L_k the first L_q - L_k positions are negative: under the
+ *   causal mask those queries see no key. A query that sees no key gets
+ *   O = 0, LSE = -inf and dQ = 0, and adds nothing to dK and dV.
  *   Key tiles lying wholly outside a query tile's window are skipped; cells on
  *   the window edge are masked ("What did fixing it take?": skip blocks
  *   entirely outside the window, mask the cells at its edge). A query tile's
@@ -54,9 +57,8 @@
  * exception crosses this boundary.
  *
  * Preconditions the host cannot check without reading device memory:
- * cu_seqlens are non-decreasing, every sequence has L_q <= L_k, and
- * L_q <= max_seqlen_q, L_k <= max_seqlen_k. If L_q <= L_k is violated,
- * queries with no visible key get O = 0, LSE = -inf and dQ = 0.
+ * cu_seqlens are non-decreasing, and every sequence has L_q <= max_seqlen_q
+ * and L_k <= max_seqlen_k.
  */
 #ifndef SWA_ATTN_H
 #define SWA_ATTN_H
@@ -82,7 +84,8 @@ typedef enum {
                                2^31 - 1 work items: ceil(max_seqlen / 32) x heads x batch ...) */
   ATTN_ERR_WINDOW = 3,      /* window < 1 */
   ATTN_ERR_UNSUPPORTED = 4, /* head_dim not 64/128 (256, 512: 16-bit dtypes only), unknown dtype, scale <= 0,
-                               a two-sided window with max_seqlen_k > 2^30 */
+                               a two-sided window below max(max_seqlen_q, max_seqlen_k) when that
+                               maximum exceeds 2^30 */
   ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than attn_bwd_workspace_bytes */
   ATTN_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
   ATTN_ERR_ALIGN = 7,       /* a tensor pointer is not 16-byte aligned */
@@ -98,8 +101,8 @@ typedef struct {
   int32_t total_k;      /* cu_seqlens_k[B] */
   int32_t max_seqlen_q; /* >= every L_q; sizes the launch grid (no device reads) */
   int32_t max_seqlen_k; /* >= every L_k */
-  int32_t window;       /* >= 1; any value >= max_seqlen_k (e.g. INT32_MAX) is no window */
-  int32_t causal;       /* 1 causal; 0 two-sided window (full attention if window >= max_seqlen_k) */
+  int32_t window;       /* >= 1; INT32_MAX (or any value >= max(max_seqlen_q, max_seqlen_k)) is no window */
+  int32_t causal;       /* 1 causal; 0 two-sided window (full attention if window >= max(L_q, L_k)) */
   float scale;          /* softmax scale, finite and > 0, e.g. 1/sqrt(head_dim) */
   int32_t dtype;        /* attn_dtype_t */
 } attn_params_t;

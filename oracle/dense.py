@@ -19,8 +19,10 @@ G = Hq / Hkv), query row i and key j:
                parity, small shapes": at window 1 the true gradient is zero).
                Without the causal mask (the same entry sweeps windows "causal
                and not"), the window is two-sided: visible iff |p - j| < w, so
-               w = 1 again sees only the token itself and any w >= L_k sees
-               every key (plain non-causal attention).
+               w = 1 again sees only the token itself and any w >=
+               max(L_q, L_k) sees every key (plain non-causal attention).
+               With more queries than keys the first L_q - L_k positions are
+               negative and the same rules apply as written.
   forward      s_ij = scale * q_i . k_j on visible cells, -inf elsewhere;
                LSE_i = log sum_j exp(s_ij) (natural log); P_ij = exp(s_ij - LSE_i);
                O_i = sum_j P_ij v_j. The saved state is O and LSE (mlx-train-perf
@@ -35,7 +37,9 @@ G = Hq / Hkv), query row i and key j:
                must give every query and key its gradient, including key
                blocks no query visits, whose gradient is zero.)
   empty rows   a query with no visible key gets O = 0, LSE = -inf, dQ = 0
-               (unreachable without a mask when L_q <= L_k).
+               (without a mask only when L_q > L_k: a causal query at a
+               negative position, or a two-sided one more than w - 1 before
+               key 0).
   mask         optional, combined with the window. The lab's "What's not
                proved" list says a window combined with an arbitrary mask still
                falls back to the full score matrix in training; its record

@@ -67,9 +67,12 @@ attn_status_t attn_check_params(const attn_params_t* p) {
       !((p->head_dim == 256 || p->head_dim == 512) && p->dtype != ATTN_F32))
     return ATTN_ERR_UNSUPPORTED;
   if (p->causal != 0 && p->causal != 1) return ATTN_ERR_UNSUPPORTED;
-  // a two-sided window (no causal mask, window < max_seqlen_k) forms p + window
-  // - 1 in 32 bits in the kernels' masks
-  if (p->causal == 0 && p->window < p->max_seqlen_k && p->max_seqlen_k > (1 << 30)) return ATTN_ERR_UNSUPPORTED;
+  // a two-sided window (no causal mask) shorter than the longer of the two
+  // lengths forms p + window - 1 in 32 bits in the kernels' masks
+  {
+    const int32_t lmax = p->max_seqlen_q > p->max_seqlen_k ? p->max_seqlen_q : p->max_seqlen_k;
+    if (p->causal == 0 && p->window < lmax && lmax > (1 << 30)) return ATTN_ERR_UNSUPPORTED;
+  }
   // the kernels fold the scale into exp2 arguments and take row maxima on raw
   // scores, which needs a positive scale
   if (!(p->scale > 0.f) || !isfinite(p->scale)) return ATTN_ERR_UNSUPPORTED;

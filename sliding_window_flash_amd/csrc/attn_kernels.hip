@@ -309,32 +309,37 @@ template <int N> using ic = std::integral_constant<int, N>;
 // key j is visible to the query at key position p iff
 // (unsigned)(mpos - j) < mlim, i.e. j lies in [mpos - mlim + 1, mpos].
 // Causal: mpos = p, mlim = w. Full attention: mpos = L_k - 1, mlim = 2^31 - 1.
-// Two-sided (w < L_k; the C ABI limits L_k to 2^30 so that mpos = p + w - 1
-// fits for every real row): mlim = 2w - 1, and keys at or past L_k (the
-// padding rows of a sequence's last tile) must be masked as well (pad_keys).
-// Only mpos is per lane, so the limit stays in a scalar register.
+// Two-sided (the C ABI limits L_q and L_k to 2^30 so that mpos = p + w - 1
+// fits): mlim = 2w - 1, and keys at or past L_k (the padding rows of a
+// sequence's last tile) must be masked as well (pad_keys). A two-sided window
+// is full attention only when w >= max(L_q, L_k): the positions run from
+// L_k - L_q to L_k - 1, so with more queries than keys (p < 0 for the first
+// rows) |p - j| reaches L_q - 1. A p below zero wraps mpos past every limit
+// when no key is in reach. Only mpos is per lane, so the limit stays in a
+// scalar register.
 struct RowWindow {
   uint32_t mpos, mlim;
   bool pad_keys;
 };
-__device__ __forceinline__ RowWindow row_window(int p, int lk, int window, bool causal) {
+__device__ __forceinline__ RowWindow row_window(int p, int lq, int lk, int window, bool causal) {
   if (causal) return {(uint32_t)p, (uint32_t)window, false};
-  if (window >= lk) return {(uint32_t)(lk - 1), 0x7fffffffu, false};
+  if (window >= max(lq, lk)) return {(uint32_t)(lk - 1), 0x7fffffffu, false};
   return {(uint32_t)p + (uint32_t)(window - 1), 2u * (uint32_t)window - 1u, true};
 }
 
 // The same rule per (query position p, key j) pair for the key-major kernels,
 // where registers run over queries: masked iff windowed and
-// (unsigned)(p - j + off) >= lim. Causal: off 0, lim w. Two-sided (w < L_k):
-// off w - 1, lim 2w - 1. Full attention: not windowed.
+// (unsigned)(p - j + off) >= lim. Causal: off 0, lim w. Two-sided
+// (w < max(L_q, L_k), as above): off w - 1, lim 2w - 1. Full attention: not
+// windowed.
 struct PairWindow {
   bool windowed;
   int off;
   uint32_t lim;
 };
-__device__ __forceinline__ PairWindow pair_window(int lk, int window, bool causal) {
+__device__ __forceinline__ PairWindow pair_window(int lq, int lk, int window, bool causal) {
   if (causal) return {true, 0, (uint32_t)window};
-  if (window >= lk) return {false, 0, 0u};
+  if (window >= max(lq, lk)) return {false, 0, 0u};
   return {true, window - 1, 2u * (uint32_t)window - 1u};
 }
 
@@ -356,7 +361,9 @@ __device__ __forceinline__ uint64_t row_keys_visible(uint32_t mb, uint32_t mlim,
 }
 // Key-major: bit o set iff row ib + o is a real row (< L_q) and, when
 // windowed, (unsigned)(mb + o) < lim (pair_window, mb = ib + L_k - L_q - j +
-// off). L_q and L_k are at most 2^30, so mb and the bounds stay in int range.
+// off). Two-sided windows need L_q, L_k <= 2^30 (the C ABI's limit), so
+// |p - j| and off stay below 2^30; causal ones have off = 0 and |p - j| below
+// the longer length plus 32: mb and the bounds stay in int range.
 __device__ __forceinline__ uint32_t key_rows_visible(int ib, int mb, int lq, const PairWindow& pw) {
   int hi = min(max(lq - ib, 0), 32), lo = 0;
   if (pw.windowed) {
@@ -429,7 +436,7 @@ fwd_kernel(AttnArgs a) {
   crd.init(lane);
   // Edge mask: visible iff (unsigned)(mpos - j) < mlim (row_window). Key rows
   // past L_k in the last tile arrive as zeros and are always masked.
-  const RowWindow rw = row_window(i + (it.lk - it.lq), it.lk, a.window, a.causal != 0);
+  const RowWindow rw = row_window(i + (it.lk - it.lq), it.lq, it.lk, a.window, a.causal != 0);
   const uint32_t mpos = rw.mpos, mlim = rw.mlim;
 
   const float c = a.scale * kLog2e;
@@ -777,7 +784,7 @@ bwd_dq_kernel(AttnArgs a) {
   rrd.init(l32, half);
   ColReader<T, D> crd;
   crd.init(lane);
-  const RowWindow rw = row_window(i + (it.lk - it.lq), it.lk, a.window, a.causal != 0);
+  const RowWindow rw = row_window(i + (it.lk - it.lq), it.lq, it.lk, a.window, a.causal != 0);
   const uint32_t mpos = rw.mpos, mlim = rw.mlim;
   const float c = a.scale * kLog2e;
 
@@ -958,7 +965,7 @@ bwd_dkdv_kernel(AttnArgs a) {
     dva[dt] = f32x16{};
   }
   const float c = a.scale * kLog2e;
-  const PairWindow pw = pair_window(lk, a.window, causal);
+  const PairWindow pw = pair_window(lq, lk, a.window, causal);
   const T* __restrict__ Qg = static_cast<const T*>(a.q);
   const T* __restrict__ Dg = static_cast<const T*>(a.dout);
 
@@ -1223,7 +1230,7 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
   ColReader<T, D> crd;
   crd.init(lane);
   const float c = a.scale * kLog2e;
-  const PairWindow pw = pair_window(lk, a.window, causal);
+  const PairWindow pw = pair_window(lq, lk, a.window, causal);
   const T* __restrict__ Qg = static_cast<const T*>(a.q);
   const T* __restrict__ Dg = static_cast<const T*>(a.dout);
 
@@ -1451,7 +1458,7 @@ __global__ void __launch_bounds__(BN * 2) bwd_dkdv4_kernel(AttnArgs a) {
   }
   const float c = a.scale * kLog2e;
   const bool causal = a.causal != 0;
-  const PairWindow pw = pair_window(lk, a.window, causal);
+  const PairWindow pw = pair_window(lq, lk, a.window, causal);
   const T* __restrict__ Qg = static_cast<const T*>(a.q);
   const T* __restrict__ Dg = static_cast<const T*>(a.dout);
 

@@ -13,10 +13,11 @@ int main() {
   long checked = 0, bad = 0;
   const int wins[] = {1, 2, 3, 5, 31, 32, 33, 64, 127, 128, 129, 1000, 2147483647};
   for (int lq = 0; lq <= 140; lq += 7)
-    for (int dl = 0; dl <= 70; dl += 35)
+    for (int dl = -70; dl <= 70; dl += 35)
       for (int w : wins)
         for (int causal = 0; causal <= 1; ++causal) {
           const int lk = lq + dl;
+          if (lk < 0) continue;
           const swa::SeqGeom g{lq, lk, w, causal != 0};
           for (int bm : {16, 32, 64})
             for (int bn : {16, 32, 64, 128})
@@ -36,10 +37,11 @@ int main() {
   // block_masked against cell-by-cell enumeration (the kernels' per-wave skip)
   long bchecked = 0, bbad = 0;
   for (int lq = 1; lq <= 140; lq += 9)
-    for (int dl = 0; dl <= 70; dl += 35)
+    for (int dl = -70; dl <= 70; dl += 35)
       for (int w : wins)
         for (int causal = 0; causal <= 1; ++causal) {
           const int lk = lq + dl;
+          if (lk < 0) continue;
           const swa::SeqGeom g{lq, lk, w, causal != 0};
           for (int rows : {32})
             for (int cols : {32, 64})
@@ -65,10 +67,11 @@ int main() {
   // key_tile_full_query_tiles == tile_full_i32, for every query tile
   long ichecked = 0, ibad = 0;
   for (int lq = 0; lq <= 200; lq += 7)
-    for (int dl : {0, 1, 37, 130})
+    for (int dl : {-130, -37, -1, 0, 1, 37, 130})
       for (int w : wins)
         for (int causal = 0; causal <= 1; ++causal) {
           const int lk = lq + dl;
+          if (lk < 0) continue;
           const swa::SeqGeom g{lq, lk, w, causal != 0};
           for (int bm : {32, 64})
             for (int bn : {32, 64, 128})

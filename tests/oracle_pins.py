@@ -24,7 +24,12 @@ AssertionError if the module disagrees with:
     mask changes nothing; a block-diagonal (document) mask equals running the
     documents as separate packed sequences; the causal lower triangle as a
     mask on a two-sided window equals the causal window; a row with no
-    visible key has O = 0, LSE = -inf and no gradient.
+    visible key has O = 0, LSE = -inf and no gradient,
+  * more queries than keys (the first L_q - L_k queries sit at negative
+    positions): finite differences and the brute-force loop, causal and
+    two-sided; under the causal mask those rows see no key and the others
+    equal a run with only the last L_k queries; a two-sided window is full
+    attention only from max(L_q, L_k) on.
 """
 from __future__ import annotations
 
@@ -415,10 +420,74 @@ def pin_mask_empty_rows(ref):
     _close(out["o"][live], full["o"][live], 1e-13, "live rows unchanged")
 
 
+LONG_Q_CASES = [
+    # (lengths_q, lengths_k, heads_q, heads_kv, head_dim, window, causal)
+    ([7, 4], [4, 6], 2, 1, 2, 3, True),
+    ([7, 4], [4, 6], 2, 1, 2, INT32_MAX, True),
+    ([7, 4], [4, 6], 2, 1, 2, 5, False),    # window >= L_k but < L_q
+    ([6, 3], [2, 3], 2, 1, 2, 2, False),
+]
+
+
+def pin_more_queries_than_keys(ref):
+    """L_q > L_k: query i sits at key position i + L_k - L_q, negative for the
+    first L_q - L_k rows."""
+    for n, (lq, lk, hq, hkv, d, win, causal) in enumerate(LONG_Q_CASES):
+        w = small_case(lq, lk, heads_q=hq, heads_kv=hkv, head_dim=d, window=win,
+                       causal=causal, seed=300 + n)
+        x = make_inputs(w)
+        out = _call(ref, w, x)
+        num = fd.grads(x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale,
+                       w.window, w.causal, forward=ref.sdpa_reference)
+        for g in ("dq", "dk", "dv"):
+            _close(out[g], num[g], 1e-8, f"L_q > L_k finite differences {g} case {n}")
+        bf = loop.sdpa_loop(x["q"], x["k"], x["v"], x["do"], x["cu_q"], x["cu_k"], w.scale,
+                            w.window, w.causal)
+        for key in ("o", "lse", "delta", "dq", "dk", "dv"):
+            scale = max(1.0, float(np.max(np.abs(bf[key][np.isfinite(bf[key])]), initial=0)))
+            _close(out[key], bf[key], 1e-12 * scale, f"L_q > L_k loop {key} case {n}")
+    # causal: the rows at negative positions see nothing; the others are the
+    # same run with only the last L_k queries of each sequence
+    w = small_case([9, 4], [5, 6], heads_q=2, heads_kv=1, head_dim=3, window=3, seed=310)
+    x = make_inputs(w)
+    out = _call(ref, w, x)
+    dead, live, cu = [], [], [0]
+    for b in range(w.batch):
+        q0, lq, lk = int(x["cu_q"][b]), w.lengths_q[b], w.lengths_k[b]
+        cut = max(lq - lk, 0)
+        dead += list(range(q0, q0 + cut))
+        live += list(range(q0 + cut, q0 + lq))
+        cu.append(cu[-1] + lq - cut)
+    assert dead, "the case must have rows at negative positions"
+    suf = _call(ref, w, x, q=x["q"][live], do=x["do"][live], cu_q=np.array(cu, np.int32))
+    _close(out["o"][dead], np.zeros_like(out["o"][dead]), 0.0, "negative position: O = 0")
+    assert np.all(out["lse"][:, dead] == -np.inf), "negative position: LSE = -inf"
+    _close(out["dq"][dead], np.zeros_like(out["dq"][dead]), 0.0, "negative position: dQ = 0")
+    _close(out["o"][live], suf["o"], 1e-13, "live rows = the last L_k queries alone: O")
+    _close(out["lse"][:, live], suf["lse"], 1e-13, "live rows = the last L_k queries alone: LSE")
+    _close(out["dq"][live], suf["dq"], 1e-13, "live rows = the last L_k queries alone: dQ")
+    for key in ("dk", "dv"):
+        _close(out[key], suf[key], 1e-13, f"rows at negative positions add no {key}")
+    # two-sided: full attention from w = max(L_q, L_k) = 9 on; at w = L_k = 5
+    # the query at position -4 sees keys 0 .. 0 only, not all five
+    w = small_case([9], [5], heads_q=1, heads_kv=1, head_dim=3, window=9, causal=False, seed=311)
+    x = make_inputs(w)
+    full = _call(ref, w, x, window=INT32_MAX)
+    a = _call(ref, w, x)
+    for key in a:
+        assert np.array_equal(a[key], full[key]), f"two-sided window max(L_q, L_k) vs full {key}"
+    b = _call(ref, w, x, window=5)
+    row0 = ref.sdpa_reference(x["q"][:1], x["k"][:1], x["v"][:1], x["do"][:1],
+                              np.array([0, 1], np.int32), np.array([0, 1], np.int32), w.scale,
+                              INT32_MAX, False)
+    _close(b["o"][0], row0["o"][0], 1e-13, "two-sided w = L_k: the row at -4 sees key 0 only")
+    assert not np.allclose(b["o"][0], full["o"][0]), "two-sided w = L_k < L_q is not full attention"
+
+
 ALL_PINS = [pin_finite_differences, pin_loop, pin_window_one, pin_scale_zero,
             pin_hand_example, pin_softmax_rows, pin_shift_identities, pin_gqa_is_repeated_mha,
             pin_packed_is_concatenation, pin_window_is_local, pin_wide_window_is_causal,
             pin_two_sided_window_one, pin_two_sided_flip, pin_two_sided_is_local,
             pin_wide_two_sided_is_full, pin_mask_finite_differences, pin_mask_loop,
             pin_mask_all_allowed, pin_mask_documents_are_sequences,
-            pin_mask_lower_triangle_is_causal, pin_mask_empty_rows]
+            pin_mask_lower_triangle_is_causal, pin_mask_empty_rows, pin_more_queries_than_keys]

@@ -59,6 +59,12 @@ def good(**kw):
     (dict(causal=False, window=50), 0),     # two-sided window
     (dict(heads_q=1, heads_kv=1, total_q=2**30 + 8, total_k=2**30 + 8, max_seqlen_q=2**30 + 8,
           max_seqlen_k=2**30 + 8, causal=False, window=50), 4),  # two-sided beyond 2^30 keys
+    (dict(heads_q=1, heads_kv=1, total_q=2**30 + 8, total_k=64, max_seqlen_q=2**30 + 8,
+          max_seqlen_k=64, causal=False, window=100), 4),  # two-sided beyond 2^30 queries
+    (dict(heads_q=1, heads_kv=1, total_q=2**30 + 8, total_k=64, max_seqlen_q=2**30 + 8,
+          max_seqlen_k=64, causal=False, window=2**30 + 8), 0),  # full attention: no limit
+    (dict(heads_q=1, heads_kv=1, total_q=2**30 + 8, total_k=64, max_seqlen_q=2**30 + 8,
+          max_seqlen_k=64, causal=True, window=100), 0),  # causal: no limit
     (dict(causal=False, window=100), 0),
     (dict(window=swa.INT32_MAX), 0),
     (dict(dtype=swa.ATTN_F32, head_dim=64), 0),

@@ -6,8 +6,8 @@ mask cell o of the lane's block by bit o. This test compiles exactly that part
 of the kernel source with g++, expands the bits into the cells the kernels'
 register layout assigns them (offset 32 kt + 8 (r / 4) + r % 4 from the lane's
 base, lanes of both halves), and compares every cell with the oracle's
-visibility matrix: causal, two-sided and full windows, L_q < L_k, ragged
-tails. Padding cells (keys past L_k in a query-major tile, rows past L_q in a
+visibility matrix: causal, two-sided and full windows, L_q < L_k and L_q > L_k,
+ragged tails. Padding cells (keys past L_k in a query-major tile, rows past L_q in a
 key-major block) must come out masked, since their operands arrive as zeros."""
 import ctypes
 import os
@@ -39,7 +39,7 @@ extern "C" {
 void qm_cells(int lq, int lk, int window, int causal, uint8_t* out) {
   const int nkb = (lk + 63) / 64, ld = nkb * 64;
   for (int i = 0; i < lq; ++i) {
-    const RowWindow rw = row_window(i + lk - lq, lk, window, causal != 0);
+    const RowWindow rw = row_window(i + lk - lq, lq, lk, window, causal != 0);
     for (int kb = 0; kb < nkb; ++kb)
       for (int half = 0; half < 2; ++half) {
         const int jb = kb * 64 + 4 * half;
@@ -54,7 +54,7 @@ void qm_cells(int lq, int lk, int window, int causal, uint8_t* out) {
 }
 // key-major (dK/dV): 32-row query blocks; out[i * lk + j], keys j < lk, rows i < nqb * 32
 void km_cells(int lq, int lk, int window, int causal, uint8_t* out) {
-  const PairWindow pw = pair_window(lk, window, causal != 0);
+  const PairWindow pw = pair_window(lq, lk, window, causal != 0);
   const int nqb = (lq + 31) / 32;
   for (int j = 0; j < lk; ++j)
     for (int qb = 0; qb < nqb; ++qb)
@@ -98,6 +98,9 @@ CASES = [
     (70, 333, 40, True), (5, 300, 3, True), (1, 97, 97, True), (257, 257, 128, True),
     (200, 200, 1, False), (200, 200, 33, False), (200, 200, 100, False), (70, 333, 40, False),
     (130, 190, INT32_MAX, False), (190, 190, 189, False), (190, 190, 190, False), (64, 300, 65, False),
+    # more queries than keys: the first L_q - L_k rows sit at negative positions
+    (400, 100, 64, True), (300, 50, INT32_MAX, True), (130, 1, 1, True), (257, 200, 33, True),
+    (300, 50, 64, False), (300, 50, 250, False), (97, 5, 3, False), (200, 130, INT32_MAX, False),
 ]
 
 

@@ -37,6 +37,9 @@ CASES = [
     # head_dim 512: 32-key forward / dQ tiles, one mask word per row and tile
     ([150, 45], [160, 90], 4, 2, 512, 70, True, "bf16", 0.6, 2),
     ([211], None, 2, 1, 512, 90, False, "fp16", 0.4, 1),
+    # more queries than keys (negative positions)
+    ([330, 60], [90, 100], 4, 2, 128, 50, True, "bf16", 0.6, 2),
+    ([330, 60], [90, 100], 2, 1, 64, 120, False, "f32", 0.7, 1),
 ]
 
 

@@ -95,6 +95,8 @@ CASES = [
     ([150, 45], [160, 90], 2, 1, 256, 70, True, "bf16", "documents"),
     ([600], None, 4, 2, 512, 300, True, "fp16", "documents"),
     ([900, 200], None, 8, 2, 128, INT32_MAX, True, "bf16", "band"),
+    ([400, 90], [100, 300], 4, 2, 128, 64, True, "bf16", "random"),      # L_q > L_k
+    ([300, 77], [50, 80], 2, 1, 64, 60, False, "f32", "random"),
 ]
 
 

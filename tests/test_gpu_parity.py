@@ -75,6 +75,15 @@ SMALL = [
     ([200, 333], None, 4, 2, 512, INT32_MAX, False, "bf16"),
     ([257, 130], None, 4, 2, 512, 100, False, "fp16"),
     ([300, 77], None, 3, 1, 512, 100, True, "bf16"),
+    # more queries than keys: the first L_q - L_k rows sit at negative positions
+    # (causal: no key at all; two-sided: a window of at least L_k but below L_q
+    # is not full attention); a sequence with queries and no keys
+    ([400, 90], [100, 300], 4, 2, 128, 64, True, "bf16"),
+    ([400, 90], [100, 300], 4, 2, 128, 150, False, "bf16"),
+    ([300, 77], [50, 80], 2, 1, 64, 60, False, "f32"),
+    ([300, 77], [50, 80], 4, 2, 256, 100, False, "fp16"),
+    ([257, 40], [60, 300], 4, 2, 512, 70, True, "bf16"),
+    ([200, 50], [0, 80], 4, 2, 128, 30, True, "bf16"),
 ]
 
 

@@ -26,6 +26,9 @@ MUTANTS = {
     "two-sided window one-sided": ("vis = np.abs(pos - j[None, :]) < window", "vis = (pos - j[None, :]) < window"),
     "two-sided window one key wider": ("vis = np.abs(pos - j[None, :]) < window",
                                        "vis = np.abs(pos - j[None, :]) <= window"),
+    "two-sided window >= L_k taken as full attention": (
+        "vis = np.abs(pos - j[None, :]) < window",
+        "vis = (np.abs(pos - j[None, :]) < window) | (window >= lk)"),
     "mask ignored": ("vis = vis & np.asarray(allowed, dtype=bool)[:, c0:c1]", "vis = vis"),
     "mask rows not offset by the sequence start": ("mask[q0 + np.asarray(rows, dtype=np.int64)]",
                                                    "mask[np.asarray(rows, dtype=np.int64)]"),

@@ -110,7 +110,8 @@ def test_row_and_head_sample_matches_full_reference():
     assert np.all(part["o"][:, [0, 1, 3]] == 0)
 
 
-@pytest.mark.parametrize("lq,lk", [(300, 300), (40, 300), (1, 1), (7, 200), (0, 5), (513, 600)])
+@pytest.mark.parametrize("lq,lk", [(300, 300), (40, 300), (1, 1), (7, 200), (0, 5), (513, 600),
+                                   (300, 40), (64, 1), (5, 0)])
 @pytest.mark.parametrize("window", [1, 2, 31, 64, 129, 700, INT32_MAX])
 @pytest.mark.parametrize("causal", [True, False])
 def test_key_band_holds_every_visible_cell(lq, lk, window, causal):
@@ -139,6 +140,8 @@ def test_key_band_holds_every_visible_cell(lq, lk, window, causal):
     ([257], None, 2, 2, 8, 1, True),                # window 1
     ([257, 90], None, 2, 1, 8, INT32_MAX, True),    # plain causal
     ([200, 333], None, 2, 1, 8, INT32_MAX, False),  # full attention
+    ([300, 90], [100, 300], 4, 2, 8, 40, True),     # more queries than keys
+    ([300, 90], [100, 300], 4, 2, 8, 150, False),   # the same, two-sided
 ])
 @pytest.mark.parametrize("masked", [False, True])
 def test_band_reference_matches_full_reference(case, masked):

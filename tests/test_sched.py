@@ -38,6 +38,9 @@ CASES = [
     # two-sided windows (no causal mask)
     (300, 300, 1, False), (300, 300, 64, False), (300, 300, 129, False), (100, 700, 64, False),
     (5, 400, 3, False), (200, 260, 100, False), (129, 129, 128, False),
+    # more queries than keys (negative positions), and queries without keys
+    (400, 100, 64, True), (300, 50, INT32_MAX, True), (130, 1, 1, True), (50, 0, 8, True),
+    (300, 50, 64, False), (300, 50, 250, False), (97, 5, 3, False), (50, 0, 8, False),
 ]
 
 
