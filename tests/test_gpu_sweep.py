@@ -23,11 +23,13 @@ WINDOWS = (1, 2, 7, 31, 64, 100, 128, 129, 300, 1000, INT32_MAX)
 LONG_WINDOWS = (1000, 2000, 5000)
 
 
-def _grid(n=60, seed=2024):
+def _grid(n=60, seed=2024, longer_q=False):
     """The record's grid: head dims 64 to 512, windows 1 to 5,000 (and none),
     grouped-query ratios, queries shorter than keys, causal and not. One case
     in ten is a single long sequence (1,500 to 6,000 tokens) under a window of
-    1,000 to 5,000, so that the long windows bite."""
+    1,000 to 5,000, so that the long windows bite. ``longer_q``: the cases
+    with unequal lengths get more queries than keys instead (down to no key),
+    beyond the record's grid."""
     rng = np.random.default_rng(seed)
     cases = []
     while len(cases) < n:
@@ -48,6 +50,8 @@ def _grid(n=60, seed=2024):
         lq = [int(x) for x in rng.integers(1, 400, nseq)]
         shorter = rng.random() < 0.35          # queries shorter than keys
         lk = [q + int(rng.integers(1, 200)) for q in lq] if shorter else None
+        if shorter and longer_q:
+            lk = [max(0, q - int(rng.integers(1, 200))) for q in lq]
         causal = rng.random() < 0.7
         window = int(WINDOWS[rng.integers(len(WINDOWS))])   # without causal: two-sided
         cases.append((tuple(lq), None if lk is None else tuple(lk), hkv * g, hkv, d, window, causal, dt))
@@ -55,8 +59,10 @@ def _grid(n=60, seed=2024):
 
 
 # SWA_SWEEP_CASES / SWA_SWEEP_SEED widen the draw for a longer run (3,000 cases
-# take about two minutes on one GPU); the default is the fixed 60-case draw
-CASES = _grid(int(os.environ.get("SWA_SWEEP_CASES", "60")), int(os.environ.get("SWA_SWEEP_SEED", "2024")))
+# take about two minutes on one GPU); the default is the fixed 60-case draw.
+# SWA_SWEEP_LONGER_Q=1 draws more queries than keys where lengths differ.
+CASES = _grid(int(os.environ.get("SWA_SWEEP_CASES", "60")), int(os.environ.get("SWA_SWEEP_SEED", "2024")),
+              os.environ.get("SWA_SWEEP_LONGER_Q", "0") == "1")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -95,7 +101,7 @@ def test_sweep_case(case):
     # dtype's half unit of rounding of the outputs. Windows below 7 keep only
     # a handful of terms per row, where a relative error says little (window 1
     # has exact-zero dQ and dK).
-    if RULE_MIN_WINDOW <= win < max(w.lengths_k):
+    if RULE_MIN_WINDOW <= win < max(max(w.lengths_q), max(w.lengths_k)):
         plain_w = w.replace(window=INT32_MAX)
         base = H.compare_full(plain_w, x, H.run_hip(plain_w, dev), scale_f32=True)
         floor = HALF_ULP[dt]
