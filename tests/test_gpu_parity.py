@@ -95,6 +95,26 @@ def test_small_cases_full_oracle(case):
     _run_full(w)
 
 
+# Softmax scales away from 1/sqrt(d): near-uniform rows (0.02) and sharp ones
+# (2 and 6: score ranges of hundreds in log2 units, so the running reference
+# max moves often and most probabilities underflow to 0). dQ and dK carry the
+# scale as a factor, so dO shrinks by the scale's ratio to 1/sqrt(d): the
+# gradients stay of the size the absolute bars are set for (bf16 itself has a
+# half unit of 0.016 at magnitude 4 and 0.03 at 8).
+@pytest.mark.parametrize("dt,d,scale,causal", [
+    ("bf16", 128, 0.02, True), ("bf16", 128, 2.0, True), ("bf16", 64, 6.0, False),
+    ("fp16", 128, 2.0, True), ("f32", 64, 2.0, True), ("bf16", 256, 2.0, True), ("fp16", 512, 0.5, False),
+])
+def test_softmax_scales(dt, d, scale, causal):
+    w = small_case([300, 77], [333, 77], heads_q=4, heads_kv=2, head_dim=d, window=100, causal=causal,
+                   dtype=dt, scale=scale, do_scale=0.1 * min(1.0, d ** -0.5 / scale), seed=37)
+    H.say(f"scale case: {dt} d={d} scale={scale} causal={causal}")
+    x = make_inputs(w)
+    got = H.run_hip(w, H.to_device(w, x))
+    stats = H.compare_full(w, x, got, scale_f32=True)
+    H.say("  ", {k: {kk: f"{vv:.2e}" for kk, vv in v.items()} for k, v in stats.items()})
+
+
 @pytest.mark.parametrize("dt,d", [("bf16", 128), ("fp16", 64), ("bf16", 256), ("f32", 64), ("fp16", 512)])
 def test_window_one_closed_form(dt, d):
     w = small_case([300, 130], [300, 200], heads_q=4, heads_kv=2, head_dim=d, window=1, dtype=dt,
