@@ -196,6 +196,19 @@ def test_stages_run_separately(dt, d, order):
     H.compare_full(w, x, dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv))
 
 
+@pytest.mark.parametrize("dt,d,causal", [("bf16", 64, True), ("f32", 128, False), ("fp16", 256, True)])
+def test_many_short_sequences(dt, d, causal):
+    """300 packed sequences of 0 to 70 tokens (many empty, some with more
+    queries than keys): the launch-id decode over a large batch, sequences
+    that end inside a tile, and work items past a sequence's end."""
+    rng = np.random.default_rng(41)
+    lq = [0 if rng.random() < 0.2 else int(rng.integers(1, 71)) for _ in range(300)]
+    lk = [max(0, q + int(rng.integers(-8, 30))) for q in lq]
+    w = small_case(lq, lk, heads_q=4, heads_kv=2, head_dim=d, window=24, causal=causal, dtype=dt,
+                   do_scale=1.0 if dt == "f32" else 0.1, seed=42)
+    _run_full(w)
+
+
 def test_gqa_2k_full_oracle():
     _run_full(W.GQA_2K)
 
