@@ -1044,6 +1044,7 @@ bwd_dkdv_kernel(AttnArgs a) {
     // barrier
     const bool work = !edge || (seen_q.lo <= qb && qb <= seen_q.hi);
     f32x16 s, dp;  // set and read only when `work`
+    f32x4 lsv[4];  // LSE * log2(e) of this lane's 16 query rows
     if (work) {
     s = f32x16{};
     // dP - D: the dP accumulator starts at -D of its rows (the workspace holds
@@ -1074,16 +1075,14 @@ bwd_dkdv_kernel(AttnArgs a) {
       apply_col_mask(s, words, l32);
     }
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int rr = 32 * mh + 8 * r4 + 4 * half;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + rr);
+    for (int r4 = 0; r4 < 4; ++r4) lsv[r4] = *reinterpret_cast<const f32x4*>(lse2s + 32 * mh + 8 * r4 + 4 * half);
+    // P and dS = P (dP - D) of the first 16 query rows (registers 0..7) now;
+    // the other 16 are formed between the first half's dV / dK MFMAs below
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * r4 + e;
-        const float pv = fast_exp2(fmaf(s[r], c, -l4[e]));
-        s[r] = pv;
-        dp[r] = pv * dp[r];  // dS = P (dP - D)
-      }
+    for (int r = 0; r < 8; ++r) {
+      const float pv = fast_exp2(fmaf(s[r], c, -lsv[r >> 2][r & 3]));
+      s[r] = pv;
+      dp[r] = pv * dp[r];
     }
     }
     // the next step's stage is filled here, after this step's row reads and
@@ -1091,16 +1090,43 @@ bwd_dkdv_kernel(AttnArgs a) {
     // row reads every wave makes (moving them here cut dK/dV time by 4%)
     if (t + 1 < steps) fill(stage ? st0 : st1);
     if (work) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const Frag<T> pf = acc_frag<T>(s, u);
-      const Frag<T> dsf = acc_frag<T>(dp, u);
+      // The two waves sharing a SIMD (the two query halves of one key block)
+      // run the same phases at the same time, so a softmax that follows all
+      // of the S / dP MFMAs finds the matrix core idle. Here each MFMA pair of
+      // the first 16 rows is followed by the exp2, FMA and multiply of two
+      // cells of the last 16, in one wave's instruction stream, so that they
+      // issue while the matrix core works (scheduling fences keep the order;
+      // each chunk reads the next chunk's operands first). dK/dV 3.3-4.5%
+      // faster in four interleaved A/B runs, outputs bitwise equal.
+      const Frag<T> pf0 = acc_frag<T>(s, 0);
+      const Frag<T> dsf0 = acc_frag<T>(dp, 0);
+      Frag<T> a0 = crd.read(dos, 32 * mh, 0), b0 = crd.read(qs, 32 * mh, 0);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        mma(dva[dt], crd.read(dos, 32 * mh + 16 * u, dt), pf);
-        mma(dka[dt], crd.read(qs, 32 * mh + 16 * u, dt), dsf);
+        // the next chunk's operands; after the last, the second half's first
+        const int row1 = dt + 1 < D / 32 ? 32 * mh : 32 * mh + 16;
+        const int dt1 = dt + 1 < D / 32 ? dt + 1 : 0;
+        const Frag<T> a1 = crd.read(dos, row1, dt1), b1 = crd.read(qs, row1, dt1);
+        mma(dva[dt], a0, pf0);
+        mma(dka[dt], b0, dsf0);
+#pragma unroll
+        for (int e2 = 0; e2 < 8 / (D / 32); ++e2) {
+          const int r = 8 + (8 / (D / 32)) * dt + e2;
+          const float pv = fast_exp2(fmaf(s[r], c, -lsv[r >> 2][r & 3]));
+          s[r] = pv;
+          dp[r] = pv * dp[r];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        a0 = a1;
+        b0 = b1;
       }
-    }
+      const Frag<T> pf1 = acc_frag<T>(s, 1);
+      const Frag<T> dsf1 = acc_frag<T>(dp, 1);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        mma(dva[dt], dt == 0 ? a0 : crd.read(dos, 32 * mh + 16, dt), pf1);
+        mma(dka[dt], dt == 0 ? b0 : crd.read(qs, 32 * mh + 16, dt), dsf1);
+      }
     }
     if (++qb > qr.hi) qb = qr.lo;
     __syncthreads();
