@@ -818,15 +818,8 @@ bwd_dq_kernel(AttnArgs a) {
     const bool edge = !(kr.full_lo <= kb && kb <= kr.full_hi);
     uint32_t mw[BN / 32] = {};
     if constexpr (M) row_mask_words(a, mrow, row_ok, kb, mw);
-#pragma unroll
-    for (int kt = 0; kt < BN / 32; ++kt) {
-      f32x16 s = f32x16{}, dp = ndlt;
-      // the mask test is skipped when the whole wave's words for this block are all ones
-#pragma unroll
-      for (int ss = 0; ss < D / 16; ++ss) {
-        mma(s, rrd.read(ks, 32 * kt, ss), qf[ss]);
-        mma(dp, rrd.read(vs, 32 * kt, ss), df[ss]);
-      }
+    // the edge mask and (with M) the caller's mask on key block kt's scores
+    auto mask_block = [&](f32x16& s, int kt) __attribute__((always_inline)) {
       if (edge) {
         const int jb = kb * BN + 32 * kt + 4 * half;  // two-sided: the keys past L_k are masked as well
         uint32_t vis = (uint32_t)row_keys_visible(mpos - (uint32_t)jb, mlim, rw.pad_keys ? max(it.lk - jb, 0) : -1);
@@ -837,9 +830,89 @@ bwd_dq_kernel(AttnArgs a) {
         if constexpr (D > 256) asm volatile("" : "+v"(vis));
         apply_visible(s, vis);
       }
+      // the mask test is skipped when the whole wave's words for this block are all ones
       if constexpr (M) {
         if (!__all(mw[kt] == 0xFFFFFFFFu)) apply_row_mask(s, mw[kt], half);
       }
+    };
+    if constexpr (BN / 32 == 2 && D > 128) {
+      // One wave per SIMD (head_dim 256): no second wave's MFMAs hide the
+      // softmax, so this wave overlaps it with its own MFMAs. Key block 1's S
+      // and dP MFMAs issue with block 0's softmax between them, and the dQ
+      // MFMAs of block 0 with block 1's softmax between them; scheduling
+      // fences keep that order, and each chunk reads the next chunk's
+      // operands first. (At head_dim 128 two waves share a SIMD and this
+      // gained nothing.)
+      f32x16 s0 = f32x16{}, dp0 = ndlt, s1 = f32x16{}, dp1 = ndlt;
+#pragma unroll
+      for (int ss = 0; ss < D / 16; ++ss) {
+        mma(s0, rrd.read(ks, 0, ss), qf[ss]);
+        mma(dp0, rrd.read(vs, 0, ss), df[ss]);
+      }
+      mask_block(s0, 0);
+      {
+        Frag<T> x0 = rrd.read(ks, 32, 0), y0 = rrd.read(vs, 32, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ss = 0; ss < D / 16; ++ss) {
+          Frag<T> x1 = x0, y1 = y0;
+          if (ss + 1 < D / 16) {
+            x1 = rrd.read(ks, 32, ss + 1);
+            y1 = rrd.read(vs, 32, ss + 1);
+          }
+          mma(s1, x0, qf[ss]);
+          mma(dp1, y0, df[ss]);
+#pragma unroll
+          for (int e2 = 0; e2 < 16 / (D / 16); ++e2) {
+            const int r = (16 / (D / 16)) * ss + e2;
+            const float pv = fast_exp2(fmaf(s0[r], c, -lse2));
+            s0[r] = pv * dp0[r];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          x0 = x1;
+          y0 = y1;
+        }
+      }
+      mask_block(s1, 1);
+      {
+        const Frag<T> d00 = acc_frag<T>(s0, 0), d01 = acc_frag<T>(s0, 1);
+        Frag<T> z0 = crd.read(ks, 0, pass * (DO / 32));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < 2 * (DO / 32); ++k) {
+          const int u = k / (DO / 32), dt = k % (DO / 32);
+          Frag<T> z1 = z0;
+          if (k + 1 < 2 * (DO / 32)) {
+            const int u1 = (k + 1) / (DO / 32), dt1 = (k + 1) % (DO / 32);
+            z1 = crd.read(ks, 16 * u1, pass * (DO / 32) + dt1);
+          }
+          mma(acc[dt], z0, u ? d01 : d00);
+#pragma unroll
+          for (int e2 = 0; e2 < 16 / (2 * (DO / 32)); ++e2) {
+            const int r = (16 / (2 * (DO / 32))) * k + e2;
+            const float pv = fast_exp2(fmaf(s1[r], c, -lse2));
+            s1[r] = pv * dp1[r];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          z0 = z1;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const Frag<T> dsf = acc_frag<T>(s1, u);
+#pragma unroll
+        for (int dt = 0; dt < DO / 32; ++dt) mma(acc[dt], crd.read(ks, 32 + 16 * u, pass * (DO / 32) + dt), dsf);
+      }
+    } else
+#pragma unroll
+    for (int kt = 0; kt < BN / 32; ++kt) {
+      f32x16 s = f32x16{}, dp = ndlt;
+#pragma unroll
+      for (int ss = 0; ss < D / 16; ++ss) {
+        mma(s, rrd.read(ks, 32 * kt, ss), qf[ss]);
+        mma(dp, rrd.read(vs, 32 * kt, ss), df[ss]);
+      }
+      mask_block(s, kt);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pv = fast_exp2(fmaf(s[r], c, -lse2));
@@ -1297,9 +1370,14 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
   __syncthreads();
 
   int qb = qr.lo;  // query tile of the current step
-  // S for this wave's 32 keys against the stage's 32 query rows, masked and
-  // turned into P (fp32); returns false when the whole block is masked
-  auto probs = [&](const char* qs, f32x16& s) -> bool {
+  // S for this wave's 32 keys against the stage's 32 query rows, masked, and
+  // the rows' LSE * log2(e); returns false when the whole block is masked.
+  // The exp2 that turns S into P is left to the passes: with one wave per
+  // SIMD nothing else hides the softmax, so each pass issues it between its
+  // own MFMAs (the dV pass between the MFMAs of the first 16 rows, the dK
+  // pass beside the dP MFMAs, which do not need P), ordered by scheduling
+  // fences, with the next operand read issued first.
+  auto scores = [&](const char* qs, f32x16& s, f32x4 (&lsv)[4]) -> bool {
     const bool edge = !tile_full_i32(lq, lk, a.window, causal, qb, BM, kb, BN);
     if (edge && block_masked(lq, lk, a.window, causal, qb * BM, BM, kb * BN + 32 * w, 32)) return false;
     s = f32x16{};
@@ -1319,11 +1397,7 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
     }
     const float* lse2s = reinterpret_cast<const float*>(qs + 2 * QTile::kBytes);
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + 8 * r4 + 4 * half);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s[4 * r4 + e] = fast_exp2(fmaf(s[4 * r4 + e], c, -l4[e]));
-    }
+    for (int r4 = 0; r4 < 4; ++r4) lsv[r4] = *reinterpret_cast<const f32x4*>(lse2s + 8 * r4 + 4 * half);
     return true;
   };
   auto next = [&]() {  // end of a step: advance the query tile, meet the stage barrier
@@ -1358,13 +1432,28 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
       const char* dos = qs + QTile::kBytes;
       if (t + 1 < total) fill(stage ? st0 : st1);
       f32x16 s;
-      if (probs(qs, s)) {
+      f32x4 lsv[4];
+      if (scores(qs, s, lsv)) {
+        // P of the first 16 rows; the last 16 rows' exp2 issue between the
+        // first half's MFMAs (a cell per chunk at 256 output columns, two
+        // at 128)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const Frag<T> pf = acc_frag<T>(s, u);
+        for (int r = 0; r < 8; ++r) s[r] = fast_exp2(fmaf(s[r], c, -lsv[r >> 2][r & 3]));
+        const Frag<T> pf0 = acc_frag<T>(s, 0);
+        Frag<T> a0 = crd.read(dos, 0, h * (DA / 32));
 #pragma unroll
-          for (int dt = 0; dt < DA / 32; ++dt) mma(dva[dt], crd.read(dos, 16 * u, h * (DA / 32) + dt), pf);
+        for (int dt = 0; dt < DA / 32; ++dt) {
+          const Frag<T> a1 = crd.read(dos, dt + 1 < DA / 32 ? 0 : 16, h * (DA / 32) + (dt + 1) % (DA / 32));
+          mma(dva[dt], a0, pf0);
+#pragma unroll
+          for (int r = 8; r < 16; ++r)
+            if ((r - 8) * (DA / 32) / 8 == dt) s[r] = fast_exp2(fmaf(s[r], c, -lsv[r >> 2][r & 3]));
+          __builtin_amdgcn_sched_barrier(0);
+          a0 = a1;
         }
+        const Frag<T> pf1 = acc_frag<T>(s, 1);
+#pragma unroll
+        for (int dt = 0; dt < DA / 32; ++dt) mma(dva[dt], dt == 0 ? a0 : crd.read(dos, 16, h * (DA / 32) + dt), pf1);
       }
       next();
     };
@@ -1385,10 +1474,25 @@ bwd_dkdv_wide_kernel(AttnArgs a) {
       const float* dlts = reinterpret_cast<const float*>(qs + 2 * QTile::kBytes + kStats);
       if (t + 1 < total) fill(stage ? st0 : st1);
       f32x16 s;
-      if (probs(qs, s)) {
+      f32x4 lsv[4];
+      if (scores(qs, s, lsv)) {
+        // dP's MFMAs do not need P: its exp2 issue between them, a cell per
+        // MFMA at head_dim 256, one every other MFMA at 512
         f32x16 dp = f32x16{};
+        {
+          Frag<T> b0 = rrd.read(dos, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ss = 0; ss < D / 16; ++ss) mma(dp, rrd.read(dos, 0, ss), vf[ss]);
+          for (int ss = 0; ss < D / 16; ++ss) {
+            const Frag<T> b1 = rrd.read(dos, 0, (ss + 1) % (D / 16));
+            mma(dp, b0, vf[ss]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (r * (D / 16) / 16 == ss) s[r] = fast_exp2(fmaf(s[r], c, -lsv[r >> 2][r & 3]));
+            __builtin_amdgcn_sched_barrier(0);
+            b0 = b1;
+          }
+        }
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlts + 8 * r4 + 4 * half);
