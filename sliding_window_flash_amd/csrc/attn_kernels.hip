@@ -841,8 +841,8 @@ bwd_dq_kernel(AttnArgs a) {
       // and dP MFMAs issue with block 0's softmax between them, and the dQ
       // MFMAs of block 0 with block 1's softmax between them; scheduling
       // fences keep that order, and each chunk reads the next chunk's
-      // operands first. (At head_dim 128 two waves share a SIMD and this
-      // gained nothing.)
+      // operands first. (At head_dim 128, where two waves share a SIMD, the
+      // same measured within 1% either way.)
       f32x16 s0 = f32x16{}, dp0 = ndlt, s1 = f32x16{}, dp1 = ndlt;
 #pragma unroll
       for (int ss = 0; ss < D / 16; ++ss) {
@@ -1167,10 +1167,11 @@ bwd_dkdv_kernel(AttnArgs a) {
       // run the same phases at the same time, so a softmax that follows all
       // of the S / dP MFMAs finds the matrix core idle. Here each MFMA pair of
       // the first 16 rows is followed by the exp2, FMA and multiply of two
-      // cells of the last 16, in one wave's instruction stream, so that they
-      // issue while the matrix core works (scheduling fences keep the order;
-      // each chunk reads the next chunk's operands first). dK/dV 3.3-4.5%
-      // faster in four interleaved A/B runs, outputs bitwise equal.
+      // cells of the last 16 (four at head_dim 64), in one wave's instruction
+      // stream, so that they issue while the matrix core works (scheduling
+      // fences keep the order; each chunk reads the next chunk's operands
+      // first). dK/dV 3.3-4.5% faster in four interleaved A/B runs, outputs
+      // bitwise equal.
       const Frag<T> pf0 = acc_frag<T>(s, 0);
       const Frag<T> dsf0 = acc_frag<T>(dp, 0);
       Frag<T> a0 = crd.read(dos, 32 * mh, 0), b0 = crd.read(qs, 32 * mh, 0);
